@@ -1,0 +1,292 @@
+"""Plain float64 restatement of the paged GQA attention step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring for who may use it).
+
+The step, in the order the pages describe it for one Qwen2 attention layer
+served by vLLM ([P2] §2.2 and §4.1; [P3] §2.1):
+
+  1. the fused QKV projection output is split into q, k, v by columns
+     (q heads, then k heads, then v heads) -- [P2] §2.2 (QKVParallelLinear),
+     §4.3 (packed_modules_mapping q_proj, k_proj, v_proj -> qkv_proj);
+  2. rotary position embedding is applied to q and k with the full head
+     dimension rotated and base rope_theta -- [P2] §2.2 (get_rope(head_dim,
+     rotary_dim=head_dim, max_position, base=rope_theta)); [P1] §2
+     (rope_theta read with default 1000000);
+  3. k and v are written into the paged KV cache, fixed-size blocks handed
+     out like OS memory pages -- [P3] §2.1 (PagedAttention), [P5] §5
+     (seq.block_table);
+  4. attention of every query row over its sequence's cached keys, causal,
+     with GQA (query heads grouped over fewer KV heads) and scaling
+     head_dim ** -0.5 -- [P1] §2 (28:4, "7 Q heads share one KV group"),
+     [P2] §2.2 and §7.3 (causal mask), [P4] §3 (flash-attn varlen packed
+     prefill), [P3] §2.1 (PagedAttention decode).
+
+Where the pages are silent the plainest reading is taken (each one is listed
+with the function that uses it):
+  * NeoX pairing: element i is rotated with element i + d/2 (half split);
+  * frequency law f_i = theta ** (-2 i / d), i < d/2;
+  * slot = physical_block * block_size + offset, slot < 0 means "skip";
+  * query row i of a sequence with n new rows and context c sits at
+    position c - n + i and sees keys 0..c-n+i (bottom-right causal);
+  * softmax is base e, max-subtracted, masked keys excluded;
+  * rotated q and k, and the output, are rounded once from float64 to the
+    storage dtype (round to nearest even); v is copied bit for bit.
+
+Cache layouts (interface definition):
+  K cache [num_blocks][num_kv_heads][block_size][head_dim]
+  V cache [num_blocks][num_kv_heads][head_dim][block_size]
+
+Storage conventions: bf16 tensors are numpy uint16 bit patterns, fp32 tensors
+are numpy float32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_inv_freq", "rope_neox", "to_f64", "from_f64", "f64_to_bf16_bits",
+    "bf16_bits_to_f64", "rope_cache_write", "gather_kv", "causal_visible",
+    "softmax_rows", "kv_head_for", "default_scale", "attention_varlen",
+    "attention_decode", "run_step",
+]
+
+
+# ---------------------------------------------------------------------------
+# storage <-> float64
+# ---------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64, exactly (bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 once, round-to-nearest-even; return uint16 bits.
+
+    bf16 keeps 8 significant bits and fp32's exponent range.  For |x| in
+    [2**(e-1), 2**e) the spacing is 2**(e-8); below the smallest normal
+    (2**-126) the spacing stays 2**-133.  Dividing by the spacing is exact
+    (a power of two), ``np.rint`` rounds half to even, and the product is
+    exactly representable, so there is a single rounding."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    _, e = np.frexp(xf)
+    e = np.maximum(e, -125)
+    ulp = np.ldexp(1.0, e - 8)
+    r = np.rint(xf / ulp) * ulp
+    with np.errstate(over="ignore"):
+        f32 = r.astype(np.float32)           # exact, or +-inf past the bf16 range
+    bits = (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(np.isnan(x), np.uint16(0x7FC0), bits)
+    bits = np.where(np.isposinf(x), np.uint16(0x7F80), bits)
+    bits = np.where(np.isneginf(x), np.uint16(0xFF80), bits)
+    return bits.astype(np.uint16)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array -> float64 (exact widening)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def from_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> storage dtype, one round-to-nearest-even rounding."""
+    if dtype == "bf16":
+        return f64_to_bf16_bits(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# 2. rotary position embedding (NeoX half split)
+# ---------------------------------------------------------------------------
+def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
+    """Rotation frequencies f_i = theta ** (-2 i / d), i = 0 .. d/2 - 1.
+
+    [P2] §2.2: get_rope(head_dim, rotary_dim=head_dim, ..., base=rope_theta)
+    -- the whole head is rotated with base rope_theta; [P1] §2: Qwen2's
+    rope_theta is 1e6.  The pages do not print the law; this is the standard
+    one for a given base."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / float(head_dim))
+
+
+def rope_neox(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate ``x[..., t, head, :]`` by the angle positions[t] * f_i.
+
+    x: float64 [T][heads][d]; positions: int [T].  NeoX pairing: for
+    i < d/2 the pair (x_i, x_{i+d/2}) is rotated:
+        y_i       = x_i * cos(a) - x_{i+d/2} * sin(a)
+        y_{i+d/2} = x_{i+d/2} * cos(a) + x_i * sin(a),  a = p * f_i
+    The angle is formed in float64 for every position."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    f = rope_inv_freq(d, theta)
+    a = np.asarray(positions, dtype=np.float64)[:, None] * f[None, :]    # [T][d/2]
+    c = np.cos(a)[:, None, :]
+    s = np.sin(a)[:, None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:]
+    y = np.empty_like(x)
+    y[..., :half] = x1 * c - x2 * s
+    y[..., half:] = x2 * c + x1 * s
+    return y
+
+
+# ---------------------------------------------------------------------------
+# 1-3. split fused QKV, rotate, write the paged cache
+# ---------------------------------------------------------------------------
+def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
+                     num_heads, num_kv_heads, head_dim, block_size, theta):
+    """Split the fused QKV rows, rotate q and k, scatter k and v into the cache.
+
+    qkv: storage [T][(H + 2 Hkv) * d]; columns [0, H d) are q, then Hkv k
+    heads, then Hkv v heads ([P2] §2.2 fused QKV; §4.3 packed q, k, v).
+    Returns (q_out [T][H][d] storage, k_cache', v_cache') -- new arrays, the
+    inputs are not modified.  For each token with slot >= 0:
+        block = slot // B, offset = slot % B
+        K[block][g][offset][:] = rot(k[t][g]);  V[block][g][:][offset] = v[t][g]
+    Slots not named keep their previous bits ([P3] §2.1 paged blocks)."""
+    H, Hkv, d, B = num_heads, num_kv_heads, head_dim, block_size
+    qkv = np.asarray(qkv)
+    T = qkv.shape[0]
+    heads = qkv.reshape(T, H + 2 * Hkv, d)
+    x = to_f64(heads, dtype)
+    q_rot = rope_neox(x[:, :H], positions, theta)
+    k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)
+    q_out = from_f64(q_rot, dtype)
+    k_store = from_f64(k_rot, dtype)
+    v_store = heads[:, H + Hkv:]              # stored unchanged (bit copy)
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    for t in range(T):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        blk, off = divmod(slot, B)
+        kc[blk, :, off, :] = k_store[t]
+        vc[blk, :, :, off] = v_store[t]
+    return q_out, kc, vc
+
+
+def gather_kv(k_cache, v_cache, block_table_row, context_len, block_size, dtype):
+    """Logical keys/values 0..c-1 of one sequence through its block table.
+
+    Logical position j lives in physical block block_table[j // B] at offset
+    j % B ([P3] §2.1; [P5] §5 seq.block_table).  Returns float64 K, V of
+    shape [c][Hkv][d]."""
+    B = block_size
+    j = np.arange(int(context_len))
+    blk = np.asarray(block_table_row)[j // B].astype(np.int64)
+    off = j % B
+    K = to_f64(np.asarray(k_cache)[blk, :, off, :], dtype)
+    V = to_f64(np.asarray(v_cache)[blk, :, :, off], dtype)
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# 4. attention
+# ---------------------------------------------------------------------------
+def causal_visible(num_rows: int, context_len: int) -> np.ndarray:
+    """Boolean [n][c]: query row i (position c - n + i) sees key j iff
+    j <= c - n + i.  [P2] §7.3 (causal mask); the alignment of new rows after
+    cached context is the plainest reading (the pages do not spell it out)."""
+    n, c = int(num_rows), int(context_len)
+    pq = c - n + np.arange(n)
+    return np.arange(c)[None, :] <= pq[:, None]
+
+
+def softmax_rows(z: np.ndarray, visible: np.ndarray) -> np.ndarray:
+    """Row softmax over visible entries: m = max z, w = exp(z - m),
+    pi = w / sum(w); masked entries are excluded (probability exactly 0)."""
+    zm = np.where(visible, z, -np.inf)
+    m = zm.max(axis=-1, keepdims=True)
+    w = np.where(visible, np.exp(zm - m), 0.0)
+    return w / w.sum(axis=-1, keepdims=True)
+
+
+def kv_head_for(h: int, num_heads: int, num_kv_heads: int) -> int:
+    """GQA: consecutive groups of H/Hkv query heads share one KV head
+    ([P1] §2: 28 query heads over 4 KV heads, seven per group)."""
+    return h // (num_heads // num_kv_heads)
+
+
+def default_scale(head_dim: int) -> float:
+    """Softmax scaling head_dim ** -0.5 ([P1] §2: 1/sqrt(128) for Qwen2-7B)."""
+    return float(head_dim) ** -0.5
+
+
+def attention_varlen(q, k_cache, v_cache, cu_seqlens_q, context_lens, block_tables,
+                     num_heads, num_kv_heads, head_dim, block_size, dtype,
+                     scale=None, return_probs=False):
+    """Causal GQA attention of packed query rows over the paged cache.
+
+    q: storage [T][H][d] (already rotated).  Sequence s owns rows
+    cu_seqlens_q[s]..cu_seqlens_q[s+1] and context_lens[s] keys (the new rows
+    included).  Head h reads KV head g = h // (H / Hkv) ([P1] §2: seven
+    query heads share one KV group).  Scores z = scale * <q_h, K_j> with
+    scale = head_dim ** -0.5 ([P1] §2 / [P2] §4.1 scaling); output
+    o = sum_j pi_j V_j.  Returns float64 [T][H][d] (and the probabilities per
+    sequence and head when return_probs)."""
+    H, Hkv, d = num_heads, num_kv_heads, head_dim
+    if scale is None:
+        scale = default_scale(d)
+    qf = to_f64(q, dtype).reshape(-1, H, d)
+    out = np.zeros(qf.shape, dtype=np.float64)
+    probs = []
+    cu = np.asarray(cu_seqlens_q)
+    for s in range(len(cu) - 1):
+        r0, r1 = int(cu[s]), int(cu[s + 1])
+        n, c = r1 - r0, int(context_lens[s])
+        if n == 0:
+            probs.append(None)
+            continue
+        K, V = gather_kv(k_cache, v_cache, block_tables[s], c, block_size, dtype)
+        vis = causal_visible(n, c)
+        ps = []
+        for h in range(H):
+            g = kv_head_for(h, H, Hkv)
+            z = scale * (qf[r0:r1, h, :] @ K[:, g, :].T)          # [n][c]
+            pi = softmax_rows(z, vis)
+            out[r0:r1, h, :] = pi @ V[:, g, :]
+            if return_probs:
+                ps.append(pi)
+        probs.append(ps if return_probs else None)
+    if return_probs:
+        return out, probs
+    return out
+
+
+def attention_decode(q, k_cache, v_cache, block_tables, context_lens,
+                     num_heads, num_kv_heads, head_dim, block_size, dtype, scale=None):
+    """Single-token decode: one query row per sequence at position c - 1,
+    attending to all c cached keys (its own key included, written before the
+    attention) -- [P3] §2.1 PagedAttention.  The same definition as
+    attention_varlen with one row per sequence."""
+    S = len(context_lens)
+    cu = np.arange(S + 1, dtype=np.int64)
+    return attention_varlen(q, k_cache, v_cache, cu, context_lens, block_tables,
+                            num_heads, num_kv_heads, head_dim, block_size, dtype, scale)
+
+
+def run_step(batch, k_cache=None, v_cache=None):
+    """The whole step for a workload batch: rope + cache write over every
+    token, then prefill attention over the prefill sequences and decode
+    attention over the rest.  Returns dict(q_out, k_cache, v_cache, out) with
+    ``out`` float64 [T][H][d] (rows in token order)."""
+    sh = batch.shape
+    kc0 = batch.k_cache if k_cache is None else k_cache
+    vc0 = batch.v_cache if v_cache is None else v_cache
+    q_out, kc, vc = rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
+                                     kc0, vc0, sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                                     sh.block_size, sh.rope_theta)
+    out = attention_varlen(q_out, kc, vc, batch.cu_seqlens_q, batch.context_lens,
+                           batch.block_tables, sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                           sh.block_size, sh.dtype)
+    return {"q_out": q_out, "k_cache": kc, "v_cache": vc, "out": out}

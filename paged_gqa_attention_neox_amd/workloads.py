@@ -1,0 +1,453 @@
+"""Seeded synthetic inputs for the paged GQA attention path.
+
+This module only builds inputs: shapes, lengths, block tables, slot mappings
+and the contents of the paged KV pool *before* a step runs.  It performs none
+of the attention arithmetic (no rotation, no softmax, no reduction); both the
+HIP path and the CPU oracle consume what it produces.
+
+Shapes follow the model configurations the pages print:
+  * Qwen2-7B: hidden 3584, 28 query heads, 4 KV heads, so head_dim 128 and a
+    GQA group of 7; rope_theta 1e6; max_position_embeddings 32768
+    ("Qwen2 model structure explained in vLLM", section 2, config JSON).
+  * Qwen3-0.6B: 16 query heads, 8 KV heads, head_dim 128
+    ("nano-vllm ... Qwen3 skeleton", section 2, configuration table).
+  * Tensor-parallel share at TP=2: 14 query heads, 2 KV heads (same page as
+    Qwen2-7B, section 2, head split rule).
+  * Request lengths 128..512 for the prefill batch follow the length spread
+    used in the continuous-batching measurement ("vLLM deployment of Qwen",
+    section 2.1).
+  * KV cache in fixed-size blocks of 16 tokens (the vLLM `--block-size`
+    default; same page, section 5.1).
+
+Cache layouts (an interface definition, identical for every consumer):
+  * K cache: ``[num_blocks][num_kv_heads][block_size][head_dim]``
+  * V cache: ``[num_blocks][num_kv_heads][head_dim][block_size]``
+A token at logical position ``p`` of a sequence lives in physical block
+``block_table[p // B]`` at offset ``p % B``; its slot number is
+``block * B + offset``.
+
+Values are stored as raw storage bits: bf16 as ``uint16`` arrays, fp32 as
+``float32`` arrays.  Unused blocks, and slots past a sequence's context, hold
+NaN so that any read outside the context shows up in the output.
+
+Draw order for every workload (one ``numpy.random.default_rng(seed)``):
+lengths -> prefix-sharing choices -> block permutation -> fused QKV rows ->
+pre-existing cache contents (K then V, sequence by sequence, shared prefix
+first).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+F32_NAN = np.float32("nan")
+
+DTYPES = ("bf16", "f32")
+
+
+# --------------------------------------------------------------------------
+# storage helpers (plain data conversion; no method arithmetic)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round-to-nearest-even); return uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def storage_nan(dtype: str):
+    return BF16_NAN_BITS if dtype == "bf16" else F32_NAN
+
+
+def storage_np_dtype(dtype: str):
+    return np.uint16 if dtype == "bf16" else np.float32
+
+
+def normal_storage(rng: np.random.Generator, shape, scale: float, dtype: str) -> np.ndarray:
+    """N(0,1) * scale drawn in float32, then stored in ``dtype``.
+
+    Each call takes one 63-bit seed from ``rng`` and draws the array with a
+    torch CPU generator (several times faster than numpy for the large pools)."""
+    seed = int(rng.integers(0, 2**63 - 1))
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(tuple(int(v) for v in np.atleast_1d(shape)) if not isinstance(shape, tuple) else shape,
+                    generator=g, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(float(scale))
+    if dtype == "bf16":
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return x.numpy()
+
+
+# --------------------------------------------------------------------------
+# workload description
+# --------------------------------------------------------------------------
+@dataclass
+class AttnShape:
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int = 16
+    dtype: str = "bf16"
+    rope_theta: float = 1.0e6
+    max_position: int = 32768
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def qkv_width(self) -> int:
+        return (self.num_heads + 2 * self.num_kv_heads) * self.head_dim
+
+    @property
+    def scale(self) -> float:
+        # head_dim ** -0.5, the softmax scaling the attention layer is built with
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+
+@dataclass
+class Batch:
+    """One step's inputs.  Sequences ``[0, num_prefill)`` are prefill chunks
+    (query rows ``cu_seqlens_q[s]..cu_seqlens_q[s+1]``); the remaining
+    sequences are single-token decodes whose query rows follow the prefill
+    rows in the same order."""
+
+    name: str
+    shape: AttnShape
+    qkv: np.ndarray            # [T][(H+2Hkv)*d] storage
+    positions: np.ndarray      # int32 [T]
+    slot_mapping: np.ndarray   # int32 [T]
+    k_cache: np.ndarray        # [nb][Hkv][B][d] storage (state before the step)
+    v_cache: np.ndarray        # [nb][Hkv][d][B] storage
+    block_tables: np.ndarray   # int32 [S][max_blocks]
+    context_lens: np.ndarray   # int32 [S] (includes this step's tokens)
+    query_lens: np.ndarray     # int32 [S]
+    num_prefill: int
+    poison_block: int
+    shared_prefix_blocks: int = 0
+    seed: int = 0
+    # logical pre-existing K/V per sequence ([m][Hkv][d] storage); only kept on request
+    pre_k: Optional[List[np.ndarray]] = None
+    pre_v: Optional[List[np.ndarray]] = None
+    notes: dict = field(default_factory=dict)
+
+    # ---- derived views ----
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.qkv.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def cu_seqlens_q(self) -> np.ndarray:
+        cu = np.zeros(self.num_seqs + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(self.query_lens)
+        return cu
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def num_prefill_tokens(self) -> int:
+        return int(self.query_lens[: self.num_prefill].sum())
+
+    @property
+    def num_decode(self) -> int:
+        return self.num_seqs - self.num_prefill
+
+    def prefill_part(self):
+        """(cu_seqlens_q, context_lens, block_tables) of the prefill sequences."""
+        p = self.num_prefill
+        cu = np.zeros(p + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(self.query_lens[:p])
+        return cu, self.context_lens[:p].copy(), self.block_tables[:p].copy()
+
+    def decode_part(self):
+        """(context_lens, block_tables) of the decode sequences."""
+        p = self.num_prefill
+        return self.context_lens[p:].copy(), self.block_tables[p:].copy()
+
+    # ---- algorithmic work (what the method must move / compute) ----
+    def decode_kv_bytes(self) -> int:
+        sh = self.shape
+        c = self.context_lens[self.num_prefill:].astype(np.int64)
+        return int(c.sum()) * 2 * sh.num_kv_heads * sh.head_dim * sh.elem_bytes
+
+    def decode_bytes(self) -> int:
+        """KV read once per KV head + q read + out written + block-table rows + context lens."""
+        sh = self.shape
+        c = self.context_lens[self.num_prefill:].astype(np.int64)
+        nd = self.num_decode
+        qo = 2 * nd * sh.num_heads * sh.head_dim * sh.elem_bytes
+        bt = 4 * int(((c + sh.block_size - 1) // sh.block_size).sum()) + 4 * nd
+        return self.decode_kv_bytes() + qo + bt
+
+    def prefill_flops(self) -> int:
+        """4*d*H per unmasked (query, key) pair: QK^T and PV, causal entries only."""
+        sh = self.shape
+        tot = 0
+        for s in range(self.num_prefill):
+            n = int(self.query_lens[s])
+            c = int(self.context_lens[s])
+            # row i sees keys 0..c-n+i  -> (c - n + i + 1) keys
+            tot += n * (c - n + 1) + n * (n - 1) // 2
+        return 4 * sh.head_dim * sh.num_heads * tot
+
+    def rope_write_bytes(self) -> int:
+        sh = self.shape
+        t = self.num_tokens
+        e = sh.elem_bytes
+        d = sh.head_dim
+        return (t * sh.qkv_width * e + t * sh.num_heads * d * e
+                + t * 2 * sh.num_kv_heads * d * e + 8 * t)
+
+
+# --------------------------------------------------------------------------
+# builder
+# --------------------------------------------------------------------------
+def _build(name: str, shape: AttnShape, seed: int, rng: np.random.Generator,
+           context_lens: np.ndarray, query_lens: np.ndarray, num_prefill: int,
+           shares_prefix: np.ndarray, shared_prefix_len: int, value_scale: float,
+           pool_size: Optional[int] = None, keep_logical: bool = False) -> Batch:
+    B = shape.block_size
+    Hkv, d, dt = shape.num_kv_heads, shape.head_dim, shape.dtype
+    S = int(context_lens.shape[0])
+    assert shared_prefix_len % B == 0
+    spb = shared_prefix_len // B
+
+    blocks_per_seq = (context_lens + B - 1) // B
+    private = np.where(shares_prefix, blocks_per_seq - spb, blocks_per_seq).astype(np.int64)
+    assert (private >= 0).all()
+    needed = spb + int(private.sum())
+    if pool_size is None:
+        pool_size = int(math.ceil(1.25 * needed))
+    assert pool_size > needed, "pool must keep at least one unused (poison) block"
+
+    ids = rng.permutation(pool_size).astype(np.int32)
+    shared_ids = ids[:spb]
+    poison = int(ids[needed])
+    max_blocks = int(blocks_per_seq.max())
+    bt = np.full((S, max_blocks), poison, dtype=np.int32)
+    nxt = spb
+    for s in range(S):
+        start = 0
+        if shares_prefix[s]:
+            bt[s, :spb] = shared_ids
+            start = spb
+        cnt = int(blocks_per_seq[s]) - start
+        bt[s, start:start + cnt] = ids[nxt:nxt + cnt]
+        nxt += cnt
+    assert nxt == needed
+
+    # query rows: prefill rows first, then one row per decode sequence
+    T = int(query_lens.sum())
+    qkv = normal_storage(rng, (T, shape.qkv_width), value_scale, dt)
+    positions = np.empty(T, dtype=np.int32)
+    slots = np.empty(T, dtype=np.int32)
+    row = 0
+    for s in range(S):
+        n, c = int(query_lens[s]), int(context_lens[s])
+        p = np.arange(c - n, c, dtype=np.int64)
+        positions[row:row + n] = p
+        slots[row:row + n] = bt[s, p // B].astype(np.int64) * B + p % B
+        row += n
+
+    # pool, NaN everywhere, then the context that earlier steps left behind
+    k_cache = np.full((pool_size, Hkv, B, d), storage_nan(dt), dtype=storage_np_dtype(dt))
+    v_cache = np.full((pool_size, Hkv, d, B), storage_nan(dt), dtype=storage_np_dtype(dt))
+
+    def put(block_ids: np.ndarray, pos: np.ndarray, kv: np.ndarray, vv: np.ndarray):
+        """Place logical rows kv/vv ([m][Hkv][d], positions pos[0].. contiguous,
+        pos[0] a multiple of B) into their blocks; the tail of the last block
+        stays NaN."""
+        m = kv.shape[0]
+        if m == 0:
+            return
+        assert pos[0] % B == 0
+        nblk = (m + B - 1) // B
+        blk = block_ids[pos[0] // B: pos[0] // B + nblk]
+        pad = nblk * B - m
+        if pad:
+            fill = np.full((pad, Hkv, d), storage_nan(dt), dtype=kv.dtype)
+            kv = np.concatenate([kv, fill])
+            vv = np.concatenate([vv, fill])
+        kb = kv.reshape(nblk, B, Hkv, d)
+        vb = vv.reshape(nblk, B, Hkv, d)
+        k_cache[blk] = kb.transpose(0, 2, 1, 3)
+        v_cache[blk] = vb.transpose(0, 2, 3, 1)
+
+    pre_k: List[np.ndarray] = []
+    pre_v: List[np.ndarray] = []
+    shared_k = shared_v = None
+    if spb:
+        pos = np.arange(shared_prefix_len, dtype=np.int64)
+        shared_k = normal_storage(rng, (shared_prefix_len, Hkv, d), value_scale, dt)
+        shared_v = normal_storage(rng, (shared_prefix_len, Hkv, d), value_scale, dt)
+        put(shared_ids.astype(np.int64), pos, shared_k, shared_v)
+    for s in range(S):
+        n, c = int(query_lens[s]), int(context_lens[s])
+        m = c - n
+        start = shared_prefix_len if shares_prefix[s] else 0
+        assert m >= start or m == 0 or not shares_prefix[s]
+        cnt = max(0, m - start)
+        pos = np.arange(start, start + cnt, dtype=np.int64)
+        kk = normal_storage(rng, (cnt, Hkv, d), value_scale, dt)
+        vv = normal_storage(rng, (cnt, Hkv, d), value_scale, dt)
+        if cnt:
+            put(bt[s].astype(np.int64), pos, kk, vv)
+        if keep_logical:
+            if start:
+                pre_k.append(np.concatenate([shared_k[:min(m, start)], kk]))
+                pre_v.append(np.concatenate([shared_v[:min(m, start)], vv]))
+            else:
+                pre_k.append(kk)
+                pre_v.append(vv)
+
+    return Batch(name=name, shape=shape, qkv=qkv, positions=positions, slot_mapping=slots,
+                 k_cache=k_cache, v_cache=v_cache, block_tables=bt,
+                 context_lens=context_lens.astype(np.int32), query_lens=query_lens.astype(np.int32),
+                 num_prefill=num_prefill, poison_block=poison, shared_prefix_blocks=spb, seed=seed,
+                 pre_k=pre_k if keep_logical else None, pre_v=pre_v if keep_logical else None)
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+def tiny_f32_steps(seed: int = 1) -> List[Batch]:
+    """Tiny fp32 GQA: one sequence, a 16-token causal prefill (positions 0..15)
+    then 4 single-token decode steps (positions 16..19); 4 q heads, 2 KV heads,
+    head_dim 64, block 16, a 4-block pool whose physical ids are permuted.
+
+    Returns the 5 steps in order.  Every step carries the same initial (all-NaN)
+    pool; a runner must thread each step's output cache into the next step."""
+    shape = AttnShape(num_heads=4, num_kv_heads=2, head_dim=64, block_size=16, dtype="f32")
+    rng = np.random.default_rng(seed)
+    B = shape.block_size
+    ids = rng.permutation(4).astype(np.int32)
+    while ids[0] == 0 and ids[1] == 1:          # redraw an identity logical->physical map
+        ids = rng.permutation(4).astype(np.int32)
+    bt = ids[None, :2].copy()                   # logical blocks 0, 1
+    poison = int(ids[2])
+    qkv = normal_storage(rng, (20, shape.qkv_width), 1.0, "f32")
+    k_cache = np.full((4, 2, B, 64), F32_NAN, dtype=np.float32)
+    v_cache = np.full((4, 2, 64, B), F32_NAN, dtype=np.float32)
+
+    def slots(pos):
+        pos = np.asarray(pos, np.int64)
+        return (bt[0, pos // B].astype(np.int64) * B + pos % B).astype(np.int32)
+
+    p0 = np.arange(16, dtype=np.int32)
+    steps = [Batch(name="tiny_f32_prefill16", shape=shape, qkv=qkv[:16].copy(), positions=p0,
+                   slot_mapping=slots(p0), k_cache=k_cache, v_cache=v_cache, block_tables=bt.copy(),
+                   context_lens=np.array([16], np.int32), query_lens=np.array([16], np.int32),
+                   num_prefill=1, poison_block=poison, seed=seed,
+                   pre_k=[k_cache[:0, 0, 0, :]], pre_v=[v_cache[:0, 0, :, 0]])]
+    for k in range(4):
+        p = np.array([16 + k], np.int32)
+        steps.append(Batch(name=f"tiny_f32_decode{k}", shape=shape, qkv=qkv[16 + k:17 + k].copy(),
+                           positions=p, slot_mapping=slots(p), k_cache=k_cache, v_cache=v_cache,
+                           block_tables=bt.copy(), context_lens=np.array([17 + k], np.int32),
+                           query_lens=np.array([1], np.int32), num_prefill=0,
+                           poison_block=poison, seed=seed))
+    return steps
+
+
+def qwen3_decode(seed: int = 2, num_seqs: int = 32, keep_logical: bool = False) -> Batch:
+    """Qwen3-0.6B-shaped decode, bf16: 16 q heads, 8 KV heads, head_dim 128,
+    block 16; batch 32; context lengths uniform in [128, 2048]; values N(0,1)*0.5."""
+    shape = AttnShape(num_heads=16, num_kv_heads=8, head_dim=128)
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(128, 2048, size=num_seqs, endpoint=True).astype(np.int32)
+    return _build("qwen3_0.6b_decode_b32", shape, seed, rng, ctx, np.ones(num_seqs, np.int32), 0,
+                  np.zeros(num_seqs, bool), 0, 0.5, keep_logical=keep_logical)
+
+
+def qwen2_prefill(seed: int = 3, num_seqs: int = 8, keep_logical: bool = False) -> Batch:
+    """Qwen2-7B-shaped varlen causal prefill, bf16: 28 q heads, 4 KV heads,
+    head_dim 128; 8 packed sequences with lengths uniform in [128, 512];
+    fresh (permuted) cache blocks written in the same step."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128)
+    rng = np.random.default_rng(seed)
+    n = rng.integers(128, 512, size=num_seqs, endpoint=True).astype(np.int32)
+    return _build("qwen2_7b_prefill_8x[128,512]", shape, seed, rng, n.copy(), n.copy(), num_seqs,
+                  np.zeros(num_seqs, bool), 0, 1.0, keep_logical=keep_logical)
+
+
+def qwen2_long_decode(seed: int = 4, num_seqs: int = 64, keep_logical: bool = False) -> Batch:
+    """Qwen2-7B-shaped long-context decode, bf16: 28 q heads, 4 KV heads,
+    head_dim 128; batch 64; context lengths log-uniform in [2048, 32768]."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128)
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(math.log(2048), math.log(32768), size=num_seqs)
+    ctx = np.clip(np.floor(np.exp(u)), 2048, 32768).astype(np.int32)
+    return _build("qwen2_7b_decode_b64_ctx[2048,32768]", shape, seed, rng, ctx,
+                  np.ones(num_seqs, np.int32), 0, np.zeros(num_seqs, bool), 0, 1.0,
+                  keep_logical=keep_logical)
+
+
+def mixed_tp2(seed: int = 5, keep_logical: bool = False) -> Batch:
+    """Mixed chunked batch at the TP=2 share of Qwen2-7B, bf16: 14 q heads,
+    2 KV heads, head_dim 128.  4 prefill chunks of 512 tokens (2 continue a
+    shared 1024-token prefix: positions 1024..1535; 2 start fresh: 0..511) plus
+    96 decode tokens with contexts uniform in [256, 8192], 48 of which share
+    the same 1024-token prefix (shared physical block ids)."""
+    shape = AttnShape(num_heads=14, num_kv_heads=2, head_dim=128)
+    rng = np.random.default_rng(seed)
+    prefix = 1024
+    dec_ctx = rng.integers(256, 8192, size=96, endpoint=True).astype(np.int32)
+    eligible = np.flatnonzero(dec_ctx > prefix)
+    share_dec = np.zeros(96, bool)
+    share_dec[rng.choice(eligible, size=48, replace=False)] = True
+    pre_ctx = np.array([1536, 1536, 512, 512], np.int32)
+    pre_share = np.array([True, True, False, False])
+    ctx = np.concatenate([pre_ctx, dec_ctx])
+    qlen = np.concatenate([np.full(4, 512, np.int32), np.ones(96, np.int32)])
+    share = np.concatenate([pre_share, share_dec])
+    return _build("qwen2_7b_tp2_mixed_4x512+96", shape, seed, rng, ctx, qlen, 4, share, prefix, 1.0,
+                  keep_logical=keep_logical)
+
+
+def small_case(seed: int, dtype: str, num_heads: int, num_kv_heads: int, head_dim: int,
+               context_lens, query_lens, num_prefill: int, block_size: int = 16,
+               value_scale: float = 1.0, keep_logical: bool = True, shares_prefix=None,
+               shared_prefix_len: int = 0) -> Batch:
+    """A custom small batch (tests): explicit lengths, any head layout."""
+    shape = AttnShape(num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                      block_size=block_size, dtype=dtype)
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(context_lens, np.int32)
+    ql = np.asarray(query_lens, np.int32)
+    sh = np.zeros(len(ctx), bool) if shares_prefix is None else np.asarray(shares_prefix, bool)
+    return _build(f"small_{dtype}_s{seed}", shape, seed, rng, ctx, ql, num_prefill, sh,
+                  shared_prefix_len, value_scale, keep_logical=keep_logical)
+
+
+WORKLOADS = {
+    "tiny_f32": tiny_f32_steps,
+    "qwen3_decode": qwen3_decode,
+    "qwen2_prefill": qwen2_prefill,
+    "qwen2_long_decode": qwen2_long_decode,
+    "mixed_tp2": mixed_tp2,
+}

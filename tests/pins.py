@@ -1,0 +1,420 @@
+"""Pins for the CPU oracle: checks against facts other than the oracle itself.
+
+Each pin is a function of the oracle module ``R`` (``oracle.reference``) and
+raises AssertionError when the oracle disagrees with the fact it checks.
+They are run against the real oracle (tests/test_oracle_pins.py) and against
+deliberately broken copies of it (tests/test_oracle_mutations.py), which shows
+that a plausible mistake in any step is caught by at least one pin.
+
+Kinds of pin used here:
+  * textbook values: cos 1, sin 1; powers of ten for the frequency law;
+  * closed forms: a unit vector rotates onto its NeoX partner; constant V
+    gives a constant output; q = 0 gives the mean of the visible V rows;
+    a single visible key returns that key's V row; a dominant "needle" key
+    returns its V row;
+  * library routines on special cases: torch's fp32->bf16 rounding for
+    fp32-representable inputs, torch scaled_dot_product_attention in float64
+    for contiguous causal GQA, numpy complex multiplication for the rotation;
+  * brute force on tiny inputs (tests/brute.py, separate code, exact
+    rational rounding);
+  * invariants the pages fix: RoPE preserves norms and makes q.k depend only
+    on m - n; GQA equals MHA with each KV head repeated; the paged layout
+    equals the contiguous one under any block permutation; softmax rows sum
+    to one; causal masking.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from paged_gqa_attention_neox_amd import workloads as W
+import brute
+
+COS1 = 0.5403023058681398     # cos(1 rad)
+SIN1 = 0.8414709848078965     # sin(1 rad)
+
+
+# ---------------------------------------------------------------------------
+# rounding
+# ---------------------------------------------------------------------------
+def pin_bf16_rounding_values(R):
+    """Hand-checked bf16 encodings, including ties and a value just above a
+    tie that a double rounding through fp32 would get wrong."""
+    cases = [
+        (1.0, 0x3F80), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+        (1.0 + 2.0**-8, 0x3F80),                 # tie -> even (down)
+        (1.0 + 3 * 2.0**-8, 0x3F82),             # tie -> even (up)
+        (1.0 + 2.0**-8 + 2.0**-40, 0x3F81),      # just above the tie -> up
+        (1.0 + 2.0**-8 - 2.0**-40, 0x3F80),      # just below -> down
+        (3.140625, 0x4049), (-0.1, 0xBDCD),
+        (2.0**-126, 0x0080), (2.0**-133, 0x0001),  # smallest normal / subnormal
+        (3.0e38, 0x7F62), (3.5e38, 0x7F80),        # largest region / overflow
+    ]
+    for x, want in cases:
+        got = int(R.f64_to_bf16_bits(np.array([x]))[0])
+        assert got == want, (x, hex(got), hex(want))
+
+
+def pin_bf16_rounding_matches_torch(R):
+    """On fp32-representable inputs one rounding fp32->bf16 is torch's."""
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    bits[::3] = (bits[::3] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)   # exact ties
+    exp = (bits >> np.uint32(23)) & np.uint32(0xFF)
+    bits = bits[(exp != 0xFF) & (exp < 0xFE)]                             # finite, no overflow
+    f = bits.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = R.f64_to_bf16_bits(f.astype(np.float64))
+    assert np.array_equal(got, want), int(np.sum(got != want))
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding
+# ---------------------------------------------------------------------------
+def _unit(d, i):
+    x = np.zeros((1, 1, d))
+    x[0, 0, i] = 1.0
+    return x
+
+
+def pin_rope_unit_vector_neox(R):
+    """e_0 at position 1 (f_0 = 1 for any base) -> cos 1 at index 0 and
+    sin 1 at index d/2: NeoX half-split pairing, counter-clockwise sign."""
+    for d in (64, 128):
+        y = R.rope_neox(_unit(d, 0), np.array([1]), 1.0e6)[0, 0]
+        want = np.zeros(d)
+        want[0], want[d // 2] = COS1, SIN1
+        assert np.allclose(y, want, atol=1e-15), (d, y[:3], y[d // 2:d // 2 + 2])
+        y = R.rope_neox(_unit(d, d // 2), np.array([1]), 1.0e6)[0, 0]
+        want = np.zeros(d)
+        want[0], want[d // 2] = -SIN1, COS1
+        assert np.allclose(y, want, atol=1e-15)
+
+
+def pin_rope_frequency_closed_forms(R):
+    """f_i = theta^(-2i/d): at i = d/4 the frequency is theta^(-1/2)
+    (1e-3 for theta = 1e6, 1e-2 for theta = 1e4), so position 1/f rotates by
+    exactly one radian; at i = d/8, theta = 1e6 the frequency is
+    10^-1.5 = 1/sqrt(1000)."""
+    for d, theta, p in ((128, 1.0e6, 1000), (64, 1.0e6, 1000), (128, 1.0e4, 100)):
+        i = d // 4
+        y = R.rope_neox(_unit(d, i), np.array([p]), theta)[0, 0]
+        assert abs(y[i] - COS1) < 1e-12 and abs(y[i + d // 2] - SIN1) < 1e-12, (d, theta)
+    d = 128
+    y = R.rope_neox(_unit(d, 16), np.array([1000]), 1.0e6)[0, 0]
+    ang = 1000.0 / math.sqrt(1000.0)
+    assert abs(y[16] - math.cos(ang)) < 1e-12 and abs(y[16 + 64] - math.sin(ang)) < 1e-12
+    f = R.rope_inv_freq(128, 1.0e6)
+    assert f.shape == (64,) and f[0] == 1.0 and abs(f[32] - 1e-3) < 1e-18
+    r = f[1:] / f[:-1]                                     # geometric progression
+    assert np.allclose(r, r[0], rtol=1e-13) and abs(r[0] - 10 ** (-6 / 64)) < 1e-15
+
+
+def pin_rope_identity_at_zero(R):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 3, 128))
+    y = R.rope_neox(x, np.zeros(5, np.int64), 1.0e6)
+    assert np.array_equal(y, x)
+
+
+def pin_rope_norm_preserved(R):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((64, 4, 128))
+    p = rng.integers(0, 32768, size=64)
+    y = R.rope_neox(x, p, 1.0e6)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
+def pin_rope_relative_position(R):
+    """<R_m q, R_n k> depends on m - n only."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        q = rng.standard_normal((1, 1, 128))
+        k = rng.standard_normal((1, 1, 128))
+        m, n, s = (int(v) for v in rng.integers(0, 16000, size=3))
+        a = np.sum(R.rope_neox(q, np.array([m]), 1e6) * R.rope_neox(k, np.array([n]), 1e6))
+        b = np.sum(R.rope_neox(q, np.array([m + s]), 1e6) * R.rope_neox(k, np.array([n + s]), 1e6))
+        assert abs(a - b) <= 1e-9 * max(1.0, abs(a)), (a, b)
+
+
+def pin_rope_composition(R):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((8, 2, 64))
+    a = rng.integers(0, 10000, size=8)
+    b = rng.integers(0, 10000, size=8)
+    y1 = R.rope_neox(R.rope_neox(x, a, 1e6), b, 1e6)
+    y2 = R.rope_neox(x, a + b, 1e6)
+    assert np.allclose(y1, y2, atol=1e-9)
+
+
+def pin_rope_complex_form(R):
+    """Rotation of the pair (x_i, x_{i+d/2}) is multiplication of the complex
+    number x_i + i x_{i+d/2} by exp(i p f_i) (numpy complex arithmetic)."""
+    rng = np.random.default_rng(5)
+    d = 128
+    x = rng.standard_normal((16, 3, d))
+    p = rng.integers(0, 32768, size=16)
+    f = R.rope_inv_freq(d, 1e6)
+    z = (x[..., :d // 2] + 1j * x[..., d // 2:]) * np.exp(1j * (p[:, None, None] * f[None, None, :]))
+    y = R.rope_neox(x, p, 1e6)
+    assert np.allclose(y[..., :d // 2], z.real, atol=1e-12)
+    assert np.allclose(y[..., d // 2:], z.imag, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# cache write / gather
+# ---------------------------------------------------------------------------
+def pin_gather_matches_generator_layout(R):
+    """The generator fills the pool block by block (reshape/transpose code of
+    its own); the oracle's per-position gather must return its logical rows."""
+    for dt in ("bf16", "f32"):
+        b = W.small_case(11, dt, 4, 2, 16, context_lens=[37, 16, 5], query_lens=[1, 1, 1],
+                         num_prefill=0)
+        for s in range(b.num_seqs):
+            m = int(b.context_lens[s]) - 1
+            K, V = R.gather_kv(b.k_cache, b.v_cache, b.block_tables[s], m, 16, dt)
+            assert np.array_equal(K, R.to_f64(b.pre_k[s], dt))
+            assert np.array_equal(V, R.to_f64(b.pre_v[s], dt))
+
+
+def pin_cache_write_v_copy_and_sentinels(R):
+    """V lands bit-exact; K at position 0 is the unrotated k (cos 0 = 1);
+    every slot not named keeps its prior bits; slot -1 writes nothing."""
+    b = W.small_case(12, "bf16", 4, 2, 32, context_lens=[21, 9], query_lens=[21, 9], num_prefill=2)
+    pos = np.zeros_like(b.positions)
+    slots = b.slot_mapping.copy()
+    slots[3] = -1
+    q_out, kc, vc = R.rope_cache_write(b.qkv, "bf16", pos, slots, b.k_cache, b.v_cache, 4, 2, 32, 16, 1e6)
+    heads = b.qkv.reshape(-1, 8, 32)
+    assert np.array_equal(q_out, heads[:, :4])
+    touched = np.zeros(kc.shape[:1] + (16,), bool)
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = divmod(int(slot), 16)
+        touched[blk, off] = True
+        assert np.array_equal(kc[blk, :, off, :], heads[t, 4:6])
+        assert np.array_equal(vc[blk, :, :, off], heads[t, 6:8])
+    kt = np.broadcast_to(touched[:, None, :, None], kc.shape)
+    vt = np.broadcast_to(touched[:, None, None, :], vc.shape)
+    assert np.array_equal(kc[~kt], b.k_cache[~kt]) and np.array_equal(vc[~vt], b.v_cache[~vt])
+    assert np.all(kc[~kt] == 0x7FC0)   # untouched slots of fresh blocks stay NaN
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+def _oracle_out(R, b):
+    sh = b.shape
+    q_out, kc, vc = R.rope_cache_write(b.qkv, sh.dtype, b.positions, b.slot_mapping, b.k_cache,
+                                       b.v_cache, sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                                       sh.block_size, sh.rope_theta)
+    out = R.attention_varlen(q_out, kc, vc, b.cu_seqlens_q, b.context_lens, b.block_tables,
+                             sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, sh.dtype)
+    return q_out, kc, vc, out
+
+
+def pin_brute_force_tiny(R):
+    """Whole step vs the brute force on tiny random cases: prefill chunks
+    after cached context, decodes, GQA groups 1..3, odd block sizes."""
+    cases = [
+        dict(seed=21, dtype="f32", num_heads=4, num_kv_heads=2, head_dim=8,
+             context_lens=[7, 12, 5], query_lens=[7, 4, 1], num_prefill=2, block_size=4),
+        dict(seed=22, dtype="bf16", num_heads=6, num_kv_heads=2, head_dim=8,
+             context_lens=[9, 3, 17], query_lens=[3, 1, 1], num_prefill=1, block_size=2),
+        dict(seed=23, dtype="bf16", num_heads=3, num_kv_heads=3, head_dim=4,
+             context_lens=[6, 1], query_lens=[6, 1], num_prefill=1, block_size=1),
+        dict(seed=24, dtype="f32", num_heads=2, num_kv_heads=1, head_dim=16,
+             context_lens=[19, 2], query_lens=[19, 1], num_prefill=1, block_size=16),
+    ]
+    for cs in cases:
+        b = W.small_case(**cs)
+        q_out, kc, vc, out = _oracle_out(R, b)
+        bq, bout = brute.run(b)
+        assert np.array_equal(R.to_f64(q_out, cs["dtype"]), np.array(bq)), cs["seed"]
+        assert np.allclose(out, np.array(bout), rtol=0, atol=1e-12), (cs["seed"], np.abs(out - np.array(bout)).max())
+
+
+def pin_sdpa_contiguous_gqa(R):
+    """Fresh causal prefill (n == c) equals torch SDPA in float64 on the
+    logical K/V with each KV head repeated G times (enable_gqa)."""
+    b = W.small_case(31, "f32", 8, 2, 32, context_lens=[40, 23], query_lens=[40, 23],
+                     num_prefill=2, block_size=16)
+    q_out, kc, vc, out = _oracle_out(R, b)
+    cu = b.cu_seqlens_q
+    for s in range(2):
+        c = int(b.context_lens[s])
+        # logical K/V, read back through the generator-independent slot list
+        ks, vs = [], []
+        for t in range(cu[s], cu[s + 1]):
+            blk, off = divmod(int(b.slot_mapping[t]), 16)
+            ks.append(kc[blk, :, off, :].astype(np.float64))
+            vs.append(vc[blk, :, :, off].astype(np.float64))
+        K = torch.from_numpy(np.stack(ks)).permute(1, 0, 2)[None]       # [1][Hkv][c][d]
+        V = torch.from_numpy(np.stack(vs)).permute(1, 0, 2)[None]
+        Q = torch.from_numpy(q_out[cu[s]:cu[s + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, enable_gqa=True)
+        want = o[0].permute(1, 0, 2).numpy()
+        assert want.shape == (c, 8, 32)
+        assert np.allclose(out[cu[s]:cu[s + 1]], want, rtol=0, atol=1e-12)
+
+
+def _decode_case(seed, dtype="f32", H=4, Hkv=2, d=16, ctx=(30, 1, 17), scale_v=1.0):
+    return W.small_case(seed, dtype, H, Hkv, d, context_lens=list(ctx), query_lens=[1] * len(ctx),
+                        num_prefill=0, value_scale=scale_v)
+
+
+def pin_constant_v_and_row_sums(R):
+    """Probabilities of every row sum to 1 and a constant V yields that
+    constant."""
+    b = _decode_case(41)
+    q_out, kc, vc, _ = _oracle_out(R, b)
+    sh = b.shape
+    out, probs = R.attention_varlen(q_out, kc, vc, b.cu_seqlens_q, b.context_lens, b.block_tables,
+                                    sh.num_heads, sh.num_kv_heads, sh.head_dim, 16, "f32",
+                                    return_probs=True)
+    for ps in probs:
+        for p in ps:
+            assert np.allclose(p.sum(axis=-1), 1.0, atol=1e-12)
+    vc2 = np.full_like(vc, 0.75)
+    out2 = R.attention_varlen(q_out, kc, vc2, b.cu_seqlens_q, b.context_lens, b.block_tables,
+                              sh.num_heads, sh.num_kv_heads, sh.head_dim, 16, "f32")
+    assert np.allclose(out2, 0.75, atol=1e-13)
+
+
+def pin_single_key_returns_v0(R):
+    """Context 1 (the first token of a sequence): the output is its V row,
+    for every head of the group."""
+    b = _decode_case(42, ctx=(1, 1))
+    q_out, kc, vc, out = _oracle_out(R, b)
+    heads = b.qkv.reshape(b.num_tokens, 8, 16)
+    for t in range(2):
+        for h in range(4):
+            assert np.array_equal(out[t, h], heads[t, 4 + 2 + h // 2].astype(np.float64))
+
+
+def pin_zero_query_gives_mean(R):
+    """q = 0 makes every score 0: the output is the plain mean of the
+    visible V rows (prefill rows see a growing prefix)."""
+    b = W.small_case(43, "f32", 4, 2, 16, context_lens=[13], query_lens=[13], num_prefill=1)
+    q_out, kc, vc, _ = _oracle_out(R, b)
+    sh = b.shape
+    out = R.attention_varlen(np.zeros_like(q_out), kc, vc, b.cu_seqlens_q, b.context_lens,
+                             b.block_tables, 4, 2, 16, 16, "f32")
+    heads = b.qkv.reshape(13, 8, 16).astype(np.float64)
+    for i in range(13):
+        for h in range(4):
+            want = heads[:i + 1, 6 + h // 2].mean(axis=0)
+            assert np.allclose(out[i, h], want, atol=1e-13)
+
+
+def pin_needle(R):
+    """One cached key equal to a large multiple of the rotated query makes
+    its score exceed every other by far more than exp's range: the output
+    is that key's V row (to 1e-12)."""
+    b = _decode_case(44, ctx=(25,))
+    sh = b.shape
+    q_out, kc, vc, _ = _oracle_out(R, b)
+    j = 9
+    blk, off = divmod(int(b.block_tables[0, j // 16]) * 16 + j % 16, 16)
+    for g in range(2):
+        kc[blk, g, off, :] = 64.0 * q_out[0, 2 * g].astype(np.float32)   # needle for head 2g
+    out = R.attention_varlen(q_out, kc, vc, b.cu_seqlens_q, b.context_lens, b.block_tables,
+                             4, 2, 16, 16, "f32")
+    for g in range(2):
+        assert np.allclose(out[0, 2 * g], vc[blk, g, :, off].astype(np.float64), atol=1e-12)
+
+
+def pin_causal_future_invisible(R):
+    """Changing K/V at positions after row i leaves rows 0..i unchanged."""
+    b = W.small_case(45, "f32", 4, 2, 16, context_lens=[20], query_lens=[20], num_prefill=1)
+    q_out, kc, vc, out = _oracle_out(R, b)
+    cut = 11
+    kc2, vc2 = kc.copy(), vc.copy()
+    for j in range(cut + 1, 20):
+        blk, off = divmod(int(b.slot_mapping[j]), 16)
+        kc2[blk, :, off, :] += 3.0
+        vc2[blk, :, :, off] -= 5.0
+    out2 = R.attention_varlen(q_out, kc2, vc2, b.cu_seqlens_q, b.context_lens, b.block_tables,
+                              4, 2, 16, 16, "f32")
+    assert np.array_equal(out2[:cut + 1], out[:cut + 1])
+    assert not np.allclose(out2[cut + 1:], out[cut + 1:])
+
+
+def pin_gqa_equals_mha(R):
+    """GQA over Hkv heads equals MHA whose KV head h is GQA's KV head
+    h // (H/Hkv) (each KV head repeated G times, consecutively)."""
+    H, Hkv, d, G = 6, 2, 16, 3
+    b = _decode_case(46, H=H, Hkv=Hkv, d=d, ctx=(20, 7))
+    q_out, kc, vc, out = _oracle_out(R, b)
+    rep = np.repeat(np.arange(Hkv), G)
+    kc_m, vc_m = kc[:, rep], vc[:, rep]
+    out_m = R.attention_varlen(q_out, kc_m, vc_m, b.cu_seqlens_q, b.context_lens, b.block_tables,
+                               H, H, d, 16, "f32")
+    assert np.array_equal(out, out_m)
+    # and the grouping is consecutive, not round-robin
+    rr = np.tile(np.arange(Hkv), G)
+    out_rr = R.attention_varlen(q_out, kc[:, rr], vc[:, rr], b.cu_seqlens_q, b.context_lens,
+                                b.block_tables, H, H, d, 16, "f32")
+    assert not np.allclose(out, out_rr)
+
+
+def pin_paged_equals_contiguous(R):
+    """Two pools holding the same logical content under different block
+    permutations give identical outputs; so does a pool with blocks in
+    logical order (the contiguous layout)."""
+    b = _decode_case(47, ctx=(45, 33), H=4, Hkv=2, d=16)
+    q_out, kc, vc, out = _oracle_out(R, b)
+    rng = np.random.default_rng(0)
+    for perm in (rng.permutation(b.num_blocks), np.arange(b.num_blocks)[::-1]):
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm))
+        kc2 = np.empty_like(kc)
+        vc2 = np.empty_like(vc)
+        kc2[inv] = kc
+        vc2[inv] = vc
+        bt2 = inv[b.block_tables]
+        out2 = R.attention_varlen(q_out, kc2, vc2, b.cu_seqlens_q, b.context_lens, bt2, 4, 2, 16,
+                                  16, "f32")
+        assert np.array_equal(out2, out)
+
+
+def pin_decode_is_last_prefill_row(R):
+    """Tiny fp32 sequence: 16-token prefill then 4 decode steps equals the
+    matching rows of one 20-token prefill."""
+    steps = W.tiny_f32_steps()
+    sh = steps[0].shape
+    kc, vc = steps[0].k_cache, steps[0].v_cache
+    outs = []
+    for st in steps:
+        q_out, kc, vc = R.rope_cache_write(st.qkv, "f32", st.positions, st.slot_mapping, kc, vc,
+                                           4, 2, 64, 16, 1e6)
+        outs.append(R.attention_varlen(q_out, kc, vc, st.cu_seqlens_q, st.context_lens,
+                                       st.block_tables, 4, 2, 64, 16, "f32"))
+    qkv = np.concatenate([st.qkv for st in steps])
+    pos = np.arange(20, dtype=np.int32)
+    slots = np.concatenate([st.slot_mapping for st in steps])
+    q_out, kc2, vc2 = R.rope_cache_write(qkv, "f32", pos, slots, steps[0].k_cache, steps[0].v_cache,
+                                         4, 2, 64, 16, 1e6)
+    full = R.attention_varlen(q_out, kc2, vc2, np.array([0, 20]), np.array([20]),
+                              steps[-1].block_tables, 4, 2, 64, 16, "f32")
+    seq = np.concatenate(outs)
+    assert np.allclose(seq, full, rtol=0, atol=1e-13), np.abs(seq - full).max()
+    assert np.array_equal(kc.view(np.uint32), kc2.view(np.uint32))      # bitwise, NaN tails included
+    assert np.array_equal(vc.view(np.uint32), vc2.view(np.uint32))
+    del sh
+
+
+ALL_PINS = [
+    pin_bf16_rounding_values, pin_bf16_rounding_matches_torch,
+    pin_rope_unit_vector_neox, pin_rope_frequency_closed_forms, pin_rope_identity_at_zero,
+    pin_rope_norm_preserved, pin_rope_relative_position, pin_rope_composition,
+    pin_rope_complex_form,
+    pin_gather_matches_generator_layout, pin_cache_write_v_copy_and_sentinels,
+    pin_brute_force_tiny, pin_sdpa_contiguous_gqa, pin_constant_v_and_row_sums,
+    pin_single_key_returns_v0, pin_zero_query_gives_mean, pin_needle,
+    pin_causal_future_invisible, pin_gqa_equals_mha, pin_paged_equals_contiguous,
+    pin_decode_is_last_prefill_row,
+]

@@ -1,0 +1,74 @@
+"""Planted mistakes in the CPU oracle must be caught by the pins.
+
+Each mutation rewrites one line of one oracle function (a dropped term, a
+wrong sign, index or operand, a missing rotation ...), swaps the rewritten
+function into ``oracle.reference`` for the duration of the test, and runs the
+pins of tests/pins.py until one fails.  A mutation that no pin notices would
+mean the pins leave that part of the oracle unchecked.  Everything here runs
+on the CPU and only touches the oracle.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.reference as R
+import pins
+
+MUTATIONS = [
+    # rotary embedding
+    ("rope_neox", "y[..., :half] = x1 * c - x2 * s", "y[..., :half] = x1 * c + x2 * s"),
+    ("rope_neox", "y[..., half:] = x2 * c + x1 * s", "y[..., half:] = x2 * c - x1 * s"),
+    ("rope_neox", "x1 = x[..., :half]\n    x2 = x[..., half:]",
+     "x1 = x[..., 0::2]\n    x2 = x[..., 1::2]"),                         # interleaved pairs
+    ("rope_neox", "np.asarray(positions, dtype=np.float64)[:, None]",
+     "(np.asarray(positions, dtype=np.float64) + 1)[:, None]"),             # position off by one
+    ("rope_neox", "c = np.cos(a)[:, None, :]", "c = np.cos(a)[:, None, :] * 0 + 1"),  # dropped cos
+    ("rope_inv_freq", "-2.0 * i / float(head_dim)", "-1.0 * i / float(head_dim)"),
+    ("rope_inv_freq", "np.power(float(theta),", "np.power(10000.0,"),      # base ignored
+    # rounding
+    ("f64_to_bf16_bits", "r = np.rint(xf / ulp) * ulp", "r = np.trunc(xf / ulp) * ulp"),
+    ("f64_to_bf16_bits", "r = np.rint(xf / ulp) * ulp",
+     "xf = xf.astype(np.float32).astype(np.float64)\n    r = np.rint(xf / ulp) * ulp"),  # double rounding
+    # cache write / gather
+    ("rope_cache_write", "blk, off = divmod(slot, B)", "off, blk = divmod(slot, B)"),
+    ("rope_cache_write", "v_store = heads[:, H + Hkv:]",
+     "v_store = from_f64(rope_neox(x[:, H + Hkv:], positions, theta), dtype)"),  # v rotated
+    ("rope_cache_write", "k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)",
+     "k_rot = x[:, H:H + Hkv]"),                                            # k not rotated
+    ("rope_cache_write", "k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)",
+     "k_rot = rope_neox(x[:, H + Hkv:], positions, theta)"),                # k from v columns
+    ("gather_kv", "off = j % B", "off = (j + 1) % B"),
+    ("gather_kv", "V = to_f64(np.asarray(v_cache)[blk, :, :, off], dtype)",
+     "V = to_f64(np.asarray(v_cache)[blk, :, off % np.asarray(v_cache).shape[2], :], dtype)"),
+    # attention
+    ("causal_visible", "<= pq[:, None]", "< pq[:, None]"),
+    ("causal_visible", "pq = c - n + np.arange(n)", "pq = np.arange(n)"),   # top-left alignment
+    ("softmax_rows", "return w / w.sum(axis=-1, keepdims=True)", "return w"),
+    ("softmax_rows", "np.exp(zm - m)", "np.exp(2.0 * (zm - m))"),
+    ("kv_head_for", "h // (num_heads // num_kv_heads)", "h % num_kv_heads"),
+    ("default_scale", "float(head_dim) ** -0.5", "float(head_dim) ** -1.0"),
+    ("attention_varlen", "out[r0:r1, h, :] = pi @ V[:, g, :]", "out[r0:r1, h, :] = pi @ K[:, g, :]"),
+    ("attention_varlen", "z = scale * (qf[r0:r1, h, :] @ K[:, g, :].T)",
+     "z = scale * (qf[r0:r1, h, :] @ V[:, g, :].T)"),
+    ("attention_varlen", "n, c = r1 - r0, int(context_lens[s])", "n, c = r1 - r0, int(context_lens[s]) - 1"),
+]
+
+
+def _mutant(fname, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(R, fname)))
+    assert old in src, (fname, old)
+    ns = dict(vars(R))
+    exec(compile(src.replace(old, new, 1), f"<mutant {fname}>", "exec"), ns)
+    return ns[fname]
+
+
+@pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
+def test_mutation_is_caught(monkeypatch, fname, old, new):
+    monkeypatch.setattr(R, fname, _mutant(fname, old, new))
+    for pin in pins.ALL_PINS:
+        try:
+            pin(R)
+        except Exception:
+            return
+    pytest.fail(f"no pin caught the mutation in {fname}: {new!r}")

@@ -1,0 +1,10 @@
+"""The CPU oracle against its pins (see tests/pins.py for what each checks)."""
+import pytest
+
+import oracle.reference as R
+import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(R)
