@@ -1,0 +1,253 @@
+"""Benchmark of the paged GQA attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Headline workload: Qwen2-7B-shaped long-context paged decode, bf16 (28 query
+heads, 4 KV heads, head_dim 128, block 16, batch 64, contexts log-uniform in
+[2048, 32768]).  One step = qwen2_rope_cache_write of the 64 new tokens (rotate
+q/k, write k/v into the paged cache) + qwen2_attn_decode_paged (split-K
+partial kernel + merge kernel).  ``value`` is KV bytes read per step divided
+by the step time (GB/s), inputs resident in HBM.  The KV pool (~2.2 GB) is far
+larger than the 256 MB last-level cache, so every step streams KV from HBM.
+
+Also reported on the same line: Qwen2-7B varlen causal prefill (8 sequences
+of 128..512 tokens) TFLOP/s, and the mixed TP=2-share batch in tokens/s, plus
+the roofline of the dominant decode kernel and the CPU oracle baseline.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_decode(steps, warmup):
+    import torch
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    log("generating the long-context decode workload")
+    b = W.qwen2_long_decode()
+    dev = runner.DeviceStep(b)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        dev.step()
+    torch.cuda.synchronize()
+    ev = [_events(3) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        dev.rope_write()
+        ev[i][1].record()
+        dev.decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    rope_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+    kv = b.decode_kv_bytes()
+    alg = b.decode_bytes()
+    return dict(batch=b, wall_ms=wall * 1e3, step_ms=step_ms, rope_ms=rope_ms, decode_ms=dec_ms,
+                kv_bytes=kv, decode_alg_bytes=alg, rope_bytes=b.rope_write_bytes())
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    b = W.qwen2_prefill()
+    dev = runner.DeviceStep(b)
+    for _ in range(warmup):
+        dev.step()
+    torch.cuda.synchronize()
+    ev = [_events(3) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        dev.rope_write()
+        ev[i][1].record()
+        dev.prefill()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    rope_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pf_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    flops = b.prefill_flops()
+    return dict(tokens=b.num_tokens, flops=flops, prefill_ms=pf_ms, rope_ms=rope_ms,
+                rope_bytes=b.rope_write_bytes())
+
+
+def bench_mixed(steps, warmup):
+    import torch
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    b = W.mixed_tp2()
+    dev = runner.DeviceStep(b)
+    for _ in range(warmup):
+        dev.step()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(steps):
+        dev.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return dict(tokens=b.num_tokens, step_ms=ms, prefill_flops=b.prefill_flops(),
+                decode_kv_bytes=b.decode_kv_bytes())
+
+
+def cpu_baseline(batch, budget_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the same decode
+    workload: the rope + cache write of all new tokens once (setup, not
+    timed: it copies the whole pool), then the decode attention of whole
+    sequences in batch order until about budget_s of work is done."""
+    import oracle.reference as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    sh = batch.shape
+    q_out, kc, vc = R.rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
+                                       batch.k_cache, batch.v_cache, sh.num_heads, sh.num_kv_heads,
+                                       sh.head_dim, sh.block_size, sh.rope_theta)
+    t_all, kv, n, ctx_tokens = 0.0, 0, 0, 0
+    for s in range(batch.num_seqs):
+        t0 = time.perf_counter()
+        R.attention_decode(q_out[s:s + 1], kc, vc, batch.block_tables[s:s + 1],
+                           batch.context_lens[s:s + 1], sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                           sh.block_size, sh.dtype)
+        t_all += time.perf_counter() - t0
+        c = int(batch.context_lens[s])
+        kv += c * 2 * sh.num_kv_heads * sh.head_dim * sh.elem_bytes
+        ctx_tokens += c
+        n += 1
+        if t_all >= budget_s:
+            break
+    return {"value": round(kv / t_all / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"decode attention of the first {n} of {batch.num_seqs} sequences "
+                      f"({ctx_tokens} context tokens, {kv / 1e6:.1f} MB of KV) in {t_all:.1f} s, "
+                      "float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-decode", action="store_true", help="time the decode workload only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no "
+              "multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_gqa_attention_neox_amd import binding
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.lib()
+
+    dec = bench_decode(args.steps, args.warmup)
+    log(f"decode: step {dec['step_ms']:.3f} ms (rope {dec['rope_ms']:.3f}, decode {dec['decode_ms']:.3f})")
+    res = {}
+    if not args.only_decode:
+        res["prefill"] = bench_prefill(args.steps, args.warmup)
+        log(f"prefill: {res['prefill']['prefill_ms']:.3f} ms")
+        res["mixed"] = bench_mixed(args.steps, args.warmup)
+        log(f"mixed: {res['mixed']['step_ms']:.3f} ms")
+
+    b = dec["batch"]
+    value = dec["kv_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
+    achieved = dec["decode_alg_bytes"] / (dec["decode_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": "paged GQA decode KV-read GB/s (%HBM peak); prefill TFLOP/s; Qwen2-7B shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen2-7b paged decode: 28 q / 4 kv heads, head_dim 128, block 16, "
+                        "batch 64, contexts log-uniform [2048, 32768], seed 4",
+            "global_batch": int(b.num_seqs),
+            "seq_len": int(b.context_lens.max()),
+            "mean_context": float(b.context_lens.mean()),
+            "kv_bytes_per_step": int(dec["kv_bytes"]),
+            "parallelism": "single-gpu",
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(b.num_seqs / (dec["step_ms"] * 1e-3), 1),
+        "wall_ms_per_step": round(dec["wall_ms"], 4),
+        "roofline": {
+            "kernel": "qwen2_attn_decode_paged (split-K partial + merge)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": int(dec["decode_alg_bytes"]),
+            "avg_launch_ms": round(dec["decode_ms"], 4),
+        },
+        "rope_cache_write": {"ms": round(dec["rope_ms"], 4), "bytes": dec["rope_bytes"],
+                             "GB/s": round(dec["rope_bytes"] / (dec["rope_ms"] * 1e-3) / 1e9, 2)},
+    }
+    if "prefill" in res:
+        p = res["prefill"]
+        tf = p["flops"] / (p["prefill_ms"] * 1e-3) / 1e12
+        out["prefill"] = {
+            "workload": "qwen2-7b varlen causal prefill: 8 seqs, lengths U[128,512], 28 q / 4 kv, seed 3",
+            "tokens": p["tokens"], "causal_gflop": round(p["flops"] / 1e9, 3),
+            "prefill_ms": round(p["prefill_ms"], 4), "TFLOP/s": round(tf, 2),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "rope_cache_write_ms": round(p["rope_ms"], 4),
+            "rope_cache_write_GB/s": round(p["rope_bytes"] / (p["rope_ms"] * 1e-3) / 1e9, 2),
+            "tokens_per_s": round(p["tokens"] / ((p["prefill_ms"] + p["rope_ms"]) * 1e-3), 1),
+        }
+    if "mixed" in res:
+        m = res["mixed"]
+        out["mixed"] = {
+            "workload": "qwen2-7b tp=2 share mixed step: 4x512 prefill chunks + 96 decodes, seed 5",
+            "step_ms": round(m["step_ms"], 4),
+            "tokens_per_s": round(m["tokens"] / (m["step_ms"] * 1e-3), 1),
+        }
+    if not args.no_cpu:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(b)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * qwen2_attn.h -- C ABI of the paged GQA attention library (libqwen2attn.so)
+ * for one AMD MI355X (gfx950).
+ *
+ * What it computes: the attention core of a Qwen2 decoder layer as the
+ * reference pages describe it running in vLLM.
+ *   - The fused QKV projection output is split by columns into q, k, v
+ *     ("Qwen2大模型架构解析与vLLM优化实践", §2.2 QKVParallelLinear; §4.3
+ *     packed_modules_mapping q_proj/k_proj/v_proj -> qkv_proj).
+ *   - q and k are rotated with rotary position embedding over the whole head
+ *     dimension with base rope_theta (same page, §2.2 get_rope(head_dim,
+ *     rotary_dim=head_dim, max_position, base=rope_theta); "Qwen2 模型结构代码详解",
+ *     §2: rope_theta 1e6).  Pairing is NeoX (element i with i + d/2).
+ *   - k and v are written into a KV cache cut into fixed-size blocks handed
+ *     out like OS pages ("vLLM 部署 Qwen", §2.1 PagedAttention).
+ *   - Causal grouped-query attention: query head h reads KV head
+ *     h / (num_heads / num_kv_heads) ("Qwen2 模型结构代码详解", §2: 28:4, seven
+ *     q heads per KV group), scores scaled by head_dim^-0.5 (same section),
+ *     for packed variable-length prefill ("Qwen 开源工程笔记", §3 flash-attn
+ *     varlen) and single-token paged decode ("vLLM 部署 Qwen", §2.1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: every array argument is a DEVICE pointer unless the comment says
+ *   HOST.  The caller owns all memory; the library allocates nothing, keeps
+ *   no pointer after returning and holds no global mutable state except a
+ *   thread-local error string.  Entry points are thread-safe.
+ * Streams: every call enqueues its kernels on `stream` (0 = the null stream)
+ *   and returns without synchronising.
+ * dtype: QW_BF16 (bfloat16 storage, fp32 arithmetic) or QW_F32.  q, k, v,
+ *   q_out, out and both caches share the one dtype.
+ * Rows: a "row" is one token.  Within a row the heads are contiguous, each
+ *   head_dim elements long.  *_row_stride is the distance between rows in
+ *   ELEMENTS (not bytes); it must be >= the row's width and keep every row
+ *   16-byte aligned.  Base pointers must be 16-byte aligned.
+ * Cache layout (both caches hold num_blocks blocks of block_size tokens):
+ *   k_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *   v_cache [num_blocks][num_kv_heads][head_dim][block_size]
+ *   A token at logical position p of sequence s lives in physical block
+ *   block_tables[s][p / block_size] at offset p % block_size; its slot is
+ *   block * block_size + offset.
+ * Supported shapes: head_dim 64 or 128, block_size 16, num_heads a multiple
+ *   of num_kv_heads, group num_heads/num_kv_heads <= 16.
+ * Errors: host-side validation runs before any launch.  A failing call
+ *   returns a nonzero qw_status, launches nothing and records a message for
+ *   qwen2_last_error().  Zero-size work returns QW_OK without a launch.
+ *   A HIP launch failure returns QW_ERR_HIP.
+ * Device metadata contract (device data the host does not read): positions
+ *   in [0, max_position); slots in [-1, num_blocks*block_size) with no slot
+ *   named twice in one call; block ids of the first ceil(c/B) table entries
+ *   in [0, num_blocks); 1 <= context_lens[s] <= max_context_len; query rows
+ *   of a sequence sit at positions c - n .. c - 1.  Kernels bounds-check
+ *   positions, slots and block ids: a token with an out-of-range position or
+ *   slot is not written (its q_out row is set to NaN), and a sequence that
+ *   names an out-of-range block produces NaN outputs -- never an
+ *   out-of-bounds access.  qwen2_check_metadata_host() verifies the whole
+ *   contract on host copies.
+ * Order per layer step: qwen2_rope_cache_write, then qwen2_attn_prefill_varlen
+ *   and/or qwen2_attn_decode_paged, on the same stream.
+ */
+#ifndef QWEN2_ATTN_H
+#define QWEN2_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QW_OK = 0,
+  QW_ERR_NULL = 1,         /* a required pointer is NULL */
+  QW_ERR_SHAPE = 2,        /* inconsistent sizes or strides */
+  QW_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head_dim, block_size, dtype, group) */
+  QW_ERR_ALIGN = 4,        /* base pointer or row stride breaks 16-byte alignment */
+  QW_ERR_WORKSPACE = 5,    /* workspace missing or too small */
+  QW_ERR_METADATA = 6,     /* qwen2_check_metadata_host found a violation */
+  QW_ERR_HIP = 7           /* a HIP runtime call or launch failed */
+} qw_status;
+
+typedef enum { QW_F32 = 0, QW_BF16 = 1 } qw_dtype;
+
+/*
+ * Fill the rotary table: for p < max_position, i < rotary_dim/2,
+ *   cos_sin[p][i]                = cos(p * f_i)
+ *   cos_sin[p][rotary_dim/2 + i] = sin(p * f_i),  f_i = rope_theta^(-2i/rotary_dim)
+ * computed in float64 on the device and stored as float32 (so the angle is
+ * never formed in float32, which at p ~ 32767 would be off by ~1e-3 rad).
+ * "Qwen2大模型架构解析与vLLM优化实践", §2.2 (get_rope(..., max_position, base));
+ * "Qwen2 模型结构代码详解", §3 (max_model_len becomes max_position).
+ * cos_sin: device, float32 [max_position][rotary_dim], written.
+ * Requires max_position >= 1, rotary_dim even in [2, 256], rope_theta > 0.
+ * Call once per (theta, rotary_dim, max_position); the table is read-only after.
+ */
+int qwen2_rope_table_init(float* cos_sin, int max_position, int rotary_dim,
+                          double rope_theta, hipStream_t stream);
+
+/*
+ * Rotate q and k of num_tokens tokens and write k, v into the paged cache.
+ *   q  [T][num_heads][head_dim]     (q_row_stride elements between tokens)
+ *   k  [T][num_kv_heads][head_dim]  (k_row_stride)
+ *   v  [T][num_kv_heads][head_dim]  (v_row_stride)
+ * q, k, v are typically column views of one fused QKV tensor
+ * [T][(H + 2 Hkv) * d] (row stride (H + 2 Hkv) * d for all three).
+ * For token t at position p = positions[t], every q and k head is rotated
+ * (NeoX pairs (i, i + d/2), angle from cos_sin row p):
+ *   y_i = x_i cos - x_{i+d/2} sin,   y_{i+d/2} = x_{i+d/2} cos + x_i sin
+ * in float32 and rounded once to the storage dtype.  Rotated q goes to
+ * q_out [T][num_heads][head_dim] (q_out_row_stride; q_out may equal q for
+ * an in-place update, any other overlap is undefined).  If slot_mapping[t]
+ * >= 0, rotated k goes to k_cache[slot/B][g][slot%B][:] and v is copied bit
+ * for bit to v_cache[slot/B][g][:][slot%B]; slot -1 writes nothing.  Slots
+ * not named are left untouched.
+ * cos_sin: table from qwen2_rope_table_init with rotary_dim == head_dim and
+ * max_position rows (max_position * head_dim floats are readable).  positions, slot_mapping: device int32 [T].
+ * "vLLM 部署 Qwen", §2.1 (paged KV cache); "Qwen2大模型架构解析与vLLM优化实践",
+ * §7.3 (RoPE as one fused kernel).
+ */
+int qwen2_rope_cache_write(const void* q, int64_t q_row_stride,
+                           void* q_out, int64_t q_out_row_stride,
+                           const void* k, int64_t k_row_stride,
+                           const void* v, int64_t v_row_stride,
+                           const int32_t* positions, const int32_t* slot_mapping,
+                           const float* cos_sin, int max_position,
+                           void* k_cache, void* v_cache, int num_blocks,
+                           int num_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int dtype, hipStream_t stream);
+
+/*
+ * Causal GQA attention for packed variable-length query rows (prefill and
+ * chunked prefill) over the paged cache.
+ *   q   [num_tokens][num_heads][head_dim], already rotated (q_row_stride)
+ *   out [num_tokens][num_heads][head_dim], written (out_row_stride)
+ *   cu_seqlens_q [num_seqs + 1]: sequence s owns rows cu[s] .. cu[s+1]-1,
+ *     cu[0] = 0, cu[num_seqs] <= num_tokens; rows outside every sequence are
+ *     not written.
+ *   context_lens [num_seqs]: keys of sequence s, the new rows included
+ *     (c >= n = cu[s+1] - cu[s]); row i sits at position c - n + i and
+ *     attends to keys 0 .. c - n + i.
+ *   block_tables [num_seqs][max_blocks_per_seq] int32.
+ * max_query_len >= every n (sizes the grid), max_context_len >= every c.
+ * scale is the softmax scaling, normally head_dim^-0.5.  Scores and softmax
+ * are float32; bf16 uses matrix-core (MFMA) products with fp32 accumulation.
+ * The cache must already hold every key the rows attend to (call
+ * qwen2_rope_cache_write for the new tokens first).
+ * "Qwen 开源工程笔记", §3 (varlen packed prefill); "Qwen2大模型架构解析与vLLM
+ * 优化实践", §7.3 (causal mask).
+ */
+int qwen2_attn_prefill_varlen(const void* q, int64_t q_row_stride,
+                              const void* k_cache, const void* v_cache, int num_blocks,
+                              const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              void* out, int64_t out_row_stride,
+                              int num_seqs, int num_tokens, int max_query_len,
+                              int max_context_len, int num_heads, int num_kv_heads,
+                              int head_dim, int block_size, float scale, int dtype,
+                              hipStream_t stream);
+
+/*
+ * Bytes of device workspace qwen2_attn_decode_paged needs for these sizes
+ * (0 when it needs none).  The same arguments must be passed to the decode
+ * call.  Returns (size_t)-1 for unsupported or invalid sizes.
+ */
+size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int dtype);
+
+/*
+ * Single-token paged decode: query row s of q [num_seqs][num_heads][head_dim]
+ * (q_row_stride) sits at position context_lens[s] - 1 and attends to all
+ * context_lens[s] keys of sequence s (its own key included: write it with
+ * qwen2_rope_cache_write first).  out [num_seqs][num_heads][head_dim]
+ * (out_row_stride) is written.  Long contexts are split into partitions
+ * whose partial softmax states are merged exactly (log-sum-exp) in a second
+ * pass; workspace (device, workspace_bytes >=
+ * qwen2_attn_decode_workspace_size(...)) holds those partial states and is
+ * scratch: its contents on entry do not matter.
+ * "vLLM 部署 Qwen", §2.1 and §4.1 (paged KV access dominates decode).
+ */
+int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride,
+                            const void* k_cache, const void* v_cache, int num_blocks,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            void* out, int64_t out_row_stride,
+                            void* workspace, size_t workspace_bytes,
+                            int num_seqs, int max_context_len, int num_heads,
+                            int num_kv_heads, int head_dim, int block_size, float scale,
+                            int dtype, hipStream_t stream);
+
+/*
+ * Verify the device-metadata contract on HOST copies (tests, debugging).
+ * positions, slot_mapping: HOST int32 [num_tokens] (either may be NULL to
+ * skip it).  cu_seqlens_q: HOST int32 [num_seqs + 1], or NULL for a decode
+ * batch (row s = sequence s).  context_lens: HOST int32 [num_seqs].
+ * block_tables: HOST int32 [num_seqs][max_blocks_per_seq].
+ * Checks: position/slot ranges, no duplicate slot, cu monotone from 0,
+ * 1 <= n <= c <= max_context_len, n <= max_query_len (when > 0), used
+ * block ids in range, positions[t] == c - n + i for the rows of each
+ * sequence, and slot_mapping[t] naming the block-table slot of that
+ * position.  Returns QW_OK or QW_ERR_METADATA (first violation in
+ * qwen2_last_error()).  No HIP call is made.
+ */
+int qwen2_check_metadata_host(const int32_t* positions, const int32_t* slot_mapping,
+                              int num_tokens, const int32_t* cu_seqlens_q,
+                              const int32_t* context_lens, const int32_t* block_tables,
+                              int num_seqs, int max_blocks_per_seq, int num_blocks,
+                              int block_size, int max_position, int max_context_len,
+                              int max_query_len);
+
+/* Static text for a qw_status value. */
+const char* qwen2_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* qwen2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWEN2_ATTN_H */

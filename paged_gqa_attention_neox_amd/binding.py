@@ -1,0 +1,219 @@
+"""ctypes binding of libqwen2attn.so (declared in include/qwen2_attn.h).
+
+Argument marshalling only: each function takes torch tensors (device memory
+owned by the caller), passes their data pointers, row strides and sizes to
+the C entry point of the same name on the current HIP stream, and raises
+``QwenAttnError`` on a nonzero status.  Every step of the computation runs
+in the library's HIP kernels; there is no Python or CPU fallback.
+
+Storage dtypes: ``torch.bfloat16`` (QW_BF16) and ``torch.float32`` (QW_F32).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqwen2attn.so")
+
+QW_F32, QW_BF16 = 0, 1
+STATUS = {0: "QW_OK", 1: "QW_ERR_NULL", 2: "QW_ERR_SHAPE", 3: "QW_ERR_UNSUPPORTED",
+          4: "QW_ERR_ALIGN", 5: "QW_ERR_WORKSPACE", 6: "QW_ERR_METADATA", 7: "QW_ERR_HIP"}
+
+# exported symbols and their C signatures (mirrors include/qwen2_attn.h)
+_p, _i, _i64, _f, _d, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_double, ctypes.c_size_t)
+SIGNATURES = {
+    "qwen2_rope_table_init": (_i, [_p, _i, _i, _d, _p]),
+    "qwen2_rope_cache_write": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
+                                    _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
+    "qwen2_attn_prefill_varlen": (_i, [_p, _i64, _p, _p, _i, _p, _p, _p, _i, _p, _i64, _i, _i,
+                                       _i, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "qwen2_attn_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "qwen2_attn_decode_paged": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _i64, _p, _sz, _i,
+                                     _i, _i, _i, _i, _i, _f, _i, _p]),
+    "qwen2_check_metadata_host": (_i, [_p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i]),
+    "qwen2_status_string": (ctypes.c_char_p, [_i]),
+    "qwen2_last_error": (ctypes.c_char_p, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class QwenAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_gqa_attention_neox_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise QwenAttnError(fn, status, lib().qwen2_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return QW_BF16
+    if t.dtype == torch.float32:
+        return QW_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _rows(t: torch.Tensor, width: int):
+    """(pointer, row stride in elements) of a [rows][width] or [rows][heads][d]
+    view whose row elements are contiguous."""
+    if t.dim() == 3:
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError("heads within a row must be contiguous")
+    elif t.dim() == 2:
+        if t.stride(1) != 1:
+            raise ValueError("row elements must be contiguous")
+    else:
+        raise ValueError("expected a 2-D or 3-D tensor")
+    if t.shape[0] > 0 and t[0].numel() != width:
+        raise ValueError(f"row width {t[0].numel()} != {width}")
+    return t.data_ptr(), t.stride(0)
+
+
+def _i32(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return 0
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError("metadata tensors must be contiguous int32")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+def qwen2_rope_table_init(cos_sin: torch.Tensor, rope_theta: float, stream=None) -> None:
+    """cos_sin: float32 [max_position][rotary_dim] on the device, filled."""
+    if cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous() or cos_sin.dim() != 2:
+        raise TypeError("cos_sin must be a contiguous float32 [max_position][rotary_dim] tensor")
+    _check("qwen2_rope_table_init",
+           lib().qwen2_rope_table_init(cos_sin.data_ptr(), cos_sin.shape[0], cos_sin.shape[1],
+                                       float(rope_theta), _stream(stream)))
+
+
+def qwen2_rope_cache_write(q, q_out, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
+                           num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                           stream=None) -> None:
+    """q [T][H*d] (or [T][H][d]) view, q_out same shape (may be q), k and v
+    [T][Hkv*d] views (e.g. column slices of the fused QKV tensor);
+    positions, slot_mapping int32 [T]; cos_sin float32 [max_position][d];
+    caches laid out as in include/qwen2_attn.h."""
+    T = q.shape[0]
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim or cos_sin.dtype != torch.float32:
+        raise ValueError("cos_sin must be float32 [max_position][head_dim]")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dim() != 4 or t.shape[1] != num_kv_heads or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [num_blocks][num_kv_heads][..] of the q dtype")
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(q_out, num_heads * head_dim)
+    kp, ks = _rows(k, num_kv_heads * head_dim)
+    vp, vs = _rows(v, num_kv_heads * head_dim)
+    _check("qwen2_rope_cache_write",
+           lib().qwen2_rope_cache_write(qp, qs, op, os_, kp, ks, vp, vs, _i32(positions),
+                                        _i32(slot_mapping), cos_sin.data_ptr(), cos_sin.shape[0],
+                                        k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[0],
+                                        T, num_heads, num_kv_heads, head_dim, block_size,
+                                        _dtype(q), _stream(stream)))
+
+
+def qwen2_attn_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, context_lens, block_tables, out,
+                              max_query_len: int, max_context_len: int, num_heads: int,
+                              num_kv_heads: int, head_dim: int, block_size: int, scale: float,
+                              stream=None) -> None:
+    """q, out: [T][H][d] (or [T][H*d]); cu_seqlens_q int32 [S+1];
+    context_lens int32 [S]; block_tables int32 [S][max_blocks]."""
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(out, num_heads * head_dim)
+    S = context_lens.shape[0]
+    _check("qwen2_attn_prefill_varlen",
+           lib().qwen2_attn_prefill_varlen(qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                                           k_cache.shape[0], _i32(cu_seqlens_q), _i32(context_lens),
+                                           _i32(block_tables), block_tables.shape[1], op, os_, S,
+                                           q.shape[0], max_query_len, max_context_len, num_heads,
+                                           num_kv_heads, head_dim, block_size, float(scale),
+                                           _dtype(q), _stream(stream)))
+
+
+def qwen2_attn_decode_workspace_size(num_seqs: int, max_context_len: int, num_heads: int,
+                                     num_kv_heads: int, head_dim: int, block_size: int,
+                                     dtype: torch.dtype) -> int:
+    n = lib().qwen2_attn_decode_workspace_size(num_seqs, max_context_len, num_heads, num_kv_heads,
+                                               head_dim, block_size,
+                                               QW_BF16 if dtype == torch.bfloat16 else QW_F32)
+    if n == ctypes.c_size_t(-1).value:
+        raise QwenAttnError("qwen2_attn_decode_workspace_size", 3, lib().qwen2_last_error().decode())
+    return n
+
+
+def qwen2_attn_decode_paged(q, k_cache, v_cache, block_tables, context_lens, out, workspace,
+                            max_context_len: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                            block_size: int, scale: float, stream=None) -> None:
+    """q, out: [S][H][d] (or [S][H*d]); workspace: a device tensor of at
+    least qwen2_attn_decode_workspace_size(...) bytes, or None when that is 0."""
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(out, num_heads * head_dim)
+    wp = workspace.data_ptr() if workspace is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("qwen2_attn_decode_paged",
+           lib().qwen2_attn_decode_paged(qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                                         k_cache.shape[0], _i32(block_tables), block_tables.shape[1],
+                                         _i32(context_lens), op, os_, wp, wb, q.shape[0],
+                                         max_context_len, num_heads, num_kv_heads, head_dim,
+                                         block_size, float(scale), _dtype(q), _stream(stream)))
+
+
+def qwen2_check_metadata_host(positions, slot_mapping, cu_seqlens_q, context_lens, block_tables,
+                              num_blocks: int, block_size: int, max_position: int,
+                              max_context_len: int, max_query_len: int = 0) -> None:
+    """Host-side contract check on numpy int32 arrays (any may be None except
+    context_lens and block_tables).  Raises QwenAttnError on a violation."""
+    def ptr(a):
+        if a is None:
+            return 0, None
+        a = np.ascontiguousarray(a, dtype=np.int32)
+        return a.ctypes.data, a
+    pp, keep1 = ptr(positions)
+    sp, keep2 = ptr(slot_mapping)
+    cp, keep3 = ptr(cu_seqlens_q)
+    lp, keep4 = ptr(context_lens)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    T = len(positions) if positions is not None else (len(slot_mapping) if slot_mapping is not None else 0)
+    _check("qwen2_check_metadata_host",
+           lib().qwen2_check_metadata_host(pp, sp, T, cp, lp, bt.ctypes.data, len(context_lens),
+                                           bt.shape[1], num_blocks, block_size, max_position,
+                                           max_context_len, max_query_len))
+    del keep1, keep2, keep3, keep4
+
+
+def status_string(status: int) -> str:
+    return lib().qwen2_status_string(status).decode()

@@ -1,0 +1,58 @@
+// Internal launcher interface between the C-ABI layer (qwen2_attn_api.cpp)
+// and the kernel translation units.  Arguments have been validated by the
+// caller; launchers only pick a kernel variant and launch it.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qw {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+struct RopeWriteArgs {
+  const void* q; int64_t q_stride;
+  void* q_out; int64_t q_out_stride;
+  const void* k; int64_t k_stride;
+  const void* v; int64_t v_stride;
+  const int32_t* positions;
+  const int32_t* slots;
+  const float* cos_sin; int max_position;
+  void* k_cache; void* v_cache; int num_blocks;
+  int num_tokens, num_heads, num_kv_heads, head_dim, block_size;
+  int dtype;
+};
+
+struct AttnArgs {
+  const void* q; int64_t q_stride;
+  const void* k_cache; const void* v_cache; int num_blocks;
+  const int32_t* cu_seqlens;     // nullptr: one query row per sequence (decode)
+  const int32_t* context_lens;
+  const int32_t* block_tables; int max_blocks;
+  void* out; int64_t out_stride;
+  int num_seqs, num_tokens, max_query_len, max_context_len;
+  int num_heads, num_kv_heads, head_dim, block_size;
+  float scale;
+  int dtype;
+  void* workspace; size_t workspace_bytes;
+};
+
+// decode plan: which kernel runs and how much workspace it needs
+struct DecodePlan {
+  bool fast;          // split-K bf16 kernel (else the generic kernel)
+  int part_tokens;    // tokens per partition
+  int max_parts;      // partitions of the longest context
+  size_t ws_bytes;
+};
+
+DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
+                       int head_dim, int block_size, int dtype);
+
+hipError_t launch_rope_table(float* tab, int max_position, int rotary_dim, double theta,
+                             hipStream_t stream);
+hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream);
+hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace qw

@@ -1,0 +1,327 @@
+// C ABI of libqwen2attn.so: argument validation, status codes, dispatch to
+// the kernel launchers.  Declared (and documented) in include/qwen2_attn.h.
+// No allocation, no retained state except the thread-local error message.
+#include "../../include/qwen2_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return QW_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) { return dtype == QW_BF16 ? 2 : 4; }
+
+// shared checks of the head layout
+int check_heads(int num_heads, int num_kv_heads, int head_dim, int block_size, int dtype) {
+  if (dtype != QW_BF16 && dtype != QW_F32) return fail(QW_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(QW_ERR_SHAPE, "num_heads=%d num_kv_heads=%d must be positive", num_heads, num_kv_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(QW_ERR_SHAPE, "num_heads=%d is not a multiple of num_kv_heads=%d", num_heads, num_kv_heads);
+  if (num_heads / num_kv_heads > 16)
+    return fail(QW_ERR_UNSUPPORTED, "group %d > 16 not supported", num_heads / num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(QW_ERR_UNSUPPORTED, "head_dim=%d not supported (64 or 128)", head_dim);
+  if (block_size != 16) return fail(QW_ERR_UNSUPPORTED, "block_size=%d not supported (16)", block_size);
+  return QW_OK;
+}
+
+// a [rows][width] view with row stride `stride` (elements)
+int check_rows(const char* name, const void* p, int64_t stride, int64_t width, int dtype) {
+  if (!p) return fail(QW_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(QW_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (stride < width) return fail(QW_ERR_SHAPE, "%s row stride %lld < row width %lld", name,
+                                  static_cast<long long>(stride), static_cast<long long>(width));
+  if ((stride * elem_size(dtype)) % 16 != 0)
+    return fail(QW_ERR_ALIGN, "%s row stride %lld elements breaks 16-byte alignment", name,
+                static_cast<long long>(stride));
+  return QW_OK;
+}
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) return fail(QW_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qwen2_status_string(int status) {
+  switch (status) {
+    case QW_OK: return "ok";
+    case QW_ERR_NULL: return "null pointer";
+    case QW_ERR_SHAPE: return "bad shape or stride";
+    case QW_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QW_ERR_ALIGN: return "misaligned pointer or stride";
+    case QW_ERR_WORKSPACE: return "workspace missing or too small";
+    case QW_ERR_METADATA: return "metadata contract violated";
+    case QW_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* qwen2_last_error(void) { return g_err; }
+
+int qwen2_rope_table_init(float* cos_sin, int max_position, int rotary_dim, double rope_theta,
+                          hipStream_t stream) {
+  if (!cos_sin) return fail(QW_ERR_NULL, "cos_sin is NULL");
+  if (max_position < 1) return fail(QW_ERR_SHAPE, "max_position=%d < 1", max_position);
+  if (rotary_dim < 2 || rotary_dim > 256 || rotary_dim % 2)
+    return fail(QW_ERR_SHAPE, "rotary_dim=%d must be even in [2, 256]", rotary_dim);
+  if (!(rope_theta > 0.0)) return fail(QW_ERR_SHAPE, "rope_theta must be > 0");
+  return launched(qw::launch_rope_table(cos_sin, max_position, rotary_dim, rope_theta, stream));
+}
+
+int qwen2_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int64_t q_out_row_stride,
+                           const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                           const int32_t* positions, const int32_t* slot_mapping,
+                           const float* cos_sin, int max_position, void* k_cache, void* v_cache,
+                           int num_blocks, int num_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int dtype, hipStream_t stream) {
+  int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st) return st;
+  if (num_tokens < 0) return fail(QW_ERR_SHAPE, "num_tokens=%d < 0", num_tokens);
+  if (num_blocks < 0) return fail(QW_ERR_SHAPE, "num_blocks=%d < 0", num_blocks);
+  if (max_position < 1) return fail(QW_ERR_SHAPE, "max_position=%d < 1", max_position);
+  if (num_tokens == 0) return ok();
+  const int64_t qw = static_cast<int64_t>(num_heads) * head_dim;
+  const int64_t kw = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if ((st = check_rows("q", q, q_row_stride, qw, dtype))) return st;
+  if ((st = check_rows("q_out", q_out, q_out_row_stride, qw, dtype))) return st;
+  if ((st = check_rows("k", k, k_row_stride, kw, dtype))) return st;
+  if ((st = check_rows("v", v, v_row_stride, kw, dtype))) return st;
+  if (q_out != q) {
+    // q_out may equal q (in place); any other overlap with the q rows is undefined
+    const char* a0 = static_cast<const char*>(q);
+    const char* a1 = a0 + ((num_tokens - 1) * q_row_stride + qw) * elem_size(dtype);
+    const char* b0 = static_cast<const char*>(q_out);
+    const char* b1 = b0 + ((num_tokens - 1) * q_out_row_stride + qw) * elem_size(dtype);
+    if (b0 < a1 && a0 < b1)
+      return fail(QW_ERR_SHAPE, "q_out overlaps q without being equal to it");
+  }
+  if (!positions) return fail(QW_ERR_NULL, "positions is NULL");
+  if (!slot_mapping) return fail(QW_ERR_NULL, "slot_mapping is NULL");
+  if (!cos_sin) return fail(QW_ERR_NULL, "cos_sin is NULL");
+  if (!aligned16(cos_sin)) return fail(QW_ERR_ALIGN, "cos_sin is not 16-byte aligned");
+  if (num_blocks > 0 && (!k_cache || !v_cache)) return fail(QW_ERR_NULL, "k_cache/v_cache is NULL");
+  if (num_blocks > 0 && (!aligned16(k_cache) || !aligned16(v_cache)))
+    return fail(QW_ERR_ALIGN, "k_cache/v_cache is not 16-byte aligned");
+  qw::RopeWriteArgs a{};
+  a.q = q; a.q_stride = q_row_stride;
+  a.q_out = q_out; a.q_out_stride = q_out_row_stride;
+  a.k = k; a.k_stride = k_row_stride;
+  a.v = v; a.v_stride = v_row_stride;
+  a.positions = positions; a.slots = slot_mapping;
+  a.cos_sin = cos_sin; a.max_position = max_position;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.num_blocks = num_blocks;
+  a.num_tokens = num_tokens; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim; a.block_size = block_size; a.dtype = dtype;
+  return launched(qw::launch_rope_cache_write(a, stream));
+}
+
+static int check_attn_common(const void* q, int64_t q_row_stride, const void* k_cache,
+                             const void* v_cache, int num_blocks, const int32_t* context_lens,
+                             const int32_t* block_tables, int max_blocks_per_seq, const void* out,
+                             int64_t out_row_stride, int num_seqs, int max_context_len,
+                             int num_heads, int num_kv_heads, int head_dim, int block_size,
+                             float scale, int dtype) {
+  int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (st) return st;
+  const int64_t qw = static_cast<int64_t>(num_heads) * head_dim;
+  if ((st = check_rows("q", q, q_row_stride, qw, dtype))) return st;
+  if ((st = check_rows("out", out, out_row_stride, qw, dtype))) return st;
+  if (num_blocks < 1) return fail(QW_ERR_SHAPE, "num_blocks=%d < 1", num_blocks);
+  if (!k_cache || !v_cache) return fail(QW_ERR_NULL, "k_cache/v_cache is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(QW_ERR_ALIGN, "k_cache/v_cache is not 16-byte aligned");
+  if (!context_lens) return fail(QW_ERR_NULL, "context_lens is NULL");
+  if (!block_tables) return fail(QW_ERR_NULL, "block_tables is NULL");
+  if (max_context_len < 1) return fail(QW_ERR_SHAPE, "max_context_len=%d < 1", max_context_len);
+  if (max_blocks_per_seq < 1 ||
+      static_cast<int64_t>(max_blocks_per_seq) * block_size < max_context_len)
+    return fail(QW_ERR_SHAPE, "max_blocks_per_seq=%d cannot hold max_context_len=%d",
+                max_blocks_per_seq, max_context_len);
+  if (!(scale > 0.0f) || !(scale < 1e30f)) return fail(QW_ERR_SHAPE, "scale must be finite and > 0");
+  (void)num_seqs;
+  return QW_OK;
+}
+
+int qwen2_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k_cache,
+                              const void* v_cache, int num_blocks, const int32_t* cu_seqlens_q,
+                              const int32_t* context_lens, const int32_t* block_tables,
+                              int max_blocks_per_seq, void* out, int64_t out_row_stride,
+                              int num_seqs, int num_tokens, int max_query_len, int max_context_len,
+                              int num_heads, int num_kv_heads, int head_dim, int block_size,
+                              float scale, int dtype, hipStream_t stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0)
+    return fail(QW_ERR_SHAPE, "negative size (num_seqs=%d num_tokens=%d max_query_len=%d)",
+                num_seqs, num_tokens, max_query_len);
+  if (num_seqs > 65535) return fail(QW_ERR_UNSUPPORTED, "num_seqs=%d > 65535", num_seqs);
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) {
+    int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
+    return st ? st : ok();
+  }
+  int st = check_attn_common(q, q_row_stride, k_cache, v_cache, num_blocks, context_lens,
+                             block_tables, max_blocks_per_seq, out, out_row_stride, num_seqs,
+                             max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                             scale, dtype);
+  if (st) return st;
+  if (!cu_seqlens_q) return fail(QW_ERR_NULL, "cu_seqlens_q is NULL");
+  if (max_query_len > max_context_len)
+    return fail(QW_ERR_SHAPE, "max_query_len=%d > max_context_len=%d", max_query_len, max_context_len);
+  qw::AttnArgs a{};
+  a.q = q; a.q_stride = q_row_stride;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.num_blocks = num_blocks;
+  a.cu_seqlens = cu_seqlens_q; a.context_lens = context_lens;
+  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq;
+  a.out = out; a.out_stride = out_row_stride;
+  a.num_seqs = num_seqs; a.num_tokens = num_tokens;
+  a.max_query_len = max_query_len; a.max_context_len = max_context_len;
+  a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.scale = scale; a.dtype = dtype;
+  return launched(qw::launch_prefill(a, stream));
+}
+
+size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size, int dtype) {
+  if (num_seqs < 0 || max_context_len < 1) return static_cast<size_t>(-1);
+  if (check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype)) return static_cast<size_t>(-1);
+  return qw::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                         dtype).ws_bytes;
+}
+
+int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride, const void* k_cache,
+                            const void* v_cache, int num_blocks, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                            int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                            int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
+                            int head_dim, int block_size, float scale, int dtype,
+                            hipStream_t stream) {
+  if (num_seqs < 0) return fail(QW_ERR_SHAPE, "num_seqs=%d < 0", num_seqs);
+  if (num_seqs > 65535) return fail(QW_ERR_UNSUPPORTED, "num_seqs=%d > 65535", num_seqs);
+  if (num_seqs == 0) {
+    int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
+    return st ? st : ok();
+  }
+  int st = check_attn_common(q, q_row_stride, k_cache, v_cache, num_blocks, context_lens,
+                             block_tables, max_blocks_per_seq, out, out_row_stride, num_seqs,
+                             max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                             scale, dtype);
+  if (st) return st;
+  const qw::DecodePlan plan = qw::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads,
+                                              head_dim, block_size, dtype);
+  if (plan.ws_bytes > 0) {
+    if (!workspace) return fail(QW_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.ws_bytes);
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(QW_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+    if (!aligned16(workspace)) return fail(QW_ERR_ALIGN, "workspace is not 16-byte aligned");
+  }
+  qw::AttnArgs a{};
+  a.q = q; a.q_stride = q_row_stride;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.num_blocks = num_blocks;
+  a.cu_seqlens = nullptr; a.context_lens = context_lens;
+  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq;
+  a.out = out; a.out_stride = out_row_stride;
+  a.num_seqs = num_seqs; a.num_tokens = num_seqs; a.max_query_len = 1;
+  a.max_context_len = max_context_len;
+  a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.scale = scale; a.dtype = dtype;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return launched(qw::launch_decode(a, plan, stream));
+}
+
+int qwen2_check_metadata_host(const int32_t* positions, const int32_t* slot_mapping, int num_tokens,
+                              const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                              const int32_t* block_tables, int num_seqs, int max_blocks_per_seq,
+                              int num_blocks, int block_size, int max_position,
+                              int max_context_len, int max_query_len) {
+  if (num_tokens < 0 || num_seqs < 0) return fail(QW_ERR_SHAPE, "negative sizes");
+  if (block_size < 1) return fail(QW_ERR_SHAPE, "block_size=%d < 1", block_size);
+  if (num_seqs > 0 && (!context_lens || !block_tables))
+    return fail(QW_ERR_NULL, "context_lens/block_tables is NULL");
+  const int64_t nslots = static_cast<int64_t>(num_blocks) * block_size;
+  if (positions) {
+    for (int t = 0; t < num_tokens; ++t)
+      if (positions[t] < 0 || positions[t] >= max_position)
+        return fail(QW_ERR_METADATA, "positions[%d]=%d outside [0, %d)", t, positions[t], max_position);
+  }
+  if (slot_mapping) {
+    std::vector<char> seen(static_cast<size_t>(nslots > 0 ? nslots : 0), 0);
+    for (int t = 0; t < num_tokens; ++t) {
+      const int sl = slot_mapping[t];
+      if (sl == -1) continue;
+      if (sl < -1 || sl >= nslots)
+        return fail(QW_ERR_METADATA, "slot_mapping[%d]=%d outside [-1, %lld)", t, sl,
+                    static_cast<long long>(nslots));
+      if (seen[sl]) return fail(QW_ERR_METADATA, "slot %d named twice (token %d)", sl, t);
+      seen[sl] = 1;
+    }
+  }
+  if (cu_seqlens_q) {
+    if (cu_seqlens_q[0] != 0) return fail(QW_ERR_METADATA, "cu_seqlens_q[0]=%d != 0", cu_seqlens_q[0]);
+    if (cu_seqlens_q[num_seqs] > num_tokens)
+      return fail(QW_ERR_METADATA, "cu_seqlens_q[%d]=%d > num_tokens=%d", num_seqs,
+                  cu_seqlens_q[num_seqs], num_tokens);
+  } else if (num_seqs > num_tokens && (positions || slot_mapping)) {
+    return fail(QW_ERR_METADATA, "decode batch: num_seqs=%d > num_tokens=%d", num_seqs, num_tokens);
+  }
+  for (int s = 0; s < num_seqs; ++s) {
+    const int r0 = cu_seqlens_q ? cu_seqlens_q[s] : s;
+    const int n = cu_seqlens_q ? cu_seqlens_q[s + 1] - r0 : 1;
+    const int c = context_lens[s];
+    if (n < 0) return fail(QW_ERR_METADATA, "cu_seqlens_q decreases at sequence %d", s);
+    if (n == 0) continue;
+    if (c < n) return fail(QW_ERR_METADATA, "sequence %d: context %d < query rows %d", s, c, n);
+    if (c > max_context_len)
+      return fail(QW_ERR_METADATA, "sequence %d: context %d > max_context_len %d", s, c, max_context_len);
+    if (max_query_len > 0 && n > max_query_len)
+      return fail(QW_ERR_METADATA, "sequence %d: %d rows > max_query_len %d", s, n, max_query_len);
+    const int nb = (c + block_size - 1) / block_size;
+    if (nb > max_blocks_per_seq)
+      return fail(QW_ERR_METADATA, "sequence %d needs %d blocks > max_blocks_per_seq %d", s, nb,
+                  max_blocks_per_seq);
+    const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
+    for (int b = 0; b < nb; ++b)
+      if (bt[b] < 0 || bt[b] >= num_blocks)
+        return fail(QW_ERR_METADATA, "block_tables[%d][%d]=%d outside [0, %d)", s, b, bt[b], num_blocks);
+    for (int i = 0; i < n; ++i) {
+      const int t = r0 + i;
+      const int p = c - n + i;
+      if (positions && positions[t] != p)
+        return fail(QW_ERR_METADATA, "positions[%d]=%d, expected %d (sequence %d row %d)", t,
+                    positions[t], p, s, i);
+      if (slot_mapping && slot_mapping[t] != -1) {
+        const int64_t want = static_cast<int64_t>(bt[p / block_size]) * block_size + p % block_size;
+        if (slot_mapping[t] != want)
+          return fail(QW_ERR_METADATA, "slot_mapping[%d]=%d, block table gives %lld", t,
+                      slot_mapping[t], static_cast<long long>(want));
+      }
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

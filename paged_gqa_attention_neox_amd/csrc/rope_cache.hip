@@ -1,0 +1,208 @@
+// Rotary table and the fused "rotate q/k + write k/v into the paged cache"
+// kernel.
+//
+// Rotary embedding over the whole head with base rope_theta
+// ("Qwen2大模型架构解析与vLLM优化实践", §2.2 get_rope; "Qwen2 模型结构代码详解",
+// §2 rope_theta = 1e6); NeoX pairing (i, i + d/2).  KV written into fixed-size
+// blocks through a slot mapping ("vLLM 部署 Qwen", §2.1 PagedAttention).  The
+// pages mention a fused RoPE kernel ("Qwen2大模型架构解析与vLLM优化实践", §7.3);
+// here rotation and cache scatter are one pass over the fused QKV rows.
+//
+// The kernel is HBM-bound: per token it reads (H + 2 Hkv) * d elements and
+// writes H * d (q_out) + 2 Hkv * d (cache) elements.  Each work item moves
+// 16-byte vectors: 8 rotation pairs (x[i..i+8], x[i+d/2..]) of one head, or
+// 8 elements of one v head.
+#include "common.h"
+#include "kernels.h"
+
+namespace qw {
+
+// ---------------------------------------------------------------------------
+// cos/sin table, float64 math stored as float32
+// ---------------------------------------------------------------------------
+__global__ void rope_table_kernel(float* __restrict__ tab, int max_position, int rot,
+                                  double theta) {
+  const int half = rot / 2;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(max_position) * half;
+  if (idx >= total) return;
+  const int p = static_cast<int>(idx / half);
+  const int i = static_cast<int>(idx % half);
+  const double f = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(rot));
+  const double a = static_cast<double>(p) * f;
+  double s, c;
+  sincos(a, &s, &c);
+  tab[static_cast<int64_t>(p) * rot + i] = static_cast<float>(c);
+  tab[static_cast<int64_t>(p) * rot + half + i] = static_cast<float>(s);
+}
+
+hipError_t launch_rope_table(float* tab, int max_position, int rotary_dim, double theta,
+                             hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(max_position) * (rotary_dim / 2);
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
+                     stream, tab, max_position, rotary_dim, theta);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 8-element vectors of the storage type
+// ---------------------------------------------------------------------------
+template <typename T> struct Vec8;
+
+template <> struct Vec8<uint16_t> {   // bf16
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint4*>(p) = w; }
+  __device__ __forceinline__ void to_f32(float (&f)[8]) const {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+  }
+  __device__ __forceinline__ void from_f32(const float (&f)[8]) {
+    w.x = pack_bf16x2(f[0], f[1]); w.y = pack_bf16x2(f[2], f[3]);
+    w.z = pack_bf16x2(f[4], f[5]); w.w = pack_bf16x2(f[6], f[7]);
+  }
+  __device__ __forceinline__ uint16_t elem(int j) const {
+    const uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
+    return static_cast<uint16_t>((j & 1) ? (x >> 16) : (x & 0xffffu));
+  }
+  static __device__ __forceinline__ uint16_t nan() { return 0x7fc0; }
+};
+
+template <> struct Vec8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void store(float* p) const {
+    *reinterpret_cast<float4*>(p) = a;
+    *reinterpret_cast<float4*>(p + 4) = b;
+  }
+  __device__ __forceinline__ void to_f32(float (&f)[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ __forceinline__ void from_f32(const float (&f)[8]) {
+    a = make_float4(f[0], f[1], f[2], f[3]);
+    b = make_float4(f[4], f[5], f[6], f[7]);
+  }
+  __device__ __forceinline__ float elem(int j) const {
+    return j == 0 ? a.x : j == 1 ? a.y : j == 2 ? a.z : j == 3 ? a.w
+         : j == 4 ? b.x : j == 5 ? b.y : j == 6 ? b.z : b.w;
+  }
+  static __device__ __forceinline__ float nan() { return __builtin_nanf(""); }
+};
+
+// ---------------------------------------------------------------------------
+// fused rotate + scatter
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) {
+  constexpr int HALF = D / 2;
+  constexpr int RCH = HALF / 8;   // rotation items per head (8 pairs each)
+  constexpr int VCH = D / 8;      // v items per head (8 elements each)
+  const int H = a.num_heads, Hkv = a.num_kv_heads, B = a.block_size;
+  const int rot_items = (H + Hkv) * RCH;
+  const int per_tok = rot_items + Hkv * VCH;
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * per_tok;
+  const int64_t cache_slots = static_cast<int64_t>(a.num_blocks) * B;
+
+  const T* q = static_cast<const T*>(a.q);            // may alias q_out (in place)
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  T* q_out = static_cast<T*>(a.q_out);
+  T* __restrict__ kc = static_cast<T*>(a.k_cache);
+  T* __restrict__ vc = static_cast<T*>(a.v_cache);
+
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int t = static_cast<int>(idx / per_tok);
+    int w = static_cast<int>(idx - static_cast<int64_t>(t) * per_tok);
+    const int pos = a.positions[t];
+    const int slot = a.slots[t];
+    const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
+    const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
+    const int64_t blk = slot_ok ? slot / B : 0;
+    const int off = slot_ok ? slot % B : 0;
+
+    if (w < rot_items) {
+      const int head = w / RCH;
+      const int i0 = (w - head * RCH) * 8;
+      const bool is_q = head < H;
+      if (!is_q && !(pos_ok && slot_ok)) continue;
+      T* dst;
+      if (is_q) {
+        dst = q_out + static_cast<int64_t>(t) * a.q_out_stride + static_cast<int64_t>(head) * D;
+        if (!pos_ok) {
+          Vec8<T> nanv;
+          float f[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = __builtin_nanf("");
+          nanv.from_f32(f);
+          nanv.store(dst + i0);
+          nanv.store(dst + HALF + i0);
+          continue;
+        }
+      } else {
+        const int gk = head - H;
+        dst = kc + ((blk * Hkv + gk) * B + off) * D;
+      }
+      const T* src = is_q ? q + static_cast<int64_t>(t) * a.q_stride + static_cast<int64_t>(head) * D
+                          : k + static_cast<int64_t>(t) * a.k_stride + static_cast<int64_t>(head - H) * D;
+      Vec8<T> x1v, x2v;
+      x1v.load(src + i0);
+      x2v.load(src + HALF + i0);
+      float x1[8], x2[8], y1[8], y2[8];
+      x1v.to_f32(x1);
+      x2v.to_f32(x2);
+      const float* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
+      const float4 c0 = *reinterpret_cast<const float4*>(cs + i0);
+      const float4 c1 = *reinterpret_cast<const float4*>(cs + i0 + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(cs + HALF + i0);
+      const float4 s1 = *reinterpret_cast<const float4*>(cs + HALF + i0 + 4);
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        y1[j] = fmaf(x1[j], cv[j], -(x2[j] * sv[j]));
+        y2[j] = fmaf(x2[j], cv[j], x1[j] * sv[j]);
+      }
+      Vec8<T> o1, o2;
+      o1.from_f32(y1);
+      o2.from_f32(y2);
+      o1.store(dst + i0);
+      o2.store(dst + HALF + i0);
+    } else {
+      if (!(pos_ok && slot_ok)) continue;
+      w -= rot_items;
+      const int gv = w / VCH;
+      const int e0 = (w - gv * VCH) * 8;
+      Vec8<T> x;
+      x.load(v + static_cast<int64_t>(t) * a.v_stride + static_cast<int64_t>(gv) * D + e0);
+      T* dst = vc + ((blk * Hkv + gv) * D + e0) * B + off;     // V tile is [d][B]
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j * B] = x.elem(j);
+    }
+  }
+}
+
+hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream) {
+  const int d = a.head_dim;
+  const int per_tok = (a.num_heads + a.num_kv_heads) * (d / 16) + a.num_kv_heads * (d / 8);
+  const int64_t total = static_cast<int64_t>(a.num_tokens) * per_tok;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 1 << 20) blocks = 1 << 20;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
+  if (a.dtype == kBF16) {
+    if (d == 128) hipLaunchKernelGGL((rope_cache_write_kernel<uint16_t, 128>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((rope_cache_write_kernel<uint16_t, 64>), grid, block, 0, stream, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((rope_cache_write_kernel<float, 128>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((rope_cache_write_kernel<float, 64>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qw

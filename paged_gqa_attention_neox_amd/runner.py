@@ -1,0 +1,115 @@
+"""Run one attention step of a workload batch through the C ABI.
+
+Uploads a ``workloads.Batch`` to device memory (torch tensors) and calls
+``qwen2_rope_cache_write`` over every token, then
+``qwen2_attn_prefill_varlen`` over the prefill sequences and
+``qwen2_attn_decode_paged`` over the decode sequences, all on the current
+stream.  Only marshalling: the arithmetic happens in the HIP library.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+_TABLES = {}
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Storage array (uint16 bf16 bits or float32) -> device tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> storage array (uint16 bits for bf16)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def rope_table(head_dim: int, theta: float, max_position: int, device="cuda") -> torch.Tensor:
+    key = (head_dim, float(theta), int(max_position), str(device))
+    t = _TABLES.get(key)
+    if t is None:
+        t = torch.empty(max_position, head_dim, dtype=torch.float32, device=device)
+        B.qwen2_rope_table_init(t, theta)
+        _TABLES[key] = t
+    return t
+
+
+class DeviceStep:
+    """Device copies of one batch plus the calls of the step."""
+
+    def __init__(self, batch, device="cuda", k_cache=None, v_cache=None):
+        sh = batch.shape
+        self.batch = batch
+        self.sh = sh
+        H, Hkv, d = sh.num_heads, sh.num_kv_heads, sh.head_dim
+        self.tdtype = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        self.qkv = to_device(batch.qkv, sh.dtype, device)
+        self.q = self.qkv[:, : H * d]
+        self.k = self.qkv[:, H * d:(H + Hkv) * d]
+        self.v = self.qkv[:, (H + Hkv) * d:]
+        T = batch.num_tokens
+        self.q_out = torch.empty(T, H, d, dtype=self.tdtype, device=device)
+        self.out = torch.full((T, H, d), float("nan"), dtype=self.tdtype, device=device)
+        self.positions = i32(batch.positions)
+        self.slots = i32(batch.slot_mapping)
+        self.k_cache = k_cache if k_cache is not None else to_device(batch.k_cache, sh.dtype, device)
+        self.v_cache = v_cache if v_cache is not None else to_device(batch.v_cache, sh.dtype, device)
+        self.cos_sin = rope_table(d, sh.rope_theta, sh.max_position, device)
+        P = batch.num_prefill
+        self.Tp = batch.num_prefill_tokens
+        if P:
+            cu, ctx, bt = batch.prefill_part()
+            self.p_cu, self.p_ctx, self.p_bt = i32(cu), i32(ctx), i32(bt)
+            self.p_max_q = int(batch.query_lens[:P].max())
+            self.p_max_c = int(ctx.max())
+        if batch.num_decode:
+            ctx, bt = batch.decode_part()
+            self.d_ctx, self.d_bt = i32(ctx), i32(bt)
+            self.d_max_c = int(ctx.max())
+            ws = B.qwen2_attn_decode_workspace_size(batch.num_decode, self.d_max_c, H, Hkv, d,
+                                                    sh.block_size, self.tdtype)
+            self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
+
+    # --- the three calls ---
+    def rope_write(self, stream=None):
+        sh = self.sh
+        B.qwen2_rope_cache_write(self.q, self.q_out, self.k, self.v, self.positions, self.slots,
+                                 self.cos_sin, self.k_cache, self.v_cache, sh.num_heads,
+                                 sh.num_kv_heads, sh.head_dim, sh.block_size, stream)
+
+    def prefill(self, stream=None):
+        if not self.batch.num_prefill:
+            return
+        sh = self.sh
+        B.qwen2_attn_prefill_varlen(self.q_out[: self.Tp], self.k_cache, self.v_cache, self.p_cu,
+                                    self.p_ctx, self.p_bt, self.out[: self.Tp], self.p_max_q,
+                                    self.p_max_c, sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                                    sh.block_size, sh.scale, stream)
+
+    def decode(self, stream=None):
+        if not self.batch.num_decode:
+            return
+        sh = self.sh
+        B.qwen2_attn_decode_paged(self.q_out[self.Tp:], self.k_cache, self.v_cache, self.d_bt,
+                                  self.d_ctx, self.out[self.Tp:], self.workspace, self.d_max_c,
+                                  sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                                  sh.scale, stream)
+
+    def step(self, stream=None):
+        self.rope_write(stream)
+        self.prefill(stream)
+        self.decode(stream)
+
+    def results(self):
+        """Host copies: q_out, k_cache, v_cache, out (storage arrays)."""
+        torch.cuda.synchronize()
+        return {"q_out": to_host(self.q_out), "k_cache": to_host(self.k_cache),
+                "v_cache": to_host(self.v_cache), "out": to_host(self.out)}

@@ -1,0 +1,121 @@
+"""Shared helpers of the GPU parity tests: run a batch on the HIP path and on
+the CPU oracle, and compare element by element."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle.reference as R
+from paged_gqa_attention_neox_amd import binding as B
+from paged_gqa_attention_neox_amd import runner
+
+# tolerances the attention outputs must meet against the float64 oracle
+TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-5, 1e-6)}
+
+
+def say(msg: str) -> None:
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    import pytest
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+
+
+def run_gpu(batch, k_cache=None, v_cache=None, repeat=1):
+    dev = runner.DeviceStep(batch, k_cache=k_cache, v_cache=v_cache)
+    for _ in range(repeat):
+        dev.step()
+    return dev.results(), dev
+
+
+def run_oracle(batch, seqs=None):
+    """Oracle step.  ``seqs`` restricts the attention to those sequence ids
+    (the cache write always covers every token)."""
+    sh = batch.shape
+    q_out, kc, vc = R.rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
+                                       batch.k_cache, batch.v_cache, sh.num_heads, sh.num_kv_heads,
+                                       sh.head_dim, sh.block_size, sh.rope_theta)
+    cu = batch.cu_seqlens_q
+    out = np.full((batch.num_tokens, sh.num_heads, sh.head_dim), np.nan)
+    ids = range(batch.num_seqs) if seqs is None else seqs
+    for s in ids:
+        r0, r1 = int(cu[s]), int(cu[s + 1])
+        o = R.attention_varlen(q_out[r0:r1], kc, vc, np.array([0, r1 - r0]),
+                               batch.context_lens[s:s + 1], batch.block_tables[s:s + 1],
+                               sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, sh.dtype)
+        out[r0:r1] = o
+    return {"q_out": q_out, "k_cache": kc, "v_cache": vc, "out": out}
+
+
+def bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint16) if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+def ulp_bf16(x):
+    """Spacing of bf16 at |x| (normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    _, e = np.frexp(ax)
+    return np.ldexp(1.0, e - 8)
+
+
+def check_rotated(gpu, ora, dtype, what):
+    """Rotated q/k stored in the storage dtype: both sides round once, so they
+    agree to one unit in the last place (bf16) or to 1e-5 (fp32); the mean
+    error stays at rounding level."""
+    g = R.to_f64(gpu, dtype)
+    o = R.to_f64(ora, dtype)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    d = np.abs(g - o)
+    if dtype == "bf16":
+        lim = ulp_bf16(o) * 1.0001
+        bad = d > lim
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond 1 ulp (max {d.max()})"
+        assert d.mean() <= 2e-3, f"{what}: mean abs {d.mean()}"
+        frac = float(np.mean(d > 0))
+        assert frac < 5e-3, f"{what}: {frac:.2e} of elements differ by a rounding"
+    else:
+        assert d.max() <= 1e-5, f"{what}: max abs {d.max()}"
+
+
+def check_out(gpu, ora64, dtype, rows=None, what="out"):
+    g = R.to_f64(gpu, dtype)
+    o = ora64
+    if rows is not None:
+        g, o = g[rows], o[rows]
+    assert np.all(np.isfinite(o)), f"{what}: oracle rows not computed"
+    assert np.all(np.isfinite(g)), f"{what}: GPU output has {int((~np.isfinite(g)).sum())} non-finite values"
+    d = np.abs(g - o)
+    mx, mean = TOL[dtype]
+    assert d.max() <= mx, f"{what}: max abs {d.max():.3e} > {mx} (at {np.unravel_index(d.argmax(), d.shape)})"
+    assert d.mean() <= mean, f"{what}: mean abs {d.mean():.3e} > {mean}"
+    return float(d.max()), float(d.mean())
+
+
+def written_mask(batch):
+    """Boolean per (block, offset): slots this step writes."""
+    B_ = batch.shape.block_size
+    m = np.zeros((batch.num_blocks, B_), bool)
+    for sl in batch.slot_mapping:
+        if sl >= 0:
+            m[sl // B_, sl % B_] = True
+    return m
+
+
+def check_caches(batch, res, ora):
+    """V cache bitwise equal everywhere; K cache bitwise equal at every slot
+    the step does not write and within rounding at the written ones."""
+    dt = batch.shape.dtype
+    assert np.array_equal(bits(res["v_cache"]), bits(ora["v_cache"])), "V cache differs"
+    wm = written_mask(batch)
+    kc_g, kc_o = res["k_cache"], ora["k_cache"]
+    diff = np.nonzero(bits(kc_g) != bits(kc_o))
+    assert wm[diff[0], diff[2]].all(), "K cache changed at slots the step does not write"
+    blk, off = np.nonzero(wm)
+    check_rotated(kc_g[blk, :, off, :], kc_o[blk, :, off, :], dt, "K cache (written slots)")

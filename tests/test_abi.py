@@ -1,0 +1,224 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry
+point, and its host-side validation returns the documented status before any
+launch.  Every call here fails validation (or is host-only), so nothing is
+enqueued on a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from paged_gqa_attention_neox_amd import binding as B
+from paged_gqa_attention_neox_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qwen2_attn.h")
+
+QW_OK, QW_ERR_NULL, QW_ERR_SHAPE, QW_ERR_UNSUPPORTED, QW_ERR_ALIGN, QW_ERR_WORKSPACE, \
+    QW_ERR_METADATA, QW_ERR_HIP = range(8)
+
+# fake, 256-byte aligned "device" addresses: validation only looks at them
+P = 0x10000
+P2 = 0x20000
+P3 = 0x30000
+MIS = 0x10008   # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libqwen2attn.so not built")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwen2_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_path_calls():
+    names = declared_functions()
+    for n in ("qwen2_rope_cache_write", "qwen2_attn_prefill_varlen", "qwen2_attn_decode_paged"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in B.SIGNATURES, f"binding lacks {n}"
+
+
+def test_exported_dynamic_symbols_match_header(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (qwen2_\w+)", out))
+    assert exported == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert B.status_string(s) and B.status_string(s) != "unknown status"
+    assert B.status_string(99) == "unknown status"
+
+
+def _decode(lib, **kw):
+    a = dict(q=P, qs=28 * 128, kc=P2, vc=P3, nb=100, bt=P, mb=64, ctx=P, out=P2, os=28 * 128,
+             ws=P3, wsb=1 << 30, S=4, maxc=1024, H=28, Hkv=4, d=128, B=16, scale=0.0884, dt=1)
+    a.update(kw)
+    return lib.qwen2_attn_decode_paged(a["q"], a["qs"], a["kc"], a["vc"], a["nb"], a["bt"], a["mb"],
+                                       a["ctx"], a["out"], a["os"], a["ws"], a["wsb"], a["S"],
+                                       a["maxc"], a["H"], a["Hkv"], a["d"], a["B"], a["scale"],
+                                       a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), QW_ERR_NULL),
+    (dict(out=0), QW_ERR_NULL),
+    (dict(kc=0), QW_ERR_NULL),
+    (dict(ctx=0), QW_ERR_NULL),
+    (dict(bt=0), QW_ERR_NULL),
+    (dict(H=30), QW_ERR_SHAPE),                    # not a multiple of Hkv
+    (dict(d=96, qs=28 * 96, os=28 * 96), QW_ERR_UNSUPPORTED),
+    (dict(B=32), QW_ERR_UNSUPPORTED),
+    (dict(dt=5), QW_ERR_UNSUPPORTED),
+    (dict(H=68, Hkv=4, qs=68 * 128, os=68 * 128), QW_ERR_UNSUPPORTED),   # group 17
+    (dict(q=MIS), QW_ERR_ALIGN),
+    (dict(qs=28 * 128 + 4), QW_ERR_ALIGN),
+    (dict(qs=100), QW_ERR_SHAPE),
+    (dict(mb=8), QW_ERR_SHAPE),                    # 8 blocks cannot hold 1024 tokens
+    (dict(maxc=0), QW_ERR_SHAPE),
+    (dict(nb=0), QW_ERR_SHAPE),
+    (dict(scale=float("nan")), QW_ERR_SHAPE),
+    (dict(S=-1), QW_ERR_SHAPE),
+    (dict(ws=0), QW_ERR_WORKSPACE),
+    (dict(wsb=16), QW_ERR_WORKSPACE),
+    (dict(ws=MIS), QW_ERR_ALIGN),
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.qwen2_last_error().decode()
+
+
+def test_zero_work_is_ok_without_launch(lib):
+    assert _decode(lib, S=0, q=0, out=0) == QW_OK
+    assert lib.qwen2_rope_cache_write(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 0, 0, 0, 0, 28, 4, 128, 16, 1,
+                                      None) == QW_OK
+
+
+def test_workspace_size(lib):
+    n = B.qwen2_attn_decode_workspace_size(64, 32768, 28, 4, 128, 16, __import__("torch").bfloat16)
+    assert n >= 64 * 28 * (32768 // 512) * 128 * 4
+    # a single partition needs no workspace
+    assert B.qwen2_attn_decode_workspace_size(8, 512, 28, 4, 128, 16, __import__("torch").bfloat16) == 0
+    assert lib.qwen2_attn_decode_workspace_size(8, 100, 28, 4, 96, 16, 1) == ctypes.c_size_t(-1).value
+
+
+def _rope(lib, **kw):
+    W_ = (28 + 8) * 128
+    a = dict(q=P, qs=W_, qo=P2, qos=28 * 128, k=P + 28 * 256, ks=W_, v=P + 32 * 256, vs=W_, pos=P,
+             slot=P, cs=P3, maxp=32768, kc=P, vc=P2, nb=10, T=5, H=28, Hkv=4, d=128, B=16, dt=1)
+    a.update(kw)
+    return lib.qwen2_rope_cache_write(a["q"], a["qs"], a["qo"], a["qos"], a["k"], a["ks"], a["v"],
+                                      a["vs"], a["pos"], a["slot"], a["cs"], a["maxp"], a["kc"], a["vc"],
+                                      a["nb"], a["T"], a["H"], a["Hkv"], a["d"], a["B"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), QW_ERR_NULL), (dict(pos=0), QW_ERR_NULL), (dict(slot=0), QW_ERR_NULL),
+    (dict(cs=0), QW_ERR_NULL), (dict(kc=0), QW_ERR_NULL),
+    (dict(T=-1), QW_ERR_SHAPE), (dict(maxp=0), QW_ERR_SHAPE),
+    (dict(qs=128), QW_ERR_SHAPE), (dict(Hkv=3), QW_ERR_SHAPE),
+    (dict(k=MIS), QW_ERR_ALIGN), (dict(cs=MIS), QW_ERR_ALIGN),
+    (dict(qo=P + 64), QW_ERR_SHAPE),            # overlaps q without being q
+    (dict(d=80), QW_ERR_UNSUPPORTED),
+])
+def test_rope_validation(lib, kw, status):
+    assert _rope(lib, **kw) == status
+
+
+def _prefill(lib, **kw):
+    a = dict(q=P, qs=28 * 128, kc=P2, vc=P3, nb=100, cu=P, ctx=P, bt=P, mb=64, out=P2, os=28 * 128,
+             S=4, T=100, maxq=50, maxc=1024, H=28, Hkv=4, d=128, B=16, scale=0.0884, dt=1)
+    a.update(kw)
+    return lib.qwen2_attn_prefill_varlen(a["q"], a["qs"], a["kc"], a["vc"], a["nb"], a["cu"], a["ctx"],
+                                         a["bt"], a["mb"], a["out"], a["os"], a["S"], a["T"], a["maxq"],
+                                         a["maxc"], a["H"], a["Hkv"], a["d"], a["B"], a["scale"],
+                                         a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=0), QW_ERR_NULL), (dict(q=0), QW_ERR_NULL), (dict(vc=0), QW_ERR_NULL),
+    (dict(maxq=2000), QW_ERR_SHAPE), (dict(S=70000), QW_ERR_UNSUPPORTED),
+    (dict(out=MIS), QW_ERR_ALIGN), (dict(H=0), QW_ERR_SHAPE), (dict(scale=-1.0), QW_ERR_SHAPE),
+])
+def test_prefill_validation(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+
+
+def test_rope_table_validation(lib):
+    assert lib.qwen2_rope_table_init(0, 10, 128, 1e6, None) == QW_ERR_NULL
+    assert lib.qwen2_rope_table_init(P, 0, 128, 1e6, None) == QW_ERR_SHAPE
+    assert lib.qwen2_rope_table_init(P, 10, 127, 1e6, None) == QW_ERR_SHAPE
+    assert lib.qwen2_rope_table_init(P, 10, 128, 0.0, None) == QW_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# host metadata checker
+# ---------------------------------------------------------------------------
+def _meta(b, **over):
+    a = dict(positions=b.positions, slot_mapping=b.slot_mapping, cu_seqlens_q=b.cu_seqlens_q,
+             context_lens=b.context_lens, block_tables=b.block_tables, num_blocks=b.num_blocks,
+             block_size=16, max_position=32768, max_context_len=int(b.context_lens.max()),
+             max_query_len=int(b.query_lens.max()))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("maker", [W.mixed_tp2, W.qwen2_prefill, W.qwen3_decode])
+def test_metadata_of_workloads_is_valid(lib, maker):
+    b = maker()
+    B.qwen2_check_metadata_host(**_meta(b))
+
+
+def test_metadata_violations(lib):
+    b = W.small_case(3, "bf16", 4, 2, 16, context_lens=[40, 17, 5], query_lens=[8, 1, 5],
+                     num_prefill=1)
+    B.qwen2_check_metadata_host(**_meta(b))
+
+    def bad(**over):
+        with pytest.raises(B.QwenAttnError) as ei:
+            B.qwen2_check_metadata_host(**_meta(b, **over))
+        assert ei.value.status == QW_ERR_METADATA
+
+    pos = b.positions.copy(); pos[2] += 1
+    bad(positions=pos)
+    pos = b.positions.copy(); pos[0] = 40000
+    bad(positions=pos)
+    sl = b.slot_mapping.copy(); sl[1] = sl[0]
+    bad(slot_mapping=sl)                                   # duplicate slot
+    sl = b.slot_mapping.copy(); sl[3] = b.num_blocks * 16
+    bad(slot_mapping=sl)
+    sl = b.slot_mapping.copy(); sl[4] = (sl[4] + 1) % (b.num_blocks * 16)
+    bad(slot_mapping=sl)                                   # disagrees with the block table
+    ctx = b.context_lens.copy(); ctx[2] = 4
+    bad(context_lens=ctx)                                  # context < rows
+    bt = b.block_tables.copy(); bt[0, 1] = -3
+    bad(block_tables=bt)
+    cu = b.cu_seqlens_q.copy(); cu[0] = 1
+    bad(cu_seqlens_q=cu)
+    bad(max_context_len=30)
+    bad(max_query_len=4)
+    # slot -1 (skip) is allowed
+    sl = b.slot_mapping.copy(); sl[0] = -1
+    B.qwen2_check_metadata_host(**_meta(b, slot_mapping=sl))
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
