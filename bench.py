@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-decode", action="store_true", help="time the decode workload only")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times), the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no "
@@ -172,6 +175,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.lib()
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "launches": 3}), flush=True)
+        return
 
     dec = bench_decode(args.steps, args.warmup)
     log(f"decode: step {dec['step_ms']:.3f} ms (rope {dec['rope_ms']:.3f}, decode {dec['decode_ms']:.3f})")
