@@ -86,15 +86,15 @@ typedef enum { QW_F32 = 0, QW_BF16 = 1 } qw_dtype;
  * Fill the rotary table: for p < max_position, i < rotary_dim/2,
  *   cos_sin[p][i]                = cos(p * f_i)
  *   cos_sin[p][rotary_dim/2 + i] = sin(p * f_i),  f_i = rope_theta^(-2i/rotary_dim)
- * computed in float64 on the device and stored as float32 (so the angle is
- * never formed in float32, which at p ~ 32767 would be off by ~1e-3 rad).
+ * computed and stored in float64 on the device (the angle is never formed
+ * in float32, which at p ~ 32767 would be off by ~1e-3 rad).
  * "Qwen2大模型架构解析与vLLM优化实践", §2.2 (get_rope(..., max_position, base));
  * "Qwen2 模型结构代码详解", §3 (max_model_len becomes max_position).
- * cos_sin: device, float32 [max_position][rotary_dim], written.
+ * cos_sin: device, float64 [max_position][rotary_dim], written.
  * Requires max_position >= 1, rotary_dim even in [2, 256], rope_theta > 0.
  * Call once per (theta, rotary_dim, max_position); the table is read-only after.
  */
-int qwen2_rope_table_init(float* cos_sin, int max_position, int rotary_dim,
+int qwen2_rope_table_init(double* cos_sin, int max_position, int rotary_dim,
                           double rope_theta, hipStream_t stream);
 
 /*
@@ -107,14 +107,15 @@ int qwen2_rope_table_init(float* cos_sin, int max_position, int rotary_dim,
  * For token t at position p = positions[t], every q and k head is rotated
  * (NeoX pairs (i, i + d/2), angle from cos_sin row p):
  *   y_i = x_i cos - x_{i+d/2} sin,   y_{i+d/2} = x_{i+d/2} cos + x_i sin
- * in float32 and rounded once to the storage dtype.  Rotated q goes to
+ * in float64 (table included) and rounded once, to nearest even, to the
+ * storage dtype: stored q/k are the correctly rounded rotation.  Rotated q goes to
  * q_out [T][num_heads][head_dim] (q_out_row_stride; q_out may equal q for
  * an in-place update, any other overlap is undefined).  If slot_mapping[t]
  * >= 0, rotated k goes to k_cache[slot/B][g][slot%B][:] and v is copied bit
  * for bit to v_cache[slot/B][g][:][slot%B]; slot -1 writes nothing.  Slots
  * not named are left untouched.
  * cos_sin: table from qwen2_rope_table_init with rotary_dim == head_dim and
- * max_position rows (max_position * head_dim floats are readable).  positions, slot_mapping: device int32 [T].
+ * max_position rows (max_position * head_dim doubles are readable).  positions, slot_mapping: device int32 [T].
  * "vLLM 部署 Qwen", §2.1 (paged KV cache); "Qwen2大模型架构解析与vLLM优化实践",
  * §7.3 (RoPE as one fused kernel).
  */
@@ -123,7 +124,7 @@ int qwen2_rope_cache_write(const void* q, int64_t q_row_stride,
                            const void* k, int64_t k_row_stride,
                            const void* v, int64_t v_row_stride,
                            const int32_t* positions, const int32_t* slot_mapping,
-                           const float* cos_sin, int max_position,
+                           const double* cos_sin, int max_position,
                            void* k_cache, void* v_cache, int num_blocks,
                            int num_tokens, int num_heads, int num_kv_heads,
                            int head_dim, int block_size, int dtype, hipStream_t stream);

@@ -113,9 +113,9 @@ def _i32(t: Optional[torch.Tensor]) -> int:
 
 # ---------------------------------------------------------------------------
 def qwen2_rope_table_init(cos_sin: torch.Tensor, rope_theta: float, stream=None) -> None:
-    """cos_sin: float32 [max_position][rotary_dim] on the device, filled."""
-    if cos_sin.dtype != torch.float32 or not cos_sin.is_contiguous() or cos_sin.dim() != 2:
-        raise TypeError("cos_sin must be a contiguous float32 [max_position][rotary_dim] tensor")
+    """cos_sin: float64 [max_position][rotary_dim] on the device, filled."""
+    if cos_sin.dtype != torch.float64 or not cos_sin.is_contiguous() or cos_sin.dim() != 2:
+        raise TypeError("cos_sin must be a contiguous float64 [max_position][rotary_dim] tensor")
     _check("qwen2_rope_table_init",
            lib().qwen2_rope_table_init(cos_sin.data_ptr(), cos_sin.shape[0], cos_sin.shape[1],
                                        float(rope_theta), _stream(stream)))
@@ -126,11 +126,11 @@ def qwen2_rope_cache_write(q, q_out, k, v, positions, slot_mapping, cos_sin, k_c
                            stream=None) -> None:
     """q [T][H*d] (or [T][H][d]) view, q_out same shape (may be q), k and v
     [T][Hkv*d] views (e.g. column slices of the fused QKV tensor);
-    positions, slot_mapping int32 [T]; cos_sin float32 [max_position][d];
+    positions, slot_mapping int32 [T]; cos_sin float64 [max_position][d];
     caches laid out as in include/qwen2_attn.h."""
     T = q.shape[0]
-    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim or cos_sin.dtype != torch.float32:
-        raise ValueError("cos_sin must be float32 [max_position][head_dim]")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim or cos_sin.dtype != torch.float64:
+        raise ValueError("cos_sin must be float64 [max_position][head_dim]")
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         if t.dim() != 4 or t.shape[1] != num_kv_heads or t.dtype != q.dtype:
             raise ValueError(f"{name} must be [num_blocks][num_kv_heads][..] of the q dtype")

@@ -17,7 +17,7 @@ struct RopeWriteArgs {
   const void* v; int64_t v_stride;
   const int32_t* positions;
   const int32_t* slots;
-  const float* cos_sin; int max_position;
+  const double* cos_sin; int max_position;
   void* k_cache; void* v_cache; int num_blocks;
   int num_tokens, num_heads, num_kv_heads, head_dim, block_size;
   int dtype;
@@ -48,7 +48,7 @@ struct DecodePlan {
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
                        int head_dim, int block_size, int dtype);
 
-hipError_t launch_rope_table(float* tab, int max_position, int rotary_dim, double theta,
+hipError_t launch_rope_table(double* tab, int max_position, int rotary_dim, double theta,
                              hipStream_t stream);
 hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& plan, hipStream_t stream);

@@ -85,7 +85,7 @@ const char* qwen2_status_string(int status) {
 
 const char* qwen2_last_error(void) { return g_err; }
 
-int qwen2_rope_table_init(float* cos_sin, int max_position, int rotary_dim, double rope_theta,
+int qwen2_rope_table_init(double* cos_sin, int max_position, int rotary_dim, double rope_theta,
                           hipStream_t stream) {
   if (!cos_sin) return fail(QW_ERR_NULL, "cos_sin is NULL");
   if (max_position < 1) return fail(QW_ERR_SHAPE, "max_position=%d < 1", max_position);
@@ -98,7 +98,7 @@ int qwen2_rope_table_init(float* cos_sin, int max_position, int rotary_dim, doub
 int qwen2_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int64_t q_out_row_stride,
                            const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
                            const int32_t* positions, const int32_t* slot_mapping,
-                           const float* cos_sin, int max_position, void* k_cache, void* v_cache,
+                           const double* cos_sin, int max_position, void* k_cache, void* v_cache,
                            int num_blocks, int num_tokens, int num_heads, int num_kv_heads,
                            int head_dim, int block_size, int dtype, hipStream_t stream) {
   int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);

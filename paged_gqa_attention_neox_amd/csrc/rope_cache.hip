@@ -1,5 +1,8 @@
 // Rotary table and the fused "rotate q/k + write k/v into the paged cache"
-// kernel.
+// kernel.  The rotation runs in float64 (the table too) and rounds once to
+// the storage type, so the stored q/k equal the correctly rounded exact
+// rotation; gfx950's float64 vector rate equals its float32 rate and the
+// kernel is bound by HBM, not arithmetic.
 //
 // Rotary embedding over the whole head with base rope_theta
 // ("Qwen2大模型架构解析与vLLM优化实践", §2.2 get_rope; "Qwen2 模型结构代码详解",
@@ -18,9 +21,9 @@
 namespace qw {
 
 // ---------------------------------------------------------------------------
-// cos/sin table, float64 math stored as float32
+// cos/sin table in float64
 // ---------------------------------------------------------------------------
-__global__ void rope_table_kernel(float* __restrict__ tab, int max_position, int rot,
+__global__ void rope_table_kernel(double* __restrict__ tab, int max_position, int rot,
                                   double theta) {
   const int half = rot / 2;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -32,11 +35,11 @@ __global__ void rope_table_kernel(float* __restrict__ tab, int max_position, int
   const double a = static_cast<double>(p) * f;
   double s, c;
   sincos(a, &s, &c);
-  tab[static_cast<int64_t>(p) * rot + i] = static_cast<float>(c);
-  tab[static_cast<int64_t>(p) * rot + half + i] = static_cast<float>(s);
+  tab[static_cast<int64_t>(p) * rot + i] = c;
+  tab[static_cast<int64_t>(p) * rot + half + i] = s;
 }
 
-hipError_t launch_rope_table(float* tab, int max_position, int rotary_dim, double theta,
+hipError_t launch_rope_table(double* tab, int max_position, int rotary_dim, double theta,
                              hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(max_position) * (rotary_dim / 2);
   const int threads = 256;
@@ -44,6 +47,17 @@ hipError_t launch_rope_table(float* tab, int max_position, int rotary_dim, doubl
   hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
                      stream, tab, max_position, rotary_dim, theta);
   return hipGetLastError();
+}
+
+// float64 -> storage with ONE rounding (round to nearest even).
+// bf16: round to odd into fp32 first (truncate, then set the last bit when
+// inexact), then fp32 -> bf16 to nearest even: with 16 extra bits kept, the
+// result is the correctly rounded bf16 of the float64 value.
+__device__ __forceinline__ uint16_t f64_to_bf16(double y) {
+  float t = __double2float_rz(y);
+  uint32_t u = __float_as_uint(t);
+  if (static_cast<double>(t) != y) u |= 1u;
+  return f32_to_bf16(__uint_as_float(u));
 }
 
 // ---------------------------------------------------------------------------
@@ -66,6 +80,21 @@ template <> struct Vec8<uint16_t> {   // bf16
   __device__ __forceinline__ uint16_t elem(int j) const {
     const uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
     return static_cast<uint16_t>((j & 1) ? (x >> 16) : (x & 0xffffu));
+  }
+  __device__ __forceinline__ void to_f64(double (&f)[8]) const {
+    float t[8];
+    to_f32(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = t[j];
+  }
+  __device__ __forceinline__ void from_f64(const double (&f)[8]) {
+    uint16_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = f64_to_bf16(f[j]);
+    w.x = b[0] | (static_cast<uint32_t>(b[1]) << 16);
+    w.y = b[2] | (static_cast<uint32_t>(b[3]) << 16);
+    w.z = b[4] | (static_cast<uint32_t>(b[5]) << 16);
+    w.w = b[6] | (static_cast<uint32_t>(b[7]) << 16);
   }
   static __device__ __forceinline__ uint16_t nan() { return 0x7fc0; }
 };
@@ -90,6 +119,18 @@ template <> struct Vec8<float> {
   __device__ __forceinline__ float elem(int j) const {
     return j == 0 ? a.x : j == 1 ? a.y : j == 2 ? a.z : j == 3 ? a.w
          : j == 4 ? b.x : j == 5 ? b.y : j == 6 ? b.z : b.w;
+  }
+  __device__ __forceinline__ void to_f64(double (&f)[8]) const {
+    float t[8];
+    to_f32(t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = t[j];
+  }
+  __device__ __forceinline__ void from_f64(const double (&f)[8]) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = static_cast<float>(f[j]);   // one rounding, nearest even
+    from_f32(t);
   }
   static __device__ __forceinline__ float nan() { return __builtin_nanf(""); }
 };
@@ -153,24 +194,27 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       Vec8<T> x1v, x2v;
       x1v.load(src + i0);
       x2v.load(src + HALF + i0);
-      float x1[8], x2[8], y1[8], y2[8];
-      x1v.to_f32(x1);
-      x2v.to_f32(x2);
-      const float* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
-      const float4 c0 = *reinterpret_cast<const float4*>(cs + i0);
-      const float4 c1 = *reinterpret_cast<const float4*>(cs + i0 + 4);
-      const float4 s0 = *reinterpret_cast<const float4*>(cs + HALF + i0);
-      const float4 s1 = *reinterpret_cast<const float4*>(cs + HALF + i0 + 4);
-      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      double x1[8], x2[8], y1[8], y2[8];
+      x1v.to_f64(x1);
+      x2v.to_f64(x2);
+      const double* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
+      double cv[8], sv[8];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const double2 c2 = *reinterpret_cast<const double2*>(cs + i0 + j);
+        const double2 s2 = *reinterpret_cast<const double2*>(cs + HALF + i0 + j);
+        cv[j] = c2.x; cv[j + 1] = c2.y;
+        sv[j] = s2.x; sv[j + 1] = s2.y;
+      }
+      // float64 rotation: the inputs are exact, each output is rounded once
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        y1[j] = fmaf(x1[j], cv[j], -(x2[j] * sv[j]));
-        y2[j] = fmaf(x2[j], cv[j], x1[j] * sv[j]);
+        y1[j] = fma(x1[j], cv[j], -(x2[j] * sv[j]));
+        y2[j] = fma(x2[j], cv[j], x1[j] * sv[j]);
       }
       Vec8<T> o1, o2;
-      o1.from_f32(y1);
-      o2.from_f32(y2);
+      o1.from_f64(y1);
+      o2.from_f64(y2);
       o1.store(dst + i0);
       o2.store(dst + HALF + i0);
     } else {

@@ -35,7 +35,7 @@ def rope_table(head_dim: int, theta: float, max_position: int, device="cuda") ->
     key = (head_dim, float(theta), int(max_position), str(device))
     t = _TABLES.get(key)
     if t is None:
-        t = torch.empty(max_position, head_dim, dtype=torch.float32, device=device)
+        t = torch.empty(max_position, head_dim, dtype=torch.float64, device=device)
         B.qwen2_rope_table_init(t, theta)
         _TABLES[key] = t
     return t

@@ -65,32 +65,23 @@ def ulp_bf16(x):
     return np.ldexp(1.0, e - 8)
 
 
-# Absolute error of the fp32 rotation x1*c - x2*s for |x| <= 16: when the
-# two products cancel, the fp32 result carries ~2^-23 * (|x1| + |x2|) of
-# absolute error, which is many bf16 ulps of a result near zero.
-FP32_ROT_ABS = 2.0 ** -18
-
-
 def check_rotated(gpu, ora, dtype, what):
-    """Rotated q/k stored in the storage dtype.  Both sides round once (the
-    oracle from float64, the GPU from float32), so elementwise they agree to
-    one bf16 ulp of the oracle value plus the fp32 cancellation error; over
-    the tensor the stated bf16 bound holds (max abs 2e-2, mean abs 2e-3).
-    fp32 storage: max abs 1e-5."""
+    """Rotated q/k in the storage dtype.  The GPU rotates in float64 and rounds
+    once, like the oracle, so the stored values are expected bit for bit.
+    The two float64 results can differ in the last place (device vs host
+    libm), which can move a value across a rounding boundary with a
+    probability of order 1e-13 per element: at most one element in a million
+    may differ, and then by one unit in the last place only."""
     g = R.to_f64(gpu, dtype)
     o = R.to_f64(ora, dtype)
     assert np.all(np.isfinite(g)), f"{what}: non-finite values"
-    d = np.abs(g - o)
-    if dtype == "bf16":
-        lim = ulp_bf16(o) * 1.0001 + FP32_ROT_ABS
-        bad = d > lim
-        assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond 1 ulp + fp32 error (max {d.max()})"
-        assert d.max() <= 2e-2, f"{what}: max abs {d.max()}"
-        assert d.mean() <= 2e-3, f"{what}: mean abs {d.mean()}"
-        frac = float(np.mean(d > 0))
-        assert frac < 5e-3, f"{what}: {frac:.2e} of elements differ by a rounding"
-    else:
-        assert d.max() <= 1e-5, f"{what}: max abs {d.max()}"
+    neq = bits(gpu) != bits(ora)
+    n_bad = int(neq.sum())
+    assert n_bad <= max(0, neq.size // 1_000_000), f"{what}: {n_bad} of {neq.size} elements differ"
+    if n_bad:
+        d = np.abs(g - o)[neq]
+        lim = (ulp_bf16(o[neq]) if dtype == "bf16" else np.abs(o[neq]) * 2.0 ** -23) * 1.0001
+        assert np.all(d <= lim), f"{what}: a differing element is off by more than one ulp"
 
 
 def check_out(gpu, ora64, dtype, rows=None, what="out"):

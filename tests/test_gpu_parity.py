@@ -112,6 +112,12 @@ SMALL = [
     ("prefill_chunks", "bf16", 14, 2, 128, [100, 700, 48], [37, 300, 48], 3),
     ("prefill_f32_d64", "f32", 4, 2, 64, [33, 20], [33, 7], 2),
     ("mixed_small", "bf16", 28, 4, 128, [90, 300, 2000, 1, 513], [90, 44, 1, 1, 1], 2),
+    ("prefill_g1", "bf16", 4, 4, 128, [33, 95, 1], [33, 95, 1], 3),
+    ("prefill_g2_chunk", "bf16", 16, 8, 128, [160, 77], [31, 77], 2),
+    ("prefill_g4", "bf16", 16, 4, 128, [64, 129], [64, 129], 2),
+    ("prefill_g8_chunk", "bf16", 32, 4, 128, [1000, 40], [65, 40], 2),
+    ("prefill_long_chunk", "bf16", 28, 4, 128, [2100], [100], 1),
+    ("prefill_d64_generic", "bf16", 8, 2, 64, [50, 20], [50, 5], 2),
 ]
 
 
