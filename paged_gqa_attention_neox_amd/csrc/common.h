@@ -30,9 +30,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // ---- DPP lane exchange (within rows of 16 lanes) ---------------------------
 // dpp_ctrl encodings (GFX9 family): quad_perm [a,b,c,d] = a|b<<2|c<<4|d<<6,
 // row_ror:n = 0x120+n, row_mirror = 0x140, row_half_mirror = 0x141.
+// Every control used here reads a valid lane, so bound_ctrl does not change
+// the result; with it set the compiler fuses "mov_dpp + add" into one
+// v_add_f32_dpp.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
@@ -61,6 +64,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+// First product of a chain: the three-operand form with an inline zero
+// accumulator (the two-operand accumulate-in-place form would need a zeroing
+// move first).
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -9,15 +9,19 @@
 //
 // Work decomposition: one 256-thread workgroup (4 waves) per
 // (partition of kPart tokens, KV head, sequence).  The waves take the
-// partition's 16-token blocks round-robin.
+// partition's 16-token blocks round-robin and stream them through kNBuf
+// register buffers, so the next blocks' loads are always in flight.
 //   Phase 1 (scores): K tile [16][128] bf16 = 4 KiB contiguous.  8 lanes per
-//     key, 16 dims (32 B, two 128-bit loads) per lane; q.k with v_dot2 bf16
-//     products accumulated in fp32, summed over the 8 lanes with DPP.  Scores
-//     (pre-multiplied by scale * log2 e) go to LDS.
-//   Phase 2 (softmax): per head max over the partition, p = 2^(z - max),
-//     sum; p replaces the score in LDS.
-//   Phase 3 (PV): V tile [128][16] bf16 (dims major).  Lane = 4 dims x 8
-//     keys (four 128-bit loads); fp32 FMA with p broadcast from LDS.
+//     key, 16 dims (two 128-bit loads) per lane; q.k with v_dot2 bf16
+//     products accumulated in fp32, summed over the 8 lanes with DPP.  Raw
+//     scores go to LDS (the scale is applied in the softmax).
+//   Phase 2 (softmax): per head max over the partition; p = 2^((z - max)
+//     * scale * log2 e) rounded to bf16 and stored as pairs of consecutive tokens; the sum of
+//     the rounded p.  The first V tile is already loading.
+//   Phase 3 (PV): V tile [128][16] bf16 (dims major), so a 32-bit word holds
+//     two consecutive tokens of one dim: acc += v_dot2(p pair, v pair), fp32
+//     accumulation.  Lane = 4 dims x 8 tokens (four 128-bit loads).  Every
+//     128-bit load instruction of a wave reads 1 KiB of a tile contiguously.
 //   Epilogue: combine key halves and waves; a single-partition sequence
 //     writes its normalised output; otherwise the partial (max, sum, acc[d])
 //     goes to the workspace and decode_reduce merges the partitions:
@@ -29,12 +33,31 @@
 
 namespace qw {
 
-constexpr int kPart = 512;              // tokens per partition
+#ifndef QW_DECODE_PART
+#define QW_DECODE_PART 512
+#endif
+#ifndef QW_DECODE_NW
+#define QW_DECODE_NW 4
+#endif
+constexpr int kPart = QW_DECODE_PART;   // tokens per partition
+constexpr int kNW = QW_DECODE_NW;       // waves per workgroup
+constexpr int kThreads = kNW * 64;
 constexpr int kBlk = 16;                // tokens per cache block
 constexpr int kD = 128;                 // head_dim
 constexpr int kPartBlocks = kPart / kBlk;
 constexpr int kMaxG = 8;
+#ifndef QW_DECODE_NBUF
+#define QW_DECODE_NBUF 2
+#endif
+constexpr int kNBuf = QW_DECODE_NBUF;   // blocks of K (or V) in flight per wave
 constexpr float kLog2e = 1.4426950408889634f;
+
+// gfx9-family buffer descriptor word 3 (raw 32-bit accesses, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ uint4 ld_buf16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
 
 struct DecodeKArgs {
   const uint16_t* q; int64_t q_stride;
@@ -56,8 +79,13 @@ __device__ __forceinline__ int checked_ctx(const DecodeKArgs& a, int s, bool* ba
   return c < 1 ? 1 : (c > a.max_context_len ? a.max_context_len : c);
 }
 
+#ifndef QW_DECODE_WAVES
+#define QW_DECODE_WAVES 4
+#endif
+
 template <int G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeKArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QW_DECODE_WAVES)))
+void decode_partial_kernel(DecodeKArgs a) {
   const int r = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   bool ctx_bad;
   const int ctx = checked_ctx(a, s, &ctx_bad);
@@ -71,48 +99,89 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeKArgs a) {
   const int wave = uniform(tid >> 6);
   const int Hkv = a.num_kv_heads;
 
-  __shared__ __attribute__((aligned(16))) float sc[kPart * 8];   // [token][8]
-  __shared__ __attribute__((aligned(16))) float sacc[4][kMaxG * kD];
+  // scores [token][8 heads] (fp32); after the softmax the same space holds
+  // the per-wave partial outputs of the merge
+  __shared__ __attribute__((aligned(16))) float sc[kPart * 8];
+  // probabilities as bf16 pairs of consecutive tokens: [token pair][8 heads]
+  __shared__ __attribute__((aligned(16))) uint32_t sp2[kPart / 2 * 8];
   __shared__ int sblk[kPartBlocks];
-  __shared__ float sred[4][8];
+  __shared__ float sred[kNW][8];
   __shared__ float sM[8], sL[8];
   __shared__ int sbad;
+  float (*sacc)[kMaxG * kD] = reinterpret_cast<float (*)[kMaxG * kD]>(sc);
+  static_assert(kNW * kMaxG * kD <= kPart * 8, "merge buffer must fit in the score buffer");
 
   if (tid == 0) sbad = ctx_bad ? 1 : 0;
   __syncthreads();
-  if (tid < nblk) {
-    int b = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + (p0 / kBlk) + tid];
+  for (int i = tid; i < nblk; i += kThreads) {
+    int b = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + (p0 / kBlk) + i];
     if (static_cast<unsigned>(b) >= static_cast<unsigned>(a.num_blocks)) {
       sbad = 1;
       b = 0;
     }
-    sblk[tid] = b;
+    sblk[i] = b;
   }
   __syncthreads();
 
-  // ---------------- phase 1: scores ----------------
+  // Blocks of this wave: b = wave + kNW i, i < nbw.
+  const int nbw = nblk > wave ? (nblk - wave + kNW - 1) / kNW : 0;
+  // Lane roles.  Each 128-bit load instruction of a wave reads 1 KiB of one
+  // tile contiguously.
+  //   phase 1: key kr of an 8-key round; dims 8u..8u+7 and 64+8u..64+8u+7
+  //   phase 3: dims d0 + 32 i (i < 4); keys 8 kh .. 8 kh + 7 of the block
+  const int kr = lane >> 3;
+  const int u = lane & 7;
+  const int d0 = lane >> 1;
+  const int kh = lane & 1;
+  // Tiles are read with buffer loads through a per-tile descriptor (uniform,
+  // in SGPRs).  Every pipeline load is issued unconditionally so the number
+  // of loads in flight is static and each wait covers exactly one block; a
+  // prefetch past the wave's last block gets a zero-size descriptor, which
+  // returns zeros without touching memory.
+  auto rsrc = [&](const uint16_t* base, int i) {
+    const bool live = i < nbw;
+    const int b = uniform(sblk[wave + kNW * (live ? i : 0)]);
+    const uint16_t* t = base + (static_cast<int64_t>(b) * Hkv + g) * (kBlk * kD);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t), static_cast<short>(0),
+                                             live ? kBlk * kD * 2 : 0, kBufferFlags);
+  };
+  const int koff = (kr * kD + u * 8) * 2;           // byte offsets within a tile
+  const int voff = lane * 16;
+  auto load_k = [&](int i, uint4 (&buf)[4]) {
+    const auto r = rsrc(a.k_cache, i);
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      buf[2 * rd] = ld_buf16(r, koff + rd * 8 * kD * 2);
+      buf[2 * rd + 1] = ld_buf16(r, koff + rd * 8 * kD * 2 + 128);
+    }
+  };
+  auto load_v = [&](int i, uint4 (&buf)[4]) {
+    const auto r = rsrc(a.v_cache, i);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) buf[d] = ld_buf16(r, voff + d * 1024);
+  };
+
+  // ---------------- phase 1: raw scores q.k ----------------
+  uint4 vbuf[kNBuf][4];
   {
-    const int kr = lane >> 3;   // key within an 8-key round
-    const int u = lane & 7;     // 16-dim slice
     uint4 qa[G], qb[G];
     const uint16_t* qp = a.q + static_cast<int64_t>(s) * a.q_stride +
-                         static_cast<int64_t>(g * G) * kD + u * 16;
+                         static_cast<int64_t>(g * G) * kD + u * 8;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       qa[h] = *reinterpret_cast<const uint4*>(qp + h * kD);
-      qb[h] = *reinterpret_cast<const uint4*>(qp + h * kD + 8);
+      qb[h] = *reinterpret_cast<const uint4*>(qp + h * kD + 64);
     }
-    for (int b = wave; b < nblk; b += 4) {
-      const uint16_t* kb = a.k_cache + (static_cast<int64_t>(sblk[b]) * Hkv + g) * (kBlk * kD);
+    auto scores = [&](int i, const uint4 (&kbuf)[4]) {
+      const int b = wave + kNW * i;
+      const bool full = (b + 1) * kBlk <= ntok;
 #pragma unroll
       for (int rd = 0; rd < 2; ++rd) {
-        const int j = rd * 8 + kr;
-        const uint4 k0 = *reinterpret_cast<const uint4*>(kb + j * kD + u * 16);
-        const uint4 k1 = *reinterpret_cast<const uint4*>(kb + j * kD + u * 16 + 8);
+        const uint4 k0 = kbuf[2 * rd], k1 = kbuf[2 * rd + 1];
         float acc[8];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float x = dot2_bf16(qa[h].x, k0.x, 0.0f);
+          float x = dot2_bf16_first(qa[h].x, k0.x);
           x = dot2_bf16(qa[h].y, k0.y, x);
           x = dot2_bf16(qa[h].z, k0.z, x);
           x = dot2_bf16(qa[h].w, k0.w, x);
@@ -122,42 +191,68 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeKArgs a) {
           x = dot2_bf16(qb[h].w, k1.w, x);
           acc[h] = sum8(x);
         }
-        const int t = b * kBlk + j;
-        if (u == 0) {
-          const bool valid = t < ntok;
-          float o[8];
 #pragma unroll
-          for (int h = 0; h < 8; ++h)
-            o[h] = (h < G && valid) ? acc[h < G ? h : 0] * a.scale_log2 : -INFINITY;
-          *reinterpret_cast<float4*>(&sc[t * 8]) = make_float4(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<float4*>(&sc[t * 8 + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+        for (int h = G; h < 8; ++h) acc[h] = -INFINITY;
+        const int t = b * kBlk + rd * 8 + kr;
+        if (!full) {                      // the partition's last block: keys past the context
+          if (t >= ntok) {                // (slots there may hold NaN) are excluded by select
+#pragma unroll
+            for (int h = 0; h < 8; ++h) acc[h] = -INFINITY;
+          }
+        }
+        if (u == 0) {
+          *reinterpret_cast<float4*>(&sc[t * 8]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          *reinterpret_cast<float4*>(&sc[t * 8 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
       }
+    };
+    uint4 kbuf[kNBuf][4];
+#pragma unroll
+    for (int j = 0; j < kNBuf - 1; ++j) load_k(j, kbuf[j]);
+    for (int i = 0; i < nbw; i += kNBuf) {
+#pragma unroll
+      for (int j = 0; j < kNBuf; ++j) {
+        load_k(i + j + kNBuf - 1, kbuf[(j + kNBuf - 1) % kNBuf]);
+        if (i + j < nbw) scores(i + j, kbuf[j]);
+      }
     }
+    // the first V tiles of this wave: in flight across the softmax phase
+#pragma unroll
+    for (int j = 0; j < kNBuf - 1; ++j) load_v(j, vbuf[j]);
   }
   __syncthreads();
 
-  // ---------------- phase 2: max, exp, sum over the partition ----------------
+  // ---------------- phase 2: max, p (bf16 pairs), sum ----------------
   {
     const int h = tid & 7;
-    const int ch = tid >> 3;           // 32 token chunks
+    const int ch = tid >> 3;           // kNW * 8 chunks
+    constexpr int kCh = kNW * 8;
     const int tend = nblk * kBlk;
     float m = -INFINITY;
-    for (int t = ch; t < tend; t += 32) m = fmaxf(m, sc[t * 8 + h]);
+    for (int t = ch; t < tend; t += kCh) m = fmaxf(m, sc[t * 8 + h]);
     m = fmaxf(m, __shfl_xor(m, 8));
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     if (lane < 8) sred[wave][h] = m;
     __syncthreads();
-    if (tid < 8) sM[tid] = fmaxf(fmaxf(sred[0][tid], sred[1][tid]), fmaxf(sred[2][tid], sred[3][tid]));
+    if (tid < 8) {
+      float mm = sred[0][tid];
+#pragma unroll
+      for (int w = 1; w < kNW; ++w) mm = fmaxf(mm, sred[w][tid]);
+      sM[tid] = mm;
+    }
     __syncthreads();
-    const float M = sM[h];
+    // p = 2^((z - max) * scale * log2 e): the raw-score max is the scaled max
+    const float c = a.scale_log2;
+    const float mc = -sM[h] * c;
     float l = 0.0f;
     if (h < G) {
-      for (int t = ch; t < tend; t += 32) {
-        const float p = __builtin_amdgcn_exp2f(sc[t * 8 + h] - M);
-        sc[t * 8 + h] = p;
-        l += p;
+      // the normaliser sums the rounded weights that P V will use
+      for (int j = ch; j < tend / 2; j += kCh) {
+        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[(2 * j) * 8 + h], c, mc)),
+                                       __builtin_amdgcn_exp2f(fmaf(sc[(2 * j + 1) * 8 + h], c, mc)));
+        sp2[j * 8 + h] = w;
+        l += bf16_lo(w) + bf16_hi(w);
       }
     }
     l += __shfl_xor(l, 8);
@@ -165,61 +260,78 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeKArgs a) {
     l += __shfl_xor(l, 32);
     if (lane < 8) sred[wave][h] = l;
     __syncthreads();
-    if (tid < 8) sL[tid] = (sred[0][tid] + sred[1][tid]) + (sred[2][tid] + sred[3][tid]);
-    __syncthreads();
+    if (tid < 8) {
+      float ll = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) ll += sred[w][tid];
+      sL[tid] = ll;
+      sM[tid] *= c;                    // partition max in the log2 domain for the merge
+    }
+    // (sp2 is complete: the barrier above came after every write)
   }
 
-  // ---------------- phase 3: P V ----------------
+  // ---------------- phase 3: P V with bf16 pairs ----------------
   {
-    const int e4 = (lane & 31) * 4;   // 4 dims
-    const int kh = lane >> 5;         // key half (8 keys)
     float acc[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[h][i] = 0.0f;
-    for (int b = wave; b < nblk; b += 4) {
-      const uint16_t* vb = a.v_cache + (static_cast<int64_t>(sblk[b]) * Hkv + g) * (kBlk * kD);
-      uint4 vr[4];
+    auto pv = [&](int i, uint4 (&vr)[4]) {
+      const int b = wave + kNW * i;
+      const int pair0 = (b * kBlk + kh * 8) / 2;     // first token pair of this lane half
+      if ((b + 1) * kBlk > ntok) {                   // last block: tail slots may hold NaN
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vr[i] = *reinterpret_cast<const uint4*>(vb + (e4 + i) * kBlk + kh * 8);
-      const bool full = (b + 1) * kBlk <= ntok;
-      const int tb = b * kBlk + kh * 8;
+        for (int d = 0; d < 4; ++d) {
+          uint32_t* w = reinterpret_cast<uint32_t*>(&vr[d]);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const float4 plo = *reinterpret_cast<const float4*>(&sc[(tb + kk) * 8]);
-        const float4 phi = *reinterpret_cast<const float4*>(&sc[(tb + kk) * 8 + 4]);
-        const float p[8] = {plo.x, plo.y, plo.z, plo.w, phi.x, phi.y, phi.z, phi.w};
-        const bool live = full || (tb + kk < ntok);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = kk < 2 ? vr[i].x : kk < 4 ? vr[i].y : kk < 6 ? vr[i].z : vr[i].w;
-          float v = (kk & 1) ? bf16_hi(w) : bf16_lo(w);
-          v = live ? v : 0.0f;           // select: tail slots may hold NaN
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][i] = fmaf(p[h], v, acc[h][i]);
+          for (int pp = 0; pp < 4; ++pp) {
+            const int t0 = 2 * (pair0 + pp);
+            w[pp] = t0 >= ntok ? 0u : (t0 + 1 >= ntok ? (w[pp] & 0xffffu) : w[pp]);
+          }
         }
+      }
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const uint4 plo = *reinterpret_cast<const uint4*>(&sp2[(pair0 + pp) * 8]);
+        const uint4 phi = *reinterpret_cast<const uint4*>(&sp2[(pair0 + pp) * 8 + 4]);
+        const uint32_t p[8] = {plo.x, plo.y, plo.z, plo.w, phi.x, phi.y, phi.z, phi.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t w = pp == 0 ? vr[d].x : pp == 1 ? vr[d].y : pp == 2 ? vr[d].z : vr[d].w;
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][d] = dot2_bf16(p[h], w, acc[h][d]);
+        }
+      }
+    };
+    for (int i = 0; i < nbw; i += kNBuf) {
+#pragma unroll
+      for (int j = 0; j < kNBuf; ++j) {
+        load_v(i + j + kNBuf - 1, vbuf[(j + kNBuf - 1) % kNBuf]);
+        if (i + j < nbw) pv(i + j, vbuf[j]);
       }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[h][i] += __shfl_xor(acc[h][i], 32);
+      for (int i = 0; i < 4; ++i) acc[h][i] += dpp<kDppXor1>(acc[h][i]);   // the other key half
+    // sc (aliased by sacc) is no longer read by anyone: phase 2 ended with a barrier
     if (kh == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        *reinterpret_cast<float4*>(&sacc[wave][h * kD + e4]) =
-            make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[wave][h * kD + d0 + 32 * i] = acc[h][i];
     }
   }
   __syncthreads();
 
   // ---------------- epilogue ----------------
   const bool bad = sbad != 0;
-  for (int idx = tid; idx < G * kD; idx += 256) {
+  for (int idx = tid; idx < G * kD; idx += kThreads) {
     const int h = idx / kD, e = idx % kD;
-    float v = (sacc[0][idx] + sacc[1][idx]) + (sacc[2][idx] + sacc[3][idx]);
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kNW; ++w) v += sacc[w][idx];
     if (bad) v = __builtin_nanf("");
     const int qh = g * G + h;
     if (nparts == 1) {
@@ -237,25 +349,61 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeKArgs a) {
   }
 }
 
-// One 128-thread workgroup per (query head, sequence): merge the partitions.
+// Merge of the partitions: one 128-thread workgroup per (query head,
+// sequence), one output element per thread.  Partitions are taken 64 at a
+// time: their (m, l) pairs go to LDS in one round of loads, the weights
+// 2^(m_r - M) follow from the running maximum, and every thread issues the
+// loads of its 64 partial sums back to back, so the merge pays a few memory
+// latencies instead of one per partition.
+constexpr int kMergeBatch = 64;
+
 __global__ __launch_bounds__(128) void decode_reduce_kernel(DecodeKArgs a) {
   const int qh = blockIdx.x, s = blockIdx.y, e = threadIdx.x;
   bool ctx_bad;
   const int ctx = checked_ctx(a, s, &ctx_bad);
   const int nparts = (ctx + kPart - 1) / kPart;
   if (nparts <= 1) return;
+  __shared__ float sm[kMergeBatch], sl[kMergeBatch];
+  __shared__ float sred[2];
   const int64_t base = static_cast<int64_t>(s) * a.num_heads + qh;
   const float* ml = a.ws_ml + base * a.max_parts * 2;
-  const float* acc = a.ws_acc + base * a.max_parts * kD;
-  float M = -INFINITY;
-  for (int r = 0; r < nparts; ++r) M = fmaxf(M, ml[2 * r]);
-  float L = 0.0f, o = 0.0f;
-  for (int r = 0; r < nparts; ++r) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * r] - M);
-    L = fmaf(ml[2 * r + 1], w, L);
-    o = fmaf(acc[static_cast<int64_t>(r) * kD + e], w, o);
+  const float* acc = a.ws_acc + base * a.max_parts * kD + e;
+
+  float M = -INFINITY, L = 0.0f, o = 0.0f;      // running over batches (uniform)
+  for (int c0 = 0; c0 < nparts; c0 += kMergeBatch) {
+    const int cn = min(kMergeBatch, nparts - c0);
+    float x[kMergeBatch];
+#pragma unroll
+    for (int r = 0; r < kMergeBatch; ++r) x[r] = r < cn ? acc[static_cast<int64_t>(c0 + r) * kD] : 0.0f;
+    if (e < cn) {
+      sm[e] = ml[2 * (c0 + e)];
+      sl[e] = ml[2 * (c0 + e) + 1];
+    }
+    __syncthreads();
+    if (e < 64) {                                // wave 0: batch max
+      float mb = e < cn ? sm[e] : -INFINITY;
+      mb = wave_max(mb);
+      if (e == 0) sred[0] = mb;
+    }
+    __syncthreads();
+    const float Mn = fmaxf(M, sred[0]);
+    const float alpha = M > -INFINITY ? __builtin_amdgcn_exp2f(M - Mn) : 0.0f;
+    float lb = 0.0f, ob = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kMergeBatch; ++r) {
+      if (r < cn) {
+        const float w = __builtin_amdgcn_exp2f(sm[r] - Mn);
+        lb = fmaf(sl[r], w, lb);
+        ob = fmaf(x[r], w, ob);
+      }
+    }
+    L = fmaf(L, alpha, lb);
+    o = fmaf(o, alpha, ob);
+    M = Mn;
+    __syncthreads();                             // sm/sl reused by the next batch
   }
-  a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] = f32_to_bf16(o / L);
+  a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
+      f32_to_bf16(ctx_bad ? __builtin_nanf("") : o / L);
 }
 
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
@@ -282,7 +430,7 @@ template <int G>
 static void launch_partial(const DecodeKArgs& k, const AttnArgs& a, const DecodePlan& p,
                            hipStream_t stream) {
   const dim3 grid(p.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL(decode_partial_kernel<G>, grid, dim3(256), 0, stream, k);
+  hipLaunchKernelGGL(decode_partial_kernel<G>, grid, dim3(kThreads), 0, stream, k);
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t stream) {
@@ -308,7 +456,8 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
     k.ws_acc = static_cast<float*>(a.workspace);
     k.ws_ml = k.ws_acc + rows * kD;
   }
-  switch (a.num_heads / a.num_kv_heads) {
+  const int G = a.num_heads / a.num_kv_heads;
+  switch (G) {
     case 1: launch_partial<1>(k, a, p, stream); break;
     case 2: launch_partial<2>(k, a, p, stream); break;
     case 3: launch_partial<3>(k, a, p, stream); break;

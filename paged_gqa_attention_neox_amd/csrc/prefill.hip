@@ -200,20 +200,28 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
     const uint16_t* kp = &sk[cur][krow * kKRow + hl * 8];
+    bf16x8_t ka[kD / 16];                       // all K fragments first: one LDS latency per tile
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      const bf16x8_t ka = as_bf16x8(*reinterpret_cast<const uint4*>(kp + ks * 16));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < kD / 16; ++ks) ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kp + ks * 16));
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], acc, 0, 0, 0);
+    // V fragments for this tile, read while the score MFMAs run
+    bf16x8_t va[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const uint16_t* vp = &sv[cur][(dt * 32 + col) * kVRow + hl * 8];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) va[dt][c] = as_bf16x8(*reinterpret_cast<const uint4*>(vp + c * kB));
     }
 
     // ---- online softmax over this tile (base 2) ----
     float sc[16];
-    const bool diag = kt * kBK + kBK - 1 > pos0 + q0;   // some key may lie past some row
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = acc[r] * a.scale_log2;
-      if (diag) x = (kt * kBK + key_of(r, hl) <= qpos) ? x : -INFINITY;
-      sc[r] = x;
+    for (int r = 0; r < 16; ++r) sc[r] = acc[r] * a.scale_log2;
+    if (kt * kBK + kBK - 1 > pos0 + q0) {        // diagonal tile: some key lies past some row
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = (kt * kBK + key_of(r, hl) <= qpos) ? sc[r] : -INFINITY;
     }
     float mt = sc[0];
 #pragma unroll
@@ -242,14 +250,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint16_t* vp = &sv[cur][(dt * 32 + col) * kVRow + hl * 8];
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8_t va = as_bf16x8(*reinterpret_cast<const uint4*>(vp + c * kB));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], o[dt], 0, 0, 0);
-      }
-    }
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pb[c], o[dt], 0, 0, 0);
 
     if (more) {
       // buffer cur^1 was last read in iteration kt-1, which every wave left
