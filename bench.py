@@ -7,7 +7,10 @@ heads, 4 KV heads, head_dim 128, block 16, batch 64, contexts log-uniform in
 [2048, 32768]).  One step = qwen2_rope_cache_write of the 64 new tokens (rotate
 q/k, write k/v into the paged cache) + qwen2_attn_decode_paged (split-K
 partial kernel + merge kernel).  ``value`` is KV bytes read per step divided
-by the step time (GB/s), inputs resident in HBM.  The KV pool (~2.2 GB) is far
+by the step time (GB/s), inputs resident in HBM.  The K timed steps are
+captured in one HIP graph and replayed once between HIP events on the
+launching stream, so the figures are GPU time without the Python call cost;
+per-call figures come from graphs of K calls of that call alone.  The KV pool (~2.2 GB) is far
 larger than the 256 MB last-level cache, so every step streams KV from HBM.
 
 Also reported on the same line: Qwen2-7B varlen causal prefill (8 sequences
@@ -41,79 +44,84 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_decode(steps, warmup):
+def _graph(fn, reps):
+    """Capture `reps` back-to-back calls of fn (on a side stream, as torch
+    requires) into one HIP graph.  The library calls allocate nothing and
+    record no memsets, so a replay re-runs exactly the captured kernels."""
     import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                     # warm the call path outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time(fn, steps, warmup):
+    """Mean GPU ms per call of fn: `warmup` eager calls, then one replay of a
+    graph holding `steps` calls, bracketed by HIP events on the launching
+    stream (the graph amortizes its launch over the steps and the replay
+    carries no Python call cost).  Also returns the wall ms per call."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    g = _graph(fn, steps)
+    g.replay()                                   # first replay uploads the graph
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def bench_decode(steps, warmup):
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
 
     log("generating the long-context decode workload")
     b = W.qwen2_long_decode()
     dev = runner.DeviceStep(b)
-    torch.cuda.synchronize()
-    for _ in range(warmup):
-        dev.step()
-    torch.cuda.synchronize()
-    ev = [_events(3) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record()
+
+    def step():
         dev.rope_write()
-        ev[i][1].record()
         dev.decode()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    rope_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
-    kv = b.decode_kv_bytes()
-    alg = b.decode_bytes()
-    return dict(batch=b, wall_ms=wall * 1e3, step_ms=step_ms, rope_ms=rope_ms, decode_ms=dec_ms,
-                kv_bytes=kv, decode_alg_bytes=alg, rope_bytes=b.rope_write_bytes())
+    step_ms, wall = _time(step, steps, warmup)
+    rope_ms, _ = _time(dev.rope_write, steps, warmup)
+    dec_ms, _ = _time(dev.decode, steps, warmup)
+    return dict(batch=b, wall_ms=wall, step_ms=step_ms, rope_ms=rope_ms, decode_ms=dec_ms,
+                kv_bytes=b.decode_kv_bytes(), decode_alg_bytes=b.decode_bytes(),
+                rope_bytes=b.rope_write_bytes())
 
 
 def bench_prefill(steps, warmup):
-    import torch
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
 
     b = W.qwen2_prefill()
     dev = runner.DeviceStep(b)
-    for _ in range(warmup):
-        dev.step()
-    torch.cuda.synchronize()
-    ev = [_events(3) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        dev.rope_write()
-        ev[i][1].record()
-        dev.prefill()
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    rope_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    pf_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    flops = b.prefill_flops()
-    return dict(tokens=b.num_tokens, flops=flops, prefill_ms=pf_ms, rope_ms=rope_ms,
+    rope_ms, _ = _time(dev.rope_write, steps, warmup)
+    pf_ms, _ = _time(dev.prefill, steps, warmup)
+    return dict(tokens=b.num_tokens, flops=b.prefill_flops(), prefill_ms=pf_ms, rope_ms=rope_ms,
                 rope_bytes=b.rope_write_bytes())
 
 
 def bench_mixed(steps, warmup):
-    import torch
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
 
     b = W.mixed_tp2()
     dev = runner.DeviceStep(b)
-    for _ in range(warmup):
-        dev.step()
-    torch.cuda.synchronize()
-    e0, e1 = _events(2)
-    e0.record()
-    for _ in range(steps):
-        dev.step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, _ = _time(dev.step, steps, warmup)
     return dict(tokens=b.num_tokens, step_ms=ms, prefill_flops=b.prefill_flops(),
                 decode_kv_bytes=b.decode_kv_bytes())
 

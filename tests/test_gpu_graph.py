@@ -1,0 +1,46 @@
+"""HIP-graph replay of a whole step equals the eager step, bit for bit.
+
+bench.py times the calls as replays of captured HIP graphs; this checks that
+a captured step (rope + cache write, prefill, decode) gives exactly the eager
+results on every replay, with eager work and synchronizations in between.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_gqa_attention_neox_amd import runner
+from paged_gqa_attention_neox_amd import workloads as W
+from gpu_common import require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager_bitwise():
+    require_gpu()
+    b = W.small_case(310, "bf16", 28, 4, 128, context_lens=[300, 77, 1500, 2049],
+                     query_lens=[300, 20, 1, 1], num_prefill=2, keep_logical=False)
+    say("graph: eager step")
+    eager = runner.DeviceStep(b)
+    eager.step()
+    ref = eager.results()
+
+    dev = runner.DeviceStep(b)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"graph: replay {rep}")
+        dev.out.fill_(float("nan"))           # eager work between replays
+        dev.q_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = dev.results()
+        for key in ("q_out", "k_cache", "v_cache", "out"):
+            assert np.array_equal(got[key].view(np.uint16), ref[key].view(np.uint16)), (rep, key)
