@@ -32,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SOURCES = ("decode.hip", "common.h", "kernels.h")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 
 
@@ -161,6 +163,22 @@ def cpu_baseline(batch, budget_s=12.0):
                       "float64 numpy"}
 
 
+def decode_traffic():
+    """HBM bytes per decode call measured with FETCH_SIZE / WRITE_SIZE counter
+    runs (scaled by a plain-copy calibration), as recorded under profiles/;
+    None once the decode kernel sources differ from the ones profiled."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "paged_gqa_attention_neox_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(rec["traffic_bytes_per_launch"]) if rec.get("sources_sha256") == h.hexdigest() else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,7 +254,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": decode_traffic(),
             "alg_bytes_per_launch": int(dec["decode_alg_bytes"]),
             "avg_launch_ms": round(dec["decode_ms"], 4),
         },
