@@ -8,14 +8,20 @@
 // Qwen", §2.1).
 //
 // bf16, head_dim 128, block 16, group G <= 8:
-//   * one workgroup per (KV head, 32-row query tile, sequence), one wave per
-//     query head of the group: the K/V tiles of the group are staged in LDS
-//     once and read by all G waves;
-//   * key tiles of 32 keys (two cache blocks) stream through a ring of four
-//     16 KB LDS stages with direct-to-LDS buffer loads (no register staging),
-//     three tiles in flight; each wave issues the same number of 1 KB loads
-//     per tile (surplus ones have an empty range and land in a scratch line),
-//     so its outstanding-load count at every wait is a compile-time constant;
+//   * one workgroup per (KV head, 16-row query tile, sequence).  A wave owns
+//     32 query columns = 2 heads of the group x 16 rows (an odd group pads
+//     its last wave with a copy of the last head, whose output is dropped);
+//     the workgroup holds two such sets of ceil(G/2) waves, the two key
+//     groups;
+//   * keys stream in super-tiles of 64 (four cache blocks): key group k takes
+//     keys 32k .. 32k + 31 of each.  The two groups' online-softmax states
+//     are merged through LDS at the end, so a query tile's keys are covered
+//     in half the steps of a single group;
+//   * super-tiles (32 KiB of K and V^T) go through a ring of four LDS stages
+//     with direct-to-LDS buffer loads (no register staging), two super-tiles
+//     ahead.  Each wave issues the same number of 1 KiB loads per super-tile
+//     (surplus ones have an empty range and land in a scratch line), so its
+//     outstanding-load count at every wait is a compile-time constant;
 //   * the block ids the workgroup needs are staged in LDS once, so no load
 //     inside the loop depends on another load;
 //   * LDS layouts are XOR-swizzled at 16-byte granularity (the source address
@@ -41,16 +47,17 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace qw {
 
 namespace {
 
 constexpr int kD = 128;
 constexpr int kB = 16;               // tokens per cache block
-constexpr int kBQ = 32;              // query rows per tile
-constexpr int kBK = 32;              // keys per tile
-constexpr int kStage = 16384;        // bytes per LDS stage: K tile 8 KB + V^T tile 8 KB
-constexpr int kLoads = 16;           // 1 KB direct-to-LDS loads per tile (8 K + 8 V)
+constexpr int kBK = 32;              // keys per key group and step
+constexpr int kTile = 16384;         // bytes of one 32-key tile in LDS: K 8 KiB + V^T 8 KiB
+constexpr int kTileLoads = 16;       // 1 KiB direct-to-LDS loads per 32-key tile
 constexpr int kBlockBytes = kB * kD * 2;   // one head's K (or V) of one cache block
 constexpr int kMaxIds = 2048;        // block ids a workgroup stages (contexts up to 32K)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -94,7 +101,13 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// LDS layouts of one stage (16-byte slots):
+// 16 bytes per lane from buffer rs at byte offset voff into LDS at lds + 16 * lane
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+// LDS layout of one 32-key tile (16-byte slots):
 //   K tile: slot(R, c) = R * 16 + (c ^ perm23(R & 15)), key R of the tile
 //           (0..31), dims chunk c (8 dims, 0..15);
 //   V^T tile (bytes 8192..): slot(b, d, h) = b * 256 + d * 2 + (h ^ vswz(d)),
@@ -114,15 +127,16 @@ __device__ __forceinline__ int load_offset(int j, int lane) {
   return d * (kB * 2) + h * 16;
 }
 
-// 16 bytes per lane from buffer rs at byte offset voff into LDS at lds + 16 * lane
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
-}
-
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
-  constexpr int NI = (kLoads + NW - 1) / NW;      // loads per wave per tile
+// KG key groups (1 or 2) of WPG waves each.  A wave owns 32 query columns:
+// one head x 32 rows (KG 1) or two heads x 16 rows (KG 2).
+template <int KG, int WPG>
+__global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArgs a) {
+  constexpr int NW = KG * WPG;                    // waves
+  constexpr int HPW = KG == 1 ? 1 : 2;            // heads per wave
+  constexpr int kBQ = 32 / HPW;                   // query rows per tile
+  constexpr int kStage = KG * kTile;              // one step's keys (32 KG)
+  constexpr int kLoads = KG * kTileLoads;         // loads per step
+  constexpr int NI = (kLoads + NW - 1) / NW;      // loads per wave per step
   // work item of this workgroup: (KV head g, sequence s, query tile qt)
   const int np = a.num_kv_heads * a.num_seqs;     // (g, s) pairs
   int p, z;
@@ -139,6 +153,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
     z = blockIdx.x / np;
     p = blockIdx.x % np;
   }
+  const int G = a.num_heads / a.num_kv_heads;
   const int g = p % a.num_kv_heads, s = p / a.num_kv_heads;
   const int qt = a.num_qtiles - 1 - z;            // longest (last) tiles first
   const int r0 = a.cu_seqlens[s];
@@ -151,14 +166,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   if (r0 < 0 || r0 + n > a.num_tokens) return;    // rows not ours to write
   const int pos0 = ctx - n;                       // position of row 0
   const int qlast = min(q0 + kBQ, n) - 1;         // last valid row of the tile
-  const int nkt = (pos0 + qlast) / kBK + 1;       // key tiles up to the causal limit
+  const int nkt = (pos0 + qlast) / kBK + 1;       // 32-key tiles up to the causal limit
+  const int nst = (nkt + KG - 1) / KG;            // steps (KG tiles each)
   const int nblk = (ctx + kB - 1) / kB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int hq = g * NW + wave;                   // query head of this wave
+  const int kg = wave / WPG;                      // key group
+  const int hw = wave - kg * WPG;                 // wave within the group
   const int hl = lane >> 5;                       // lane half
   const int col = lane & 31;                      // query column of this lane
+  const int hslot = HPW * hw + col / kBQ;         // head of the group for this column
+  const bool hvalid = hslot < G;
+  const int hq = g * G + min(hslot, G - 1);       // query head (padding column: a copy)
+  const int rq = col % kBQ;                       // row within the tile
   const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
 
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
@@ -167,12 +188,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t st3[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t trash[1024];
   __shared__ int sbad;
-  __shared__ __attribute__((aligned(16))) int sids[kMaxIds];   // block ids of tiles 0 .. nkt-1
+  __shared__ __attribute__((aligned(16))) int sids[kMaxIds];   // block ids of super-tiles 0 .. nst-1
 
-  // Q^T operand: column = query row q0 + col (clamped), 8 dims per k-step
+  // Q^T operand: column = (head, row q0 + rq (clamped)), 8 dims per k-step
   bf16x8_t qb[kD / 16];
   {
-    const int row = min(q0 + col, n - 1);
+    const int row = min(q0 + rq, n - 1);
     const uint16_t* qp = a.q + static_cast<int64_t>(r0 + row) * a.q_stride +
                          static_cast<int64_t>(hq) * kD + hl * 8;
 #pragma unroll
@@ -182,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   // stage the block ids; ids past the context or out of the pool read block 0
   {
     bool lbad = false;
-    for (int i = tid; i < 2 * nkt; i += NW * 64) {
+    for (int i = tid; i < 2 * KG * nst; i += NW * 64) {
       int blk = 0;
       if (i < nblk) {
         blk = bt[i];
@@ -198,43 +219,56 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
     if (lbad) sbad = 1;
   }
 
-  // per-lane source offsets of this wave's loads (load j = wave + NW * i)
-  int voff[NI];
+  // per-lane source offsets of this wave's loads (load j = wave + NW * i;
+  // j / 16 is the 32-key tile of the step, j % 16 the load within it)
+  // (kept in registers when there are few; recomputed per load otherwise)
+  constexpr int NV = NI <= 8 ? NI : 1;
+  int voff[NV];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int j = wave + NW * i;
-    voff[i] = j < kLoads ? load_offset(j, lane) : 0;
+    voff[i] = j < kLoads ? load_offset(j & 15, lane) : 0;
   }
   const int64_t head_off = static_cast<int64_t>(g) * (kB * kD);
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * (kB * kD);
 
-  // issue the loads of key tile t into stage dst
+  // issue the loads of step t's keys into stage dst; a 32-key tile past the
+  // causal limit gets empty ranges (no traffic)
   auto issue = [&](int t, uint8_t* dst) {
-    const int2 ids = *reinterpret_cast<const int2*>(&sids[2 * t]);
-    const int b0 = uniform(ids.x), b1 = uniform(ids.y);
+    int b0, b1, b2 = 0, b3 = 0;                   // block ids of the step
+    if constexpr (KG == 2) {
+      const int4 ids = *reinterpret_cast<const int4*>(&sids[4 * t]);
+      b0 = uniform(ids.x), b1 = uniform(ids.y), b2 = uniform(ids.z), b3 = uniform(ids.w);
+    } else {
+      const int2 ids = *reinterpret_cast<const int2*>(&sids[2 * t]);
+      b0 = uniform(ids.x), b1 = uniform(ids.y);
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int j = wave + NW * i;
-      const bool live = j < kLoads;
-      const int blk = ((j >> 2) & 1) ? b1 : b0;
-      const uint16_t* base = ((j & 15) >= 8 ? a.v_cache : a.k_cache) + blk * blk_elems + head_off;
+      const int half = KG == 2 ? (j >> 4) & 1 : 0, jj = j & 15;
+      const bool live = j < kLoads && KG * t + half < nkt;
+      const int bi = 2 * half + ((jj >> 2) & 1);
+      const int blk = bi == 0 ? b0 : bi == 1 ? b1 : bi == 2 ? b2 : b3;
+      const uint16_t* base = (jj >= 8 ? a.v_cache : a.k_cache) + blk * blk_elems + head_off;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(base), static_cast<short>(0), live ? kBlockBytes : 0, 0x00020000);
-      uint8_t* l = live ? dst + j * 1024 : trash;
-      load_lds16(rs, l, voff[i]);
+      const int vo = NI <= 8 ? voff[i < NV ? i : 0] : (j < kLoads ? load_offset(jj, lane) : 0);
+      load_lds16(rs, j < kLoads ? dst + half * kTile + jj * 1024 : trash, vo);
     }
   };
 
   // V^T entries of keys >= ctx may hold anything (NaN): zero them, a zero
   // probability times NaN would poison the row
   auto sanitize = [&](int t, uint8_t* stg) {
-    uint4* vt = reinterpret_cast<uint4*>(stg + 8192);
-    for (int sl = tid; sl < 512; sl += NW * 64) {
-      const int b = sl >> 8, u = sl & 255, d = u >> 1;
+    for (int sl = tid; sl < KG * 512; sl += NW * 64) {
+      const int half = sl >> 9, w = sl & 511;
+      const int b = w >> 8, u = w & 255, d = u >> 1;
       const int h = (u & 1) ^ vswz(d);
-      const int key0 = t * kBK + b * kB + h * 8;
+      const int key0 = t * KG * kBK + half * kBK + b * kB + h * 8;
       if (key0 + 8 > ctx) {
-        uint4 v = vt[sl];
+        uint4* vt = reinterpret_cast<uint4*>(stg + half * kTile + 8192) + w;
+        uint4 v = *vt;
         uint32_t* e = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -244,7 +278,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
           if (k0 + 1 >= ctx) x &= 0x0000ffffu;
           e[q] = x;
         }
-        vt[sl] = v;
+        *vt = v;
       }
     }
   };
@@ -255,7 +289,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
   float m = -INFINITY, l = 0.0f;                  // running max (log2 units), sum
-  const int qpos = pos0 + q0 + col;
+  const int qpos = pos0 + q0 + rq;
   const float c2 = a.scale_log2;
 
   // K row read by this lane for the S^T MFMA: MFMA row i = col holds key
@@ -263,25 +297,29 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   const int krow = (col & 16) | perm23(col & 15);
   const int kx = hl ^ (col & 15);
   const int vlane = (col * 2 + (hl ^ vswz(col))) * 16;
-  const int sani_tile = (ctx % kBK) ? ctx / kBK : -1;   // tile holding keys >= ctx
+  const int sani_st = (ctx % (KG * kBK)) ? ctx / (KG * kBK) : -1;   // step holding keys >= ctx
+  const int tile_off = kg * kTile;                // this key group's tile in a stage
 
-  // S^T = K Q^T of the key tile in stage stg
+  // S^T = K Q^T of this group's tile in stage stg
   auto qk = [&](const uint8_t* stg) {
     f32x16_t acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    const uint8_t* kp = stg + krow * (kD * 2);
-    bf16x8_t ka[kD / 16];
+    const uint8_t* kp = stg + tile_off + krow * (kD * 2);
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
-      ka[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kp + ((2 * ks) ^ kx) * 16));
+    for (int kb = 0; kb < kD / 16; kb += 4) {     // K fragments four at a time (register pressure)
+      bf16x8_t ka[4];
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[ks], acc, 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        ka[i] = as_bf16x8(*reinterpret_cast<const uint4*>(kp + ((2 * (kb + i)) ^ kx) * 16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qb[kb + i], acc, 0, 0, 0);
+    }
     return acc;
   };
 
-  // causal mask of a diagonal tile (some key lies past some row of the tile)
+  // causal mask of a diagonal 32-key tile kt (some key lies past some row)
   auto mask = [&](int kt, f32x16_t& sc) {
     if (kt * kBK + kBK - 1 > pos0 + q0) {
 #pragma unroll
@@ -308,24 +346,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c * 8 + j], c2, -m));
-        lt += p;
-        pb[c][j] = static_cast<__bf16>(p);
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[c * 8 + j], c2, -m));
+        lt += pr;
+        pb[c][j] = static_cast<__bf16>(pr);
       }
     }
     l = l * alpha + lt;
     return alpha;
   };
 
-  // O^T = alpha O^T + V^T P^T for the key tile in stage stg
+  // O^T = alpha O^T + V^T P^T for this group's tile in stage stg
   auto pv = [&](float alpha, const uint8_t* stg) {
-    bf16x8_t va[4][2];
-    const uint8_t* vp = stg + 8192 + vlane;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        va[dt][c] = as_bf16x8(*reinterpret_cast<const uint4*>(vp + c * 4096 + dt * 1024));
+    const uint8_t* vp = stg + tile_off + 8192 + vlane;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -333,53 +365,98 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c) {                 // V fragments per 16-key half (register pressure)
+      bf16x8_t va[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][c], pb[c], o[dt], 0, 0, 0);
+        va[dt] = as_bf16x8(*reinterpret_cast<const uint4*>(vp + c * 4096 + dt * 1024));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pb[c], o[dt], 0, 0, 0);
+    }
   };
 
-  // one key tile: wait until it is in LDS for every wave (the waits leave
-  // the loads of later tiles outstanding), refill the stage of tile kt - 1
-  // (every wave passed the barrier, so it finished with it) with tile
-  // kt + 3, then scores, softmax and PV of tile kt
-  auto step = [&](int kt, uint8_t* cur, uint8_t* refill) {
-    if (kt + 2 < nkt) wait_vm<2 * NI>();
-    else if (kt + 1 < nkt) wait_vm<NI>();
+  // softmax and PV of a score tile of 32-key tile kt held in stage stg
+  auto finish = [&](int kt, f32x16_t sc, const uint8_t* stg) {
+    mask(kt, sc);
+    const float alpha = softmax(sc);
+    pv(alpha, stg);
+  };
+
+  // One super-tile step: wait until super-tile t is in LDS for every wave
+  // (the wait leaves the loads of super-tile t + 1 outstanding), refill the
+  // stage of super-tile t - 2 (every wave passed the barrier, so it finished
+  // with it) with super-tile t + 2, then scores, softmax and PV of this key
+  // group's tile of super-tile t.  (Refilling t - 1 instead would work too;
+  // the ring keeps one spare stage so the loads run two super-tiles ahead.)
+  auto step = [&](int t, uint8_t* cur, uint8_t* refill) {
+    if (t + 1 < nst) wait_vm<NI>();
     else wait_vm<0>();
     barrier();
-    if (kt == sani_tile) {
-      sanitize(kt, cur);
+    if (t == sani_st) {
+      sanitize(t, cur);
       wait_lds();
       barrier();
     }
-    if (kt + 3 < nkt) issue(kt + 3, refill);
-    f32x16_t sc = qk(cur);
-    mask(kt, sc);
-    const float alpha = softmax(sc);
-    pv(alpha, cur);
+    if (t + 2 < nst) issue(t + 2, refill);
+    if (KG * t + kg < nkt) finish(KG * t + kg, qk(cur), cur);
   };
 
   issue(0, st0);
-  if (nkt > 1) issue(1, st1);
-  if (nkt > 2) issue(2, st2);
-  for (int kt = 0; kt < nkt; kt += 4) {
-    step(kt, st0, st3);
-    if (kt + 1 >= nkt) break;
-    step(kt + 1, st1, st0);
-    if (kt + 2 >= nkt) break;
-    step(kt + 2, st2, st1);
-    if (kt + 3 >= nkt) break;
-    step(kt + 3, st3, st2);
+  if (nst > 1) issue(1, st1);
+  for (int t = 0; t < nst; t += 4) {
+    step(t, st0, st2);
+    if (t + 1 >= nst) break;
+    step(t + 1, st1, st3);
+    if (t + 2 >= nst) break;
+    step(t + 2, st2, st0);
+    if (t + 3 >= nst) break;
+    step(t + 3, st3, st1);
   }
+
   __syncthreads();
   if (sbad) bad = true;
+  if constexpr (KG == 2) {
+  // ---- merge the key groups through LDS (the ring is free now) ----
+  uint8_t* mg = hw == 0 ? st0 : hw == 1 ? st1 : hw == 2 ? st2 : st3;
+  float4* mo = reinterpret_cast<float4*>(mg);
+  float* ml = reinterpret_cast<float*>(mg + 16 * 64 * 16);
+  if (kg == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        mo[(dt * 4 + r4) * 64 + lane] = make_float4(o[dt][r4 * 4], o[dt][r4 * 4 + 1],
+                                                    o[dt][r4 * 4 + 2], o[dt][r4 * 4 + 3]);
+    ml[lane] = m;
+    ml[64 + lane] = l;
+  }
+  __syncthreads();
+  if (kg == 1) return;
+  {
+    const float m1 = ml[lane], l1 = ml[64 + lane];
+    const float mm = fmaxf(m, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m - mm);
+    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 v = mo[(dt * 4 + r4) * 64 + lane];
+        o[dt][r4 * 4 + 0] = o[dt][r4 * 4 + 0] * a0 + v.x * a1;
+        o[dt][r4 * 4 + 1] = o[dt][r4 * 4 + 1] * a0 + v.y * a1;
+        o[dt][r4 * 4 + 2] = o[dt][r4 * 4 + 2] * a0 + v.z * a1;
+        o[dt][r4 * 4 + 3] = o[dt][r4 * 4 + 3] * a0 + v.w * a1;
+      }
+  }
+  }
 
-  // ---- epilogue: O = O^T / l, column col -> row q0 + col ----
+  // ---- epilogue: O = O^T / l, column col -> (row q0 + rq, head hq) ----
   const float lt = l + __shfl_xor(l, 32);
   const float inv = bad ? __builtin_nanf("") : 1.0f / lt;
-  const int row = q0 + col;
-  if (row < n) {
+  const int row = q0 + rq;
+  if (row < n && hvalid) {
     uint16_t* op = a.out + static_cast<int64_t>(r0 + row) * a.out_stride + static_cast<int64_t>(hq) * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -395,19 +472,37 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   }
 }
 
-template <int NW>
-void launch_nw(const PrefillKArgs& k, const AttnArgs& a, hipStream_t stream) {
-  const int64_t np = static_cast<int64_t>(a.num_kv_heads) * a.num_seqs;
+template <int KG, int WPG>
+void launch_kg(const PrefillKArgs& k, hipStream_t stream) {
+  const int64_t np = static_cast<int64_t>(k.num_kv_heads) * k.num_seqs;
   const int64_t slots = k.pairs_per_xcd > 0 ? int64_t{8} * k.pairs_per_xcd : np;
   const dim3 grid(static_cast<unsigned>(slots * k.num_qtiles));
-  hipLaunchKernelGGL(prefill_mfma_kernel<NW>, grid, dim3(NW * 64), 0, stream, k);
+  hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG>), grid, dim3(KG * WPG * 64), 0, stream, k);
 }
 
 }  // namespace
 
+// One or two key groups.  Estimated time of each layout = max(longest work
+// item, average work per CU) from measured costs on this GPU: a workgroup's
+// start and finish (ids, first K/V tile, merge, stores) ~4 us with one group
+// and ~5 us with two; a 32-key tile ~1.0 us (one group, 32 rows x G heads);
+// a 64-key step ~1.5 us (two groups, 16 rows x 2 ceil(G/2) heads).  Only
+// host-side maxima are known, so a row's keys are estimated from the longest
+// context and chunk: c - n / 2 on average, c at most.
+int key_groups(const AttnArgs& a) {
+  const double c = a.max_context_len, n = a.max_query_len;
+  const double rows = static_cast<double>(a.num_kv_heads) * a.num_tokens;   // (row, KV head) pairs
+  const double avg_keys = c - 0.5 * n;
+  const double cu = 256.0;
+  const double t1 = std::max(4.0 + c / 32.0, rows / 32.0 * (4.0 + avg_keys / 32.0) / cu);
+  const double t2 = std::max(5.0 + 1.5 * c / 64.0, rows / 16.0 * (5.0 + 1.5 * avg_keys / 64.0) / cu);
+  return t2 < t1 ? 2 : 1;
+}
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
-  const int ids = 2 * ((a.max_context_len + kBK - 1) / kBK);
+  const int KG = key_groups(a);
+  const int ids = 2 * KG * ((a.max_context_len + KG * kBK - 1) / (KG * kBK));
   const bool mfma = a.dtype == kBF16 && a.head_dim == kD && a.block_size == kB && G >= 1 &&
                     G <= 8 && ids <= kMaxIds;
   if (!mfma) return launch_attn_generic(a, stream);
@@ -428,19 +523,29 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   k.num_heads = a.num_heads;
   k.num_kv_heads = a.num_kv_heads;
   k.num_seqs = a.num_seqs;
-  k.num_qtiles = (a.max_query_len + kBQ - 1) / kBQ;
+  const int rows = KG == 1 ? 32 : 16;
+  k.num_qtiles = (a.max_query_len + rows - 1) / rows;
   const int np = a.num_kv_heads * a.num_seqs;
   k.pairs_per_xcd = np >= 8 ? (np + 7) / 8 : 0;
   k.scale_log2 = a.scale * kLog2e;
-  switch (G) {
-    case 1: launch_nw<1>(k, a, stream); break;
-    case 2: launch_nw<2>(k, a, stream); break;
-    case 3: launch_nw<3>(k, a, stream); break;
-    case 4: launch_nw<4>(k, a, stream); break;
-    case 5: launch_nw<5>(k, a, stream); break;
-    case 6: launch_nw<6>(k, a, stream); break;
-    case 7: launch_nw<7>(k, a, stream); break;
-    default: launch_nw<8>(k, a, stream); break;
+  if (KG == 1) {
+    switch (G) {
+      case 1: launch_kg<1, 1>(k, stream); break;
+      case 2: launch_kg<1, 2>(k, stream); break;
+      case 3: launch_kg<1, 3>(k, stream); break;
+      case 4: launch_kg<1, 4>(k, stream); break;
+      case 5: launch_kg<1, 5>(k, stream); break;
+      case 6: launch_kg<1, 6>(k, stream); break;
+      case 7: launch_kg<1, 7>(k, stream); break;
+      default: launch_kg<1, 8>(k, stream); break;
+    }
+  } else {
+    switch ((G + 1) / 2) {
+      case 1: launch_kg<2, 1>(k, stream); break;
+      case 2: launch_kg<2, 2>(k, stream); break;
+      case 3: launch_kg<2, 3>(k, stream); break;
+      default: launch_kg<2, 4>(k, stream); break;
+    }
   }
   return hipGetLastError();
 }
