@@ -156,6 +156,11 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   const int G = a.num_heads / a.num_kv_heads;
   const int g = p % a.num_kv_heads, s = p / a.num_kv_heads;
   const int qt = a.num_qtiles - 1 - z;            // longest (last) tiles first
+  const int tid = threadIdx.x;
+  // this thread's block-table entry, fetched before (and in parallel with)
+  // the sequence metadata: the table row needs only s
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const int bt_early = tid < a.max_blocks ? bt[tid] : 0;
   const int r0 = a.cu_seqlens[s];
   const int n = a.cu_seqlens[s + 1] - r0;
   const int q0 = qt * kBQ;
@@ -169,7 +174,6 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   const int nkt = (pos0 + qlast) / kBK + 1;       // 32-key tiles up to the causal limit
   const int nst = (nkt + KG - 1) / KG;            // steps (KG tiles each)
   const int nblk = (ctx + kB - 1) / kB;
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int kg = wave / WPG;                      // key group
@@ -177,10 +181,8 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   const int hl = lane >> 5;                       // lane half
   const int col = lane & 31;                      // query column of this lane
   const int hslot = HPW * hw + col / kBQ;         // head of the group for this column
-  const bool hvalid = hslot < G;
   const int hq = g * G + min(hslot, G - 1);       // query head (padding column: a copy)
   const int rq = col % kBQ;                       // row within the tile
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
 
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
@@ -200,13 +202,15 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     for (int ks = 0; ks < kD / 16; ++ks) qb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + ks * 16));
   }
 
-  // stage the block ids; ids past the context or out of the pool read block 0
+  // stage the block ids; ids past the context or out of the pool read block
+  // 0.  The barrier waits for the table loads only: the Q loads (issued
+  // later) stay in flight until the first tile's wait.
   {
     bool lbad = false;
     for (int i = tid; i < 2 * KG * nst; i += NW * 64) {
       int blk = 0;
       if (i < nblk) {
-        blk = bt[i];
+        blk = i == tid ? bt_early : bt[i];
         if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
           lbad = true;
           blk = 0;
@@ -215,7 +219,8 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
       sids[i] = blk;
     }
     if (tid == 0) sbad = 0;
-    __syncthreads();
+    wait_lds();
+    barrier();
     if (lbad) sbad = 1;
   }
 
@@ -383,14 +388,13 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     pv(alpha, stg);
   };
 
-  // One super-tile step: wait until super-tile t is in LDS for every wave
-  // (the wait leaves the loads of super-tile t + 1 outstanding), refill the
-  // stage of super-tile t - 2 (every wave passed the barrier, so it finished
-  // with it) with super-tile t + 2, then scores, softmax and PV of this key
-  // group's tile of super-tile t.  (Refilling t - 1 instead would work too;
-  // the ring keeps one spare stage so the loads run two super-tiles ahead.)
+  // One step: wait until step t's keys are in LDS for every wave (the wait
+  // leaves the loads of steps t + 1 and t + 2 outstanding), refill the stage
+  // of step t - 1 (every wave passed the barrier, so it finished with it)
+  // with step t + 3, then scores, softmax and PV of this key group's tile.
   auto step = [&](int t, uint8_t* cur, uint8_t* refill) {
-    if (t + 1 < nst) wait_vm<NI>();
+    if (t + 2 < nst) wait_vm<2 * NI>();
+    else if (t + 1 < nst) wait_vm<NI>();
     else wait_vm<0>();
     barrier();
     if (t == sani_st) {
@@ -398,27 +402,28 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
       wait_lds();
       barrier();
     }
-    if (t + 2 < nst) issue(t + 2, refill);
+    if (t + 3 < nst) issue(t + 3, refill);
     if (KG * t + kg < nkt) finish(KG * t + kg, qk(cur), cur);
   };
 
   issue(0, st0);
   if (nst > 1) issue(1, st1);
+  if (nst > 2) issue(2, st2);
   for (int t = 0; t < nst; t += 4) {
-    step(t, st0, st2);
+    step(t, st0, st3);
     if (t + 1 >= nst) break;
-    step(t + 1, st1, st3);
+    step(t + 1, st1, st0);
     if (t + 2 >= nst) break;
-    step(t + 2, st2, st0);
+    step(t + 2, st2, st1);
     if (t + 3 >= nst) break;
-    step(t + 3, st3, st1);
+    step(t + 3, st3, st2);
   }
 
   __syncthreads();
   if (sbad) bad = true;
+  uint8_t* mg = hw == 0 ? st0 : hw == 1 ? st1 : hw == 2 ? st2 : st3;
   if constexpr (KG == 2) {
   // ---- merge the key groups through LDS (the ring is free now) ----
-  uint8_t* mg = hw == 0 ? st0 : hw == 1 ? st1 : hw == 2 ? st2 : st3;
   float4* mo = reinterpret_cast<float4*>(mg);
   float* ml = reinterpret_cast<float*>(mg + 16 * 64 * 16);
   if (kg == 1) {
@@ -453,21 +458,39 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   }
 
   // ---- epilogue: O = O^T / l, column col -> (row q0 + rq, head hq) ----
+  // The wave's 32 x 128 bf16 tile goes through LDS (16-byte slots, slot of
+  // (column, dims chunk c) = column * 16 + (c ^ (column & 15))) so that each
+  // store instruction writes four whole 256-byte output rows.
   const float lt = l + __shfl_xor(l, 32);
   const float inv = bad ? __builtin_nanf("") : 1.0f / lt;
-  const int row = q0 + rq;
-  if (row < n && hvalid) {
-    uint16_t* op = a.out + static_cast<int64_t>(r0 + row) * a.out_stride + static_cast<int64_t>(hq) * kD;
+  uint8_t* ot;                                    // this wave's 8 KiB in the (free) ring
+  if constexpr (KG == 2) {
+    ot = mg + 16 * 64 * 16 + 512;                 // after the merge data of the wave's stage
+  } else {
+    uint8_t* sg = (wave >> 1) == 0 ? st0 : (wave >> 1) == 1 ? st1 : (wave >> 1) == 2 ? st2 : st3;
+    ot = sg + (wave & 1) * 8192;
+  }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = dt * 32 + r4 * 8 + hl * 4;
-        uint2 w;
-        w.x = pack_bf16x2(o[dt][r4 * 4 + 0] * inv, o[dt][r4 * 4 + 1] * inv);
-        w.y = pack_bf16x2(o[dt][r4 * 4 + 2] * inv, o[dt][r4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d) = w;
-      }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = dt * 4 + r4;                  // dims chunk of d = 8c + 4 hl .. + 3
+      uint2 w;
+      w.x = pack_bf16x2(o[dt][r4 * 4 + 0] * inv, o[dt][r4 * 4 + 1] * inv);
+      w.y = pack_bf16x2(o[dt][r4 * 4 + 2] * inv, o[dt][r4 * 4 + 3] * inv);
+      *reinterpret_cast<uint2*>(ot + (col * 16 + (c ^ (col & 15))) * 16 + hl * 8) = w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int idx = k * 64 + lane;
+    const int oc = idx >> 4, c = idx & 15;        // column, dims chunk
+    const uint4 v = *reinterpret_cast<const uint4*>(ot + (oc * 16 + (c ^ (oc & 15))) * 16);
+    const int orow = q0 + oc % kBQ, oslot = HPW * hw + oc / kBQ;
+    if (orow < n && oslot < G) {
+      uint16_t* op = a.out + static_cast<int64_t>(r0 + orow) * a.out_stride +
+                     static_cast<int64_t>(g * G + oslot) * kD + c * 8;
+      *reinterpret_cast<uint4*>(op) = v;
     }
   }
 }
