@@ -31,13 +31,18 @@ with the function that uses it):
   * softmax is base e, max-subtracted, masked keys excluded;
   * rotated q and k, and the output, are rounded once from float64 to the
     storage dtype (round to nearest even); v is copied bit for bit.
+  * FP8 KV cache ([P2] §4.1 and §4.2 list FP8 KV-cache quantization with
+    per-layer cache scale parameters; §6.3 names the E4M3FN format): the
+    cache holds E4M3FN codes of the exact rotated key (or the value) divided
+    by one scale per tensor (k_scale, v_scale), rounded once to nearest even
+    and saturated at +-448; attention reads code value * scale.
 
 Cache layouts (interface definition):
   K cache [num_blocks][num_kv_heads][block_size][head_dim]
   V cache [num_blocks][num_kv_heads][head_dim][block_size]
 
 Storage conventions: bf16 tensors are numpy uint16 bit patterns, fp32 tensors
-are numpy float32.
+are numpy float32, FP8 cache entries are numpy uint8 E4M3FN codes.
 """
 from __future__ import annotations
 
@@ -47,7 +52,7 @@ __all__ = [
     "rope_inv_freq", "rope_neox", "to_f64", "from_f64", "f64_to_bf16_bits",
     "bf16_bits_to_f64", "rope_cache_write", "gather_kv", "causal_visible",
     "softmax_rows", "kv_head_for", "default_scale", "attention_varlen",
-    "attention_decode", "run_step",
+    "attention_decode", "run_step", "fp8_e4m3_decode", "fp8_e4m3_encode", "E4M3_MAX",
 ]
 
 
@@ -140,10 +145,58 @@ def rope_neox(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# FP8 E4M3FN codes (the FP8 KV cache)
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0                    # largest finite E4M3FN value, 1.75 * 2**8
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3FN code -> float64.  Bit 7 sign, bits 6..3 exponent e (bias 7),
+    bits 2..0 mantissa m: e = 0 gives m/8 * 2**-6 (subnormal), otherwise
+    (1 + m/8) * 2**(e - 7); the two codes with e = 15, m = 7 are NaN (there
+    is no infinity).  ([P2] §6.3 names the format; the layout is its
+    definition.)"""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, sign * mag)
+
+
+def fp8_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float64 -> E4M3FN code, rounded once to nearest (ties to the even
+    code) and saturated at +-448 (a cache entry must stay finite: the plain
+    reading where the pages give no overflow rule).  Zero keeps its sign."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(x).astype(np.int64) << 7
+    a = np.minimum(np.abs(x), E4M3_MAX)                     # saturate (0x7f is NaN)
+    out = np.zeros(x.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    # subnormal range: multiples of 2**-9; m = 8 lands on the smallest normal
+    out[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)
+    nrm = ~sub
+    if np.any(nrm):
+        an = a[nrm]
+        e = np.floor(np.log2(an)).astype(np.int64)
+        # guard the floor(log2) against rounding at exact powers of two
+        e = np.where(np.exp2(e.astype(np.float64)) > an, e - 1, e)
+        e = np.where(np.exp2((e + 1).astype(np.float64)) <= an, e + 1, e)
+        frac = an / np.exp2(e.astype(np.float64))          # [1, 2), exact
+        m = np.rint((frac - 1.0) * 8.0).astype(np.int64)    # ties to even
+        carry = m == 8
+        e = np.where(carry, e + 1, e)
+        m = np.where(carry, 0, m)
+        out[nrm] = ((e + 7) << 3) | m
+    return (out | sign).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
 # 1-3. split fused QKV, rotate, write the paged cache
 # ---------------------------------------------------------------------------
 def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
-                     num_heads, num_kv_heads, head_dim, block_size, theta):
+                     num_heads, num_kv_heads, head_dim, block_size, theta,
+                     cache_dtype=None, k_scale=1.0, v_scale=1.0):
     """Split the fused QKV rows, rotate q and k, scatter k and v into the cache.
 
     qkv: storage [T][(H + 2 Hkv) * d]; columns [0, H d) are q, then Hkv k
@@ -152,7 +205,9 @@ def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
     inputs are not modified.  For each token with slot >= 0:
         block = slot // B, offset = slot % B
         K[block][g][offset][:] = rot(k[t][g]);  V[block][g][:][offset] = v[t][g]
-    Slots not named keep their previous bits ([P3] §2.1 paged blocks)."""
+    Slots not named keep their previous bits ([P3] §2.1 paged blocks).
+    cache_dtype "fp8": the caches hold E4M3FN codes, K = code(rot(k) /
+    k_scale), V = code(v / v_scale), each one rounding from float64."""
     H, Hkv, d, B = num_heads, num_kv_heads, head_dim, block_size
     qkv = np.asarray(qkv)
     T = qkv.shape[0]
@@ -161,8 +216,12 @@ def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
     q_rot = rope_neox(x[:, :H], positions, theta)
     k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)
     q_out = from_f64(q_rot, dtype)
-    k_store = from_f64(k_rot, dtype)
-    v_store = heads[:, H + Hkv:]              # stored unchanged (bit copy)
+    if cache_dtype == "fp8":
+        k_store = fp8_e4m3_encode(k_rot / float(k_scale))
+        v_store = fp8_e4m3_encode(x[:, H + Hkv:] / float(v_scale))
+    else:
+        k_store = from_f64(k_rot, dtype)
+        v_store = heads[:, H + Hkv:]          # stored unchanged (bit copy)
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
     for t in range(T):
@@ -175,16 +234,21 @@ def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
     return q_out, kc, vc
 
 
-def gather_kv(k_cache, v_cache, block_table_row, context_len, block_size, dtype):
+def gather_kv(k_cache, v_cache, block_table_row, context_len, block_size, dtype,
+              cache_dtype=None, k_scale=1.0, v_scale=1.0):
     """Logical keys/values 0..c-1 of one sequence through its block table.
 
     Logical position j lives in physical block block_table[j // B] at offset
     j % B ([P3] §2.1; [P5] §5 seq.block_table).  Returns float64 K, V of
-    shape [c][Hkv][d]."""
+    shape [c][Hkv][d] (FP8 caches: code value times the tensor's scale)."""
     B = block_size
     j = np.arange(int(context_len))
     blk = np.asarray(block_table_row)[j // B].astype(np.int64)
     off = j % B
+    if cache_dtype == "fp8":
+        K = fp8_e4m3_decode(np.asarray(k_cache)[blk, :, off, :]) * float(k_scale)
+        V = fp8_e4m3_decode(np.asarray(v_cache)[blk, :, :, off]) * float(v_scale)
+        return K, V
     K = to_f64(np.asarray(k_cache)[blk, :, off, :], dtype)
     V = to_f64(np.asarray(v_cache)[blk, :, :, off], dtype)
     return K, V
@@ -224,7 +288,8 @@ def default_scale(head_dim: int) -> float:
 
 def attention_varlen(q, k_cache, v_cache, cu_seqlens_q, context_lens, block_tables,
                      num_heads, num_kv_heads, head_dim, block_size, dtype,
-                     scale=None, return_probs=False):
+                     scale=None, return_probs=False, cache_dtype=None, k_scale=1.0,
+                     v_scale=1.0):
     """Causal GQA attention of packed query rows over the paged cache.
 
     q: storage [T][H][d] (already rotated).  Sequence s owns rows
@@ -247,7 +312,8 @@ def attention_varlen(q, k_cache, v_cache, cu_seqlens_q, context_lens, block_tabl
         if n == 0:
             probs.append(None)
             continue
-        K, V = gather_kv(k_cache, v_cache, block_tables[s], c, block_size, dtype)
+        K, V = gather_kv(k_cache, v_cache, block_tables[s], c, block_size, dtype,
+                         cache_dtype, k_scale, v_scale)
         vis = causal_visible(n, c)
         ps = []
         for h in range(H):
@@ -264,7 +330,8 @@ def attention_varlen(q, k_cache, v_cache, cu_seqlens_q, context_lens, block_tabl
 
 
 def attention_decode(q, k_cache, v_cache, block_tables, context_lens,
-                     num_heads, num_kv_heads, head_dim, block_size, dtype, scale=None):
+                     num_heads, num_kv_heads, head_dim, block_size, dtype, scale=None,
+                     cache_dtype=None, k_scale=1.0, v_scale=1.0):
     """Single-token decode: one query row per sequence at position c - 1,
     attending to all c cached keys (its own key included, written before the
     attention) -- [P3] §2.1 PagedAttention.  The same definition as
@@ -272,7 +339,8 @@ def attention_decode(q, k_cache, v_cache, block_tables, context_lens,
     S = len(context_lens)
     cu = np.arange(S + 1, dtype=np.int64)
     return attention_varlen(q, k_cache, v_cache, cu, context_lens, block_tables,
-                            num_heads, num_kv_heads, head_dim, block_size, dtype, scale)
+                            num_heads, num_kv_heads, head_dim, block_size, dtype, scale,
+                            cache_dtype=cache_dtype, k_scale=k_scale, v_scale=v_scale)
 
 
 def run_step(batch, k_cache=None, v_cache=None):
@@ -283,10 +351,12 @@ def run_step(batch, k_cache=None, v_cache=None):
     sh = batch.shape
     kc0 = batch.k_cache if k_cache is None else k_cache
     vc0 = batch.v_cache if v_cache is None else v_cache
+    cd = getattr(sh, "cache_dtype", None)
+    ks, vs = getattr(sh, "k_scale", 1.0), getattr(sh, "v_scale", 1.0)
     q_out, kc, vc = rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
                                      kc0, vc0, sh.num_heads, sh.num_kv_heads, sh.head_dim,
-                                     sh.block_size, sh.rope_theta)
+                                     sh.block_size, sh.rope_theta, cd, ks, vs)
     out = attention_varlen(q_out, kc, vc, batch.cu_seqlens_q, batch.context_lens,
                            batch.block_tables, sh.num_heads, sh.num_kv_heads, sh.head_dim,
-                           sh.block_size, sh.dtype)
+                           sh.block_size, sh.dtype, cache_dtype=cd, k_scale=ks, v_scale=vs)
     return {"q_out": q_out, "k_cache": kc, "v_cache": vc, "out": out}

@@ -27,8 +27,10 @@ A token at logical position ``p`` of a sequence lives in physical block
 ``block * B + offset``.
 
 Values are stored as raw storage bits: bf16 as ``uint16`` arrays, fp32 as
-``float32`` arrays.  Unused blocks, and slots past a sequence's context, hold
-NaN so that any read outside the context shows up in the output.
+``float32`` arrays, an FP8 cache as ``uint8`` E4M3FN codes (torch's
+float8_e4m3fn conversion of the drawn value divided by the cache's scale).
+Unused blocks, and slots past a sequence's context, hold NaN (code 0x7f in an
+FP8 cache) so that any read outside the context shows up in the output.
 
 Draw order for every workload (one ``numpy.random.default_rng(seed)``):
 lengths -> prefix-sharing choices -> block permutation -> fused QKV rows ->
@@ -46,6 +48,7 @@ import torch
 
 BF16_NAN_BITS = np.uint16(0x7FC0)
 F32_NAN = np.float32("nan")
+FP8_NAN_CODE = np.uint8(0x7F)
 
 DTYPES = ("bf16", "f32")
 
@@ -66,11 +69,18 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def storage_nan(dtype: str):
-    return BF16_NAN_BITS if dtype == "bf16" else F32_NAN
+    return {"bf16": BF16_NAN_BITS, "f32": F32_NAN, "fp8": FP8_NAN_CODE}[dtype]
 
 
 def storage_np_dtype(dtype: str):
-    return np.uint16 if dtype == "bf16" else np.float32
+    return {"bf16": np.uint16, "f32": np.float32, "fp8": np.uint8}[dtype]
+
+
+def to_fp8_codes(x: np.ndarray, scale: float) -> np.ndarray:
+    """Synthetic FP8 cache contents: float32 values divided by the scale,
+    clamped to the finite range and converted with torch's float8_e4m3fn."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)) / float(scale)
+    return t.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def normal_storage(rng: np.random.Generator, shape, scale: float, dtype: str) -> np.ndarray:
@@ -101,6 +111,9 @@ class AttnShape:
     dtype: str = "bf16"
     rope_theta: float = 1.0e6
     max_position: int = 32768
+    cache_dtype: Optional[str] = None   # None: the caches use `dtype`; "fp8": E4M3FN codes
+    k_scale: float = 1.0                # FP8 cache: value = code * scale
+    v_scale: float = 1.0
 
     @property
     def group(self) -> int:
@@ -118,6 +131,14 @@ class AttnShape:
     @property
     def elem_bytes(self) -> int:
         return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def cache_storage(self) -> str:
+        return self.cache_dtype or self.dtype
+
+    @property
+    def cache_elem_bytes(self) -> int:
+        return 1 if self.cache_dtype == "fp8" else self.elem_bytes
 
 
 @dataclass
@@ -193,7 +214,7 @@ class Batch:
     def decode_kv_bytes(self) -> int:
         sh = self.shape
         c = self.context_lens[self.num_prefill:].astype(np.int64)
-        return int(c.sum()) * 2 * sh.num_kv_heads * sh.head_dim * sh.elem_bytes
+        return int(c.sum()) * 2 * sh.num_kv_heads * sh.head_dim * sh.cache_elem_bytes
 
     def decode_bytes(self) -> int:
         """KV read once per KV head + q read + out written + block-table rows + context lens."""
@@ -221,7 +242,7 @@ class Batch:
         e = sh.elem_bytes
         d = sh.head_dim
         return (t * sh.qkv_width * e + t * sh.num_heads * d * e
-                + t * 2 * sh.num_kv_heads * d * e + 8 * t)
+                + t * 2 * sh.num_kv_heads * d * sh.cache_elem_bytes + 8 * t)
 
 
 # --------------------------------------------------------------------------
@@ -275,8 +296,20 @@ def _build(name: str, shape: AttnShape, seed: int, rng: np.random.Generator,
         row += n
 
     # pool, NaN everywhere, then the context that earlier steps left behind
-    k_cache = np.full((pool_size, Hkv, B, d), storage_nan(dt), dtype=storage_np_dtype(dt))
-    v_cache = np.full((pool_size, Hkv, d, B), storage_nan(dt), dtype=storage_np_dtype(dt))
+    cdt = shape.cache_storage
+    k_cache = np.full((pool_size, Hkv, B, d), storage_nan(cdt), dtype=storage_np_dtype(cdt))
+    v_cache = np.full((pool_size, Hkv, d, B), storage_nan(cdt), dtype=storage_np_dtype(cdt))
+
+    def draw_kv(shape3):
+        """Pre-existing context rows: (k, v) in the cache's storage, plus the
+        logical values in the step dtype when the cache is FP8."""
+        if cdt != "fp8":
+            kk = normal_storage(rng, shape3, value_scale, dt)
+            vv = normal_storage(rng, shape3, value_scale, dt)
+            return kk, vv, kk, vv
+        kf = normal_storage(rng, shape3, value_scale, "f32")
+        vf = normal_storage(rng, shape3, value_scale, "f32")
+        return to_fp8_codes(kf, shape.k_scale), to_fp8_codes(vf, shape.v_scale), kf, vf
 
     def put(block_ids: np.ndarray, pos: np.ndarray, kv: np.ndarray, vv: np.ndarray):
         """Place logical rows kv/vv ([m][Hkv][d], positions pos[0].. contiguous,
@@ -290,7 +323,7 @@ def _build(name: str, shape: AttnShape, seed: int, rng: np.random.Generator,
         blk = block_ids[pos[0] // B: pos[0] // B + nblk]
         pad = nblk * B - m
         if pad:
-            fill = np.full((pad, Hkv, d), storage_nan(dt), dtype=kv.dtype)
+            fill = np.full((pad, Hkv, d), storage_nan(cdt), dtype=kv.dtype)
             kv = np.concatenate([kv, fill])
             vv = np.concatenate([vv, fill])
         kb = kv.reshape(nblk, B, Hkv, d)
@@ -303,9 +336,8 @@ def _build(name: str, shape: AttnShape, seed: int, rng: np.random.Generator,
     shared_k = shared_v = None
     if spb:
         pos = np.arange(shared_prefix_len, dtype=np.int64)
-        shared_k = normal_storage(rng, (shared_prefix_len, Hkv, d), value_scale, dt)
-        shared_v = normal_storage(rng, (shared_prefix_len, Hkv, d), value_scale, dt)
-        put(shared_ids.astype(np.int64), pos, shared_k, shared_v)
+        sk, sv, shared_k, shared_v = draw_kv((shared_prefix_len, Hkv, d))
+        put(shared_ids.astype(np.int64), pos, sk, sv)
     for s in range(S):
         n, c = int(query_lens[s]), int(context_lens[s])
         m = c - n
@@ -313,10 +345,9 @@ def _build(name: str, shape: AttnShape, seed: int, rng: np.random.Generator,
         assert m >= start or m == 0 or not shares_prefix[s]
         cnt = max(0, m - start)
         pos = np.arange(start, start + cnt, dtype=np.int64)
-        kk = normal_storage(rng, (cnt, Hkv, d), value_scale, dt)
-        vv = normal_storage(rng, (cnt, Hkv, d), value_scale, dt)
+        kc_, vc_, kk, vv = draw_kv((cnt, Hkv, d))
         if cnt:
-            put(bt[s].astype(np.int64), pos, kk, vv)
+            put(bt[s].astype(np.int64), pos, kc_, vc_)
         if keep_logical:
             if start:
                 pre_k.append(np.concatenate([shared_k[:min(m, start)], kk]))
@@ -407,6 +438,27 @@ def qwen2_long_decode(seed: int = 4, num_seqs: int = 64, keep_logical: bool = Fa
                   keep_logical=keep_logical)
 
 
+# FP8 cache scales of the FP8 workloads: with N(0,1) values the codes use
+# the upper part of the E4M3FN range (|x| / scale up to ~180 < 448) and stay
+# clear of its subnormals; deliberately not powers of two.
+FP8_K_SCALE = 0.0312
+FP8_V_SCALE = 0.0287
+
+
+def qwen2_long_decode_fp8(seed: int = 4, num_seqs: int = 64, keep_logical: bool = False) -> Batch:
+    """The Qwen2-7B long-context decode with an FP8 (E4M3FN) KV cache: same
+    lengths, rows and draws as the bf16 workload, the cache holding codes of
+    value / scale (k_scale 0.0312, v_scale 0.0287)."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128, cache_dtype="fp8",
+                      k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(math.log(2048), math.log(32768), size=num_seqs)
+    ctx = np.clip(np.floor(np.exp(u)), 2048, 32768).astype(np.int32)
+    return _build("qwen2_7b_decode_b64_ctx[2048,32768]_fp8kv", shape, seed, rng, ctx,
+                  np.ones(num_seqs, np.int32), 0, np.zeros(num_seqs, bool), 0, 1.0,
+                  keep_logical=keep_logical)
+
+
 def mixed_tp2(seed: int = 5, keep_logical: bool = False) -> Batch:
     """Mixed chunked batch at the TP=2 share of Qwen2-7B, bf16: 14 q heads,
     2 KV heads, head_dim 128.  4 prefill chunks of 512 tokens (2 continue a
@@ -432,10 +484,12 @@ def mixed_tp2(seed: int = 5, keep_logical: bool = False) -> Batch:
 def small_case(seed: int, dtype: str, num_heads: int, num_kv_heads: int, head_dim: int,
                context_lens, query_lens, num_prefill: int, block_size: int = 16,
                value_scale: float = 1.0, keep_logical: bool = True, shares_prefix=None,
-               shared_prefix_len: int = 0) -> Batch:
+               shared_prefix_len: int = 0, cache_dtype=None, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> Batch:
     """A custom small batch (tests): explicit lengths, any head layout."""
     shape = AttnShape(num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
-                      block_size=block_size, dtype=dtype)
+                      block_size=block_size, dtype=dtype, cache_dtype=cache_dtype,
+                      k_scale=k_scale, v_scale=v_scale)
     rng = np.random.default_rng(seed)
     ctx = np.asarray(context_lens, np.int32)
     ql = np.asarray(query_lens, np.int32)
@@ -450,4 +504,5 @@ WORKLOADS = {
     "qwen2_prefill": qwen2_prefill,
     "qwen2_long_decode": qwen2_long_decode,
     "mixed_tp2": mixed_tp2,
+    "qwen2_long_decode_fp8": qwen2_long_decode_fp8,
 }

@@ -407,7 +407,117 @@ def pin_decode_is_last_prefill_row(R):
     del sh
 
 
+# ---------------------------------------------------------------------------
+# FP8 E4M3FN cache codes
+# ---------------------------------------------------------------------------
+def pin_fp8_decode_table(R):
+    """Values the E4M3FN definition fixes (sign, 4-bit exponent with bias 7,
+    3-bit mantissa, subnormals below 2**-6, NaN at S.1111.111, no infinity)."""
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x48: 4.0, 0x77: 240.0, 0x78: 256.0,
+             0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in table.items():
+        got = float(R.fp8_e4m3_decode(np.array([c], np.uint8))[0])
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), (hex(c), got, v)
+    assert np.isnan(R.fp8_e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def pin_fp8_matches_torch(R):
+    """torch's float8_e4m3fn: decode of all 256 codes, and round-to-nearest-
+    even encoding of random in-range values and of every midpoint between
+    neighbouring codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    dec = R.fp8_e4m3_decode(codes)
+    fin = np.isfinite(ref)
+    assert np.array_equal(dec[fin], ref[fin]) and np.isnan(dec[~fin]).all()
+    rng = np.random.default_rng(11)
+    pos = np.sort(ref[fin & (ref > 0)])
+    x = np.concatenate([rng.standard_normal(20000) * np.exp2(rng.integers(-14, 9, 20000)),
+                        (pos[:-1] + pos[1:]) / 2, -(pos[:-1] + pos[1:]) / 2, ref[fin]])
+    x = x[np.abs(x) <= 448.0]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(R.fp8_e4m3_encode(x), want)
+
+
+def pin_fp8_roundtrip_ties_saturation(R):
+    """Every finite code re-encodes to itself; ties go to the even mantissa;
+    magnitudes past 448 saturate; the relative error of a normal value is at
+    most 2**-4 (half a unit in the last of 3 mantissa bits)."""
+    codes = np.arange(256, dtype=np.uint8)
+    fin = (codes & 0x7F) != 0x7F
+    assert np.array_equal(R.fp8_e4m3_encode(R.fp8_e4m3_decode(codes[fin])), codes[fin])
+    ties = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 432.0: 0x7E}
+    for v, c in ties.items():
+        assert int(R.fp8_e4m3_encode(np.array([v]))[0]) == c, (v, c)
+    big = np.array([448.0, 449.0, 464.0, 465.0, 1e6, -500.0, -1e30])
+    assert R.fp8_e4m3_encode(big).tolist() == [0x7E] * 5 + [0xFE] * 2
+    rng = np.random.default_rng(12)
+    x = rng.uniform(2.0 ** -6, 448.0, 50000) * rng.choice([-1.0, 1.0], 50000)
+    err = np.abs(R.fp8_e4m3_decode(R.fp8_e4m3_encode(x)) - x)
+    assert np.all(err <= 2.0 ** -4 * np.abs(x) * (1 + 1e-12))
+
+
+def pin_fp8_cache_write(R):
+    """FP8 cache write: values that are exact E4M3FN multiples of the scale
+    are stored exactly; other K and V entries land within the format's
+    half-step of the float64 reference rows; slots not named keep their
+    previous codes."""
+    b = W.small_case(61, "bf16", 4, 2, 16, context_lens=[20, 5], query_lens=[20, 5],
+                     num_prefill=2, keep_logical=True)
+    sh = b.shape
+    ks, vs = 0.0312, 0.0287
+    kc0 = np.full(b.k_cache.shape, 0x55, np.uint8)
+    vc0 = np.full(b.v_cache.shape, 0xAA, np.uint8)
+    _, kc, vc = R.rope_cache_write(b.qkv, sh.dtype, b.positions, b.slot_mapping, kc0, vc0,
+                                   sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
+                                   sh.rope_theta, "fp8", ks, vs)
+    T, H, Hkv, d, B = b.num_tokens, sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size
+    heads = R.bf16_bits_to_f64(b.qkv).reshape(T, H + 2 * Hkv, d)
+    krot = R.rope_neox(heads[:, H:H + Hkv], b.positions, sh.rope_theta)
+    written = np.zeros(kc.shape[:3], bool)
+    for t in range(T):
+        blk, off = divmod(int(b.slot_mapping[t]), B)
+        written[blk, :, off] = True
+        kd = R.fp8_e4m3_decode(kc[blk, :, off, :]) * ks
+        vd = R.fp8_e4m3_decode(vc[blk, :, :, off]) * vs
+        for got, ref, sc in ((kd, krot[t], ks), (vd, heads[t, H + Hkv:], vs)):
+            tol = np.maximum(2.0 ** -4 * np.abs(ref), 2.0 ** -10 * sc) * (1 + 1e-9)
+            assert np.all(np.abs(got - ref) <= tol)
+    assert np.all(kc[~written] == 0x55)
+    assert np.all(vc.transpose(0, 1, 3, 2)[~written] == 0xAA)
+    # exact multiples of the scale: the codes' own values come back exactly
+    vals = R.fp8_e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    xs = (vals * 0.25)[None, :]
+    assert np.array_equal(R.fp8_e4m3_encode(xs / 0.25)[0], np.arange(0, 0x7F, dtype=np.uint8))
+
+
+def pin_fp8_attention_reads_dequantized_cache(R):
+    """Attention over an FP8 cache equals attention over a float cache holding
+    the decoded values times the scales (power-of-two scales keep the float
+    copy exact)."""
+    b = W.small_case(62, "bf16", 8, 2, 16, context_lens=[40, 9, 33], query_lens=[7, 1, 33],
+                     num_prefill=3, keep_logical=True)
+    sh = b.shape
+    ks, vs = 0.25, 2.0
+    rng = np.random.default_rng(63)
+    kc = rng.integers(0, 256, b.k_cache.shape).astype(np.uint8)
+    vc = rng.integers(0, 256, b.v_cache.shape).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x38
+    vc[(vc & 0x7F) == 0x7F] = 0xB8
+    kf = (R.fp8_e4m3_decode(kc) * ks).astype(np.float32)
+    vf = (R.fp8_e4m3_decode(vc) * vs).astype(np.float32)
+    q = R.from_f64(rng.standard_normal((b.num_tokens, sh.num_heads, sh.head_dim)), "f32")
+    args = (b.cu_seqlens_q, b.context_lens, b.block_tables, sh.num_heads, sh.num_kv_heads,
+            sh.head_dim, sh.block_size, "f32")
+    want = R.attention_varlen(q, kf, vf, *args)
+    got = R.attention_varlen(q, kc, vc, *args, cache_dtype="fp8", k_scale=ks, v_scale=vs)
+    assert np.array_equal(got, want)
+
+
 ALL_PINS = [
+    pin_fp8_decode_table, pin_fp8_matches_torch, pin_fp8_roundtrip_ties_saturation,
+    pin_fp8_cache_write, pin_fp8_attention_reads_dequantized_cache,
     pin_bf16_rounding_values, pin_bf16_rounding_matches_torch,
     pin_rope_unit_vector_neox, pin_rope_frequency_closed_forms, pin_rope_identity_at_zero,
     pin_rope_norm_preserved, pin_rope_relative_position, pin_rope_composition,

@@ -52,6 +52,18 @@ MUTATIONS = [
     ("attention_varlen", "z = scale * (qf[r0:r1, h, :] @ K[:, g, :].T)",
      "z = scale * (qf[r0:r1, h, :] @ V[:, g, :].T)"),
     ("attention_varlen", "n, c = r1 - r0, int(context_lens[s])", "n, c = r1 - r0, int(context_lens[s]) - 1"),
+    # FP8 cache codes and scales
+    ("fp8_e4m3_decode", "(1.0 + m / 8.0)", "(m / 8.0)"),                  # implicit one dropped
+    ("fp8_e4m3_decode", "np.exp2((e - 7)", "np.exp2((e - 8)"),            # wrong bias
+    ("fp8_e4m3_encode", "m = np.rint((frac - 1.0) * 8.0)", "m = np.floor((frac - 1.0) * 8.0)"),
+    ("fp8_e4m3_encode", "a = np.minimum(np.abs(x), E4M3_MAX)", "a = np.abs(x)"),   # no saturation
+    ("fp8_e4m3_encode", "np.rint(a[sub] / 2.0 ** -9)", "np.rint(a[sub] / 2.0 ** -10)"),
+    ("rope_cache_write", "k_store = fp8_e4m3_encode(k_rot / float(k_scale))",
+     "k_store = fp8_e4m3_encode(k_rot * float(k_scale))"),
+    ("rope_cache_write", "v_store = fp8_e4m3_encode(x[:, H + Hkv:] / float(v_scale))",
+     "v_store = fp8_e4m3_encode(x[:, H + Hkv:] / float(k_scale))"),
+    ("gather_kv", "V = fp8_e4m3_decode(np.asarray(v_cache)[blk, :, :, off]) * float(v_scale)",
+     "V = fp8_e4m3_decode(np.asarray(v_cache)[blk, :, :, off]) * float(k_scale)"),
 ]
 
 
