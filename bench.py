@@ -105,6 +105,24 @@ def bench_decode(steps, warmup):
                 rope_bytes=b.rope_write_bytes())
 
 
+def bench_decode_fp8(steps, warmup):
+    """The long-context decode with an FP8 (E4M3FN) KV cache: half the KV bytes."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    log("generating the long-context decode workload with an FP8 cache")
+    b = W.qwen2_long_decode_fp8()
+    dev = runner.DeviceStep(b)
+
+    def step():
+        dev.rope_write()
+        dev.decode()
+    step_ms, _ = _time(step, steps, warmup)
+    dec_ms, _ = _time(dev.decode, steps, warmup)
+    return dict(step_ms=step_ms, decode_ms=dec_ms, kv_bytes=b.decode_kv_bytes(),
+                alg_bytes=b.decode_bytes(), seqs=b.num_seqs)
+
+
 def bench_prefill(steps, warmup):
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
@@ -218,6 +236,8 @@ def main():
         log(f"prefill: {res['prefill']['prefill_ms']:.3f} ms")
         res["mixed"] = bench_mixed(args.steps, args.warmup)
         log(f"mixed: {res['mixed']['step_ms']:.3f} ms")
+        res["fp8"] = bench_decode_fp8(args.steps, args.warmup)
+        log(f"fp8 decode: step {res['fp8']['step_ms']:.3f} ms (decode {res['fp8']['decode_ms']:.3f})")
 
     b = dec["batch"]
     value = dec["kv_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
@@ -279,6 +299,20 @@ def main():
             "workload": "qwen2-7b tp=2 share mixed step: 4x512 prefill chunks + 96 decodes, seed 5",
             "step_ms": round(m["step_ms"], 4),
             "tokens_per_s": round(m["tokens"] / (m["step_ms"] * 1e-3), 1),
+        }
+    if "fp8" in res:
+        f = res["fp8"]
+        out["fp8_kv_decode"] = {
+            "workload": "the same qwen2-7b long-context decode with an FP8 E4M3FN KV cache "
+                        "(k_scale 0.0312, v_scale 0.0287), seed 4",
+            "kv_bytes_per_step": int(f["kv_bytes"]),
+            "ms_per_step": round(f["step_ms"], 4),
+            "decode_ms": round(f["decode_ms"], 4),
+            "kv_read_GB/s": round(f["kv_bytes"] / (f["step_ms"] * 1e-3) / 1e9, 2),
+            "decode_alg_GB/s": round(f["alg_bytes"] / (f["decode_ms"] * 1e-3) / 1e9, 2),
+            "hbm_frac": round(f["alg_bytes"] / (f["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(f["seqs"] / (f["step_ms"] * 1e-3), 1),
+            "speedup_vs_bf16_cache": round(dec["step_ms"] / f["step_ms"], 3),
         }
     if not args.no_cpu:
         log("CPU oracle baseline")

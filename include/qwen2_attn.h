@@ -191,6 +191,65 @@ int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride,
                             int dtype, hipStream_t stream);
 
 /*
+ * FP8 KV cache.  The three calls below are the ones above with a cache of
+ * one-byte E4M3FN codes (OCP FP8: sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; largest finite value 448; no infinity; S.1111.111 is NaN)
+ * and one scale per tensor: a cached key is k_scale * value(code), a cached
+ * value v_scale * value(code).  Layouts are unchanged ([num_blocks][Hkv][B][d]
+ * and [num_blocks][Hkv][d][B]), one byte per element, so a (block, KV head)
+ * tile is 2 KiB at head_dim 128.  q, k, v and out keep `dtype` (bf16 or
+ * f32).  k_scale, v_scale must be finite and > 0 (else QW_ERR_SHAPE).
+ * "Qwen2大模型架构解析与vLLM优化实践", §4.1-4.2 (FP8 / INT8 KV-cache
+ * quantization, per-layer cache scale parameters) and §6.3 (the E4M3FN
+ * format).
+ *
+ * qwen2_rope_cache_write_fp8: as qwen2_rope_cache_write, except that the
+ * cache receives code(rot(k) / k_scale) and code(v / v_scale): the exact
+ * float64 rotation (or the value) divided by the scale, rounded once to the
+ * nearest code (ties to even) and saturated to +-448.  q_out is written as
+ * in qwen2_rope_cache_write.
+ */
+int qwen2_rope_cache_write_fp8(const void* q, int64_t q_row_stride,
+                               void* q_out, int64_t q_out_row_stride,
+                               const void* k, int64_t k_row_stride,
+                               const void* v, int64_t v_row_stride,
+                               const int32_t* positions, const int32_t* slot_mapping,
+                               const double* cos_sin, int max_position,
+                               void* k_cache, void* v_cache, int num_blocks,
+                               int num_tokens, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int dtype,
+                               float k_scale, float v_scale, hipStream_t stream);
+
+/*
+ * qwen2_attn_prefill_varlen_fp8: as qwen2_attn_prefill_varlen over an FP8
+ * cache (keys and values read as scale * value(code)).
+ */
+int qwen2_attn_prefill_varlen_fp8(const void* q, int64_t q_row_stride,
+                                  const void* k_cache, const void* v_cache, int num_blocks,
+                                  const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  void* out, int64_t out_row_stride,
+                                  int num_seqs, int num_tokens, int max_query_len,
+                                  int max_context_len, int num_heads, int num_kv_heads,
+                                  int head_dim, int block_size, float scale, int dtype,
+                                  float k_scale, float v_scale, hipStream_t stream);
+
+/*
+ * qwen2_attn_decode_paged_fp8: as qwen2_attn_decode_paged over an FP8 cache;
+ * the workspace is sized by qwen2_attn_decode_workspace_size with the same
+ * arguments (it does not depend on the cache format).
+ */
+int qwen2_attn_decode_paged_fp8(const void* q, int64_t q_row_stride,
+                                const void* k_cache, const void* v_cache, int num_blocks,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens,
+                                void* out, int64_t out_row_stride,
+                                void* workspace, size_t workspace_bytes,
+                                int num_seqs, int max_context_len, int num_heads,
+                                int num_kv_heads, int head_dim, int block_size, float scale,
+                                int dtype, float k_scale, float v_scale, hipStream_t stream);
+
+/*
  * Verify the device-metadata contract on HOST copies (tests, debugging).
  * positions, slot_mapping: HOST int32 [num_tokens] (either may be NULL to
  * skip it).  cu_seqlens_q: HOST int32 [num_seqs + 1], or NULL for a decode

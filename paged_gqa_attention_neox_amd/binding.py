@@ -36,6 +36,12 @@ SIGNATURES = {
     "qwen2_attn_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "qwen2_attn_decode_paged": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _i64, _p, _sz, _i,
                                      _i, _i, _i, _i, _i, _f, _i, _p]),
+    "qwen2_rope_cache_write_fp8": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
+                                        _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _f, _p]),
+    "qwen2_attn_prefill_varlen_fp8": (_i, [_p, _i64, _p, _p, _i, _p, _p, _p, _i, _p, _i64, _i,
+                                           _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _f, _p]),
+    "qwen2_attn_decode_paged_fp8": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _i64, _p, _sz,
+                                         _i, _i, _i, _i, _i, _i, _f, _i, _f, _f, _p]),
     "qwen2_check_metadata_host": (_i, [_p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i]),
     "qwen2_status_string": (ctypes.c_char_p, [_i]),
     "qwen2_last_error": (ctypes.c_char_p, []),
@@ -190,6 +196,76 @@ def qwen2_attn_decode_paged(q, k_cache, v_cache, block_tables, context_lens, out
                                          _i32(context_lens), op, os_, wp, wb, q.shape[0],
                                          max_context_len, num_heads, num_kv_heads, head_dim,
                                          block_size, float(scale), _dtype(q), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3FN) KV cache: the caches are uint8 code tensors of the same layouts
+def _fp8_caches(k_cache, v_cache, num_kv_heads):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dim() != 4 or t.shape[1] != num_kv_heads or t.dtype != torch.uint8:
+            raise ValueError(f"{name} must be a uint8 [num_blocks][num_kv_heads][..] code tensor")
+
+
+def qwen2_rope_cache_write_fp8(q, q_out, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
+                               num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                               k_scale: float, v_scale: float, stream=None) -> None:
+    """As qwen2_rope_cache_write; the caches receive E4M3FN codes of
+    rot(k) / k_scale and v / v_scale."""
+    T = q.shape[0]
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim or cos_sin.dtype != torch.float64:
+        raise ValueError("cos_sin must be float64 [max_position][head_dim]")
+    _fp8_caches(k_cache, v_cache, num_kv_heads)
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(q_out, num_heads * head_dim)
+    kp, ks = _rows(k, num_kv_heads * head_dim)
+    vp, vs = _rows(v, num_kv_heads * head_dim)
+    _check("qwen2_rope_cache_write_fp8",
+           lib().qwen2_rope_cache_write_fp8(qp, qs, op, os_, kp, ks, vp, vs, _i32(positions),
+                                            _i32(slot_mapping), cos_sin.data_ptr(),
+                                            cos_sin.shape[0], k_cache.data_ptr(),
+                                            v_cache.data_ptr(), k_cache.shape[0], T, num_heads,
+                                            num_kv_heads, head_dim, block_size, _dtype(q),
+                                            float(k_scale), float(v_scale), _stream(stream)))
+
+
+def qwen2_attn_prefill_varlen_fp8(q, k_cache, v_cache, cu_seqlens_q, context_lens, block_tables,
+                                  out, max_query_len: int, max_context_len: int, num_heads: int,
+                                  num_kv_heads: int, head_dim: int, block_size: int, scale: float,
+                                  k_scale: float, v_scale: float, stream=None) -> None:
+    """As qwen2_attn_prefill_varlen over FP8 code caches."""
+    _fp8_caches(k_cache, v_cache, num_kv_heads)
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(out, num_heads * head_dim)
+    S = context_lens.shape[0]
+    _check("qwen2_attn_prefill_varlen_fp8",
+           lib().qwen2_attn_prefill_varlen_fp8(qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                                               k_cache.shape[0], _i32(cu_seqlens_q),
+                                               _i32(context_lens), _i32(block_tables),
+                                               block_tables.shape[1], op, os_, S, q.shape[0],
+                                               max_query_len, max_context_len, num_heads,
+                                               num_kv_heads, head_dim, block_size, float(scale),
+                                               _dtype(q), float(k_scale), float(v_scale),
+                                               _stream(stream)))
+
+
+def qwen2_attn_decode_paged_fp8(q, k_cache, v_cache, block_tables, context_lens, out, workspace,
+                                max_context_len: int, num_heads: int, num_kv_heads: int,
+                                head_dim: int, block_size: int, scale: float, k_scale: float,
+                                v_scale: float, stream=None) -> None:
+    """As qwen2_attn_decode_paged over FP8 code caches."""
+    _fp8_caches(k_cache, v_cache, num_kv_heads)
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(out, num_heads * head_dim)
+    wp = workspace.data_ptr() if workspace is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("qwen2_attn_decode_paged_fp8",
+           lib().qwen2_attn_decode_paged_fp8(qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                                             k_cache.shape[0], _i32(block_tables),
+                                             block_tables.shape[1], _i32(context_lens), op, os_,
+                                             wp, wb, q.shape[0], max_context_len, num_heads,
+                                             num_kv_heads, head_dim, block_size, float(scale),
+                                             _dtype(q), float(k_scale), float(v_scale),
+                                             _stream(stream)))
 
 
 def qwen2_check_metadata_host(positions, slot_mapping, cu_seqlens_q, context_lens, block_tables,

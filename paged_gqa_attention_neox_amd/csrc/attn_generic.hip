@@ -1,8 +1,8 @@
 // Generic causal GQA attention over the paged cache, one query row and head
 // per thread, fp32 arithmetic with an online (running-max) softmax.
 //
-// It serves the fp32 storage path, head_dim 64, and group sizes the tuned
-// bf16 kernels do not instantiate; it is the plain, per-row statement of the
+// It serves the fp32 storage path, head_dim 64, group sizes the tuned bf16
+// kernels do not instantiate, and FP8 (E4M3FN) caches in prefill; it is the plain, per-row statement of the
 // method: row i of a sequence with n new rows and context c sits at position
 // c - n + i and attends to keys 0..c-n+i ("Qwen2大模型架构解析与vLLM优化实践",
 // §7.3 causal mask; "Qwen 开源工程笔记", §3 varlen rows), head h reads KV
@@ -16,11 +16,18 @@ namespace qw {
 template <typename T> __device__ __forceinline__ float ld(const T* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+// cache element: the storage type itself, or an E4M3FN code (uint8)
+template <typename C> __device__ __forceinline__ float ldc(const C* p) { return ld<C>(p); }
+template <> __device__ __forceinline__ float ldc<uint8_t>(const uint8_t* p) {
+  return __builtin_amdgcn_cvt_f32_fp8(static_cast<uint32_t>(*p), 0);
+}
 template <typename T> __device__ __forceinline__ T st(float v);
 template <> __device__ __forceinline__ float st<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t st<uint16_t>(float v) { return f32_to_bf16(v); }
 
-template <typename T, int D>
+// C: cache element type (T, or uint8_t E4M3FN codes whose values are scaled
+// by k_scale / v_scale: folded into the query scaling and the final divide)
+template <typename T, typename C, int D>
 __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
   const int s = blockIdx.z, h = blockIdx.y;
   const int row = blockIdx.x * 64 + threadIdx.x;
@@ -42,14 +49,16 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
   const int64_t t = static_cast<int64_t>(r0) + row;
   if (r0 < 0 || t >= a.num_tokens) return;       // rows outside the packed batch (bad cu_seqlens)
   const T* qp = static_cast<const T*>(a.q) + t * a.q_stride + static_cast<int64_t>(h) * D;
-  const T* kc = static_cast<const T*>(a.k_cache);
-  const T* vc = static_cast<const T*>(a.v_cache);
+  const C* kc = static_cast<const C*>(a.k_cache);
+  const C* vc = static_cast<const C*>(a.v_cache);
+  const bool f8 = sizeof(C) == 1;
+  const float qs = a.scale * (f8 ? a.k_scale : 1.0f);
   const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
 
   float qv[D], acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    qv[e] = ld<T>(qp + e) * a.scale;
+    qv[e] = ld<T>(qp + e) * qs;
     acc[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
@@ -61,21 +70,21 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
       break;
     }
     const int off = j % B;
-    const T* kr = kc + ((static_cast<int64_t>(blk) * Hkv + g) * B + off) * D;
+    const C* kr = kc + ((static_cast<int64_t>(blk) * Hkv + g) * B + off) * D;
     float z = 0.0f;
 #pragma unroll
-    for (int e = 0; e < D; ++e) z = fmaf(qv[e], ld<T>(kr + e), z);
+    for (int e = 0; e < D; ++e) z = fmaf(qv[e], ldc<C>(kr + e), z);
     const float mn = fmaxf(m, z);
     const float alpha = expf(m - mn);
     const float pz = expf(z - mn);
     l = fmaf(l, alpha, pz);
-    const T* vr = vc + (static_cast<int64_t>(blk) * Hkv + g) * D * B + off;
+    const C* vr = vc + (static_cast<int64_t>(blk) * Hkv + g) * D * B + off;
 #pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] = fmaf(acc[e], alpha, pz * ld<T>(vr + static_cast<int64_t>(e) * B));
+    for (int e = 0; e < D; ++e) acc[e] = fmaf(acc[e], alpha, pz * ldc<C>(vr + static_cast<int64_t>(e) * B));
     m = mn;
   }
   T* op = static_cast<T*>(a.out) + t * a.out_stride + static_cast<int64_t>(h) * D;
-  const float inv = bad ? __builtin_nanf("") : 1.0f / l;
+  const float inv = bad ? __builtin_nanf("") : (f8 ? a.v_scale : 1.0f) / l;
 #pragma unroll
   for (int e = 0; e < D; ++e) op[e] = st<T>(acc[e] * inv);
 }
@@ -83,13 +92,16 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream) {
   const int rows = a.cu_seqlens ? a.max_query_len : 1;
   const dim3 grid((rows + 63) / 64, a.num_heads, a.num_seqs);
+#define QW_GEN(T, C, D) hipLaunchKernelGGL((attn_generic_kernel<T, C, D>), grid, dim3(64), 0, stream, a)
+  const bool d128 = a.head_dim == 128;
   if (a.dtype == kBF16) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((attn_generic_kernel<uint16_t, 128>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((attn_generic_kernel<uint16_t, 64>), grid, dim3(64), 0, stream, a);
+    if (a.cache_fp8) { if (d128) QW_GEN(uint16_t, uint8_t, 128); else QW_GEN(uint16_t, uint8_t, 64); }
+    else { if (d128) QW_GEN(uint16_t, uint16_t, 128); else QW_GEN(uint16_t, uint16_t, 64); }
   } else {
-    if (a.head_dim == 128) hipLaunchKernelGGL((attn_generic_kernel<float, 128>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((attn_generic_kernel<float, 64>), grid, dim3(64), 0, stream, a);
+    if (a.cache_fp8) { if (d128) QW_GEN(float, uint8_t, 128); else QW_GEN(float, uint8_t, 64); }
+    else { if (d128) QW_GEN(float, float, 128); else QW_GEN(float, float, 64); }
   }
+#undef QW_GEN
   return hipGetLastError();
 }
 

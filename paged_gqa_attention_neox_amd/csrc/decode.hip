@@ -1,5 +1,9 @@
 // Paged single-token GQA decode for bf16, head_dim 128, block 16, with the
 // context split into partitions ("split-K") and an exact log-sum-exp merge.
+// The cache may hold bf16 or FP8 E4M3FN codes ("Qwen2大模型架构解析与vLLM优化
+// 实践", §4.1-4.2 FP8 KV-cache quantization with cache scales, §6.3 E4M3FN):
+// FP8 tiles are half the bytes and are widened to bf16 pairs in registers
+// (exact), k_scale folds into the score scale and v_scale into the output.
 //
 // Attention of one new token over its sequence's paged KV ("vLLM 部署 Qwen",
 // §2.1 PagedAttention; §4.1: access to KV pages is what decode tuning is
@@ -58,17 +62,32 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ uint4 ld_buf16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+__device__ __forceinline__ uint2 ld_buf8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// two E4M3FN codes (bytes 2 HI, 2 HI + 1 of w) -> a bf16 pair, exactly
+// (every E4M3FN value is a bf16 value)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 c) {
+  return make_uint4(fp8x2_to_bf16x2<false>(c.x), fp8x2_to_bf16x2<true>(c.x),
+                    fp8x2_to_bf16x2<false>(c.y), fp8x2_to_bf16x2<true>(c.y));
+}
 
 struct DecodeKArgs {
   const uint16_t* q; int64_t q_stride;
-  const uint16_t* k_cache; const uint16_t* v_cache; int num_blocks;
+  const uint8_t* k_cache; const uint8_t* v_cache; int num_blocks;   // bf16 or E4M3FN tiles
   const int32_t* block_tables; int max_blocks;
   const int32_t* context_lens;
   uint16_t* out; int64_t out_stride;
   float* ws_acc;   // [S][H][max_parts][128]
   float* ws_ml;    // [S][H][max_parts][2]  (max in log2 domain, sum)
   int num_heads, num_kv_heads, max_parts, max_context_len;
-  float scale_log2;
+  float scale_log2;   // scale * log2 e (* k_scale with an FP8 cache)
+  float out_scale;    // 1, or v_scale with an FP8 cache
 };
 
 // Context length of sequence s clamped to what the grid and workspace were
@@ -83,9 +102,13 @@ __device__ __forceinline__ int checked_ctx(const DecodeKArgs& a, int s, bool* ba
 #define QW_DECODE_WAVES 4
 #endif
 
-template <int G>
+// F8: the caches hold E4M3FN codes (K tile 2 KiB, V tile 2 KiB); they are
+// widened to bf16 pairs in registers and the same arithmetic follows.
+template <int G, bool F8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QW_DECODE_WAVES)))
 void decode_partial_kernel(DecodeKArgs a) {
+  constexpr int kEl = F8 ? 1 : 2;                 // bytes per cache element
+  constexpr int kTileBytes = kBlk * kD * kEl;
   const int r = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   bool ctx_bad;
   const int ctx = checked_ctx(a, s, &ctx_bad);
@@ -128,6 +151,7 @@ void decode_partial_kernel(DecodeKArgs a) {
   // Lane roles.  Each 128-bit load instruction of a wave reads 1 KiB of one
   // tile contiguously.
   //   phase 1: key kr of an 8-key round; dims 8u..8u+7 and 64+8u..64+8u+7
+  //            (FP8: dims 16u..16u+15, one 16-byte load)
   //   phase 3: dims d0 + 32 i (i < 4); keys 8 kh .. 8 kh + 7 of the block
   const int kr = lane >> 3;
   const int u = lane & 7;
@@ -138,27 +162,40 @@ void decode_partial_kernel(DecodeKArgs a) {
   // of loads in flight is static and each wait covers exactly one block; a
   // prefetch past the wave's last block gets a zero-size descriptor, which
   // returns zeros without touching memory.
-  auto rsrc = [&](const uint16_t* base, int i) {
+  auto rsrc = [&](const uint8_t* base, int i) {
     const bool live = i < nbw;
     const int b = uniform(sblk[wave + kNW * (live ? i : 0)]);
-    const uint16_t* t = base + (static_cast<int64_t>(b) * Hkv + g) * (kBlk * kD);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t), static_cast<short>(0),
-                                             live ? kBlk * kD * 2 : 0, kBufferFlags);
+    const uint8_t* t = base + (static_cast<int64_t>(b) * Hkv + g) * kTileBytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(t), static_cast<short>(0),
+                                             live ? kTileBytes : 0, kBufferFlags);
   };
-  const int koff = (kr * kD + u * 8) * 2;           // byte offsets within a tile
-  const int voff = lane * 16;
+  // byte offsets within a tile (bf16 K: key kr, dims 8u.. and 64+8u..; FP8 K:
+  // key kr, dims 16u..16u+15; V: dims d0 + 32 i, keys 8 kh..8 kh+7)
+  const int koff = F8 ? kr * kD + u * 16 : (kr * kD + u * 8) * 2;
+  const int voff = F8 ? d0 * kBlk + kh * 8 : lane * 16;
   auto load_k = [&](int i, uint4 (&buf)[4]) {
     const auto r = rsrc(a.k_cache, i);
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
-      buf[2 * rd] = ld_buf16(r, koff + rd * 8 * kD * 2);
-      buf[2 * rd + 1] = ld_buf16(r, koff + rd * 8 * kD * 2 + 128);
+      if constexpr (F8) {
+        buf[rd] = ld_buf16(r, koff + rd * 8 * kD);
+      } else {
+        buf[2 * rd] = ld_buf16(r, koff + rd * 8 * kD * 2);
+        buf[2 * rd + 1] = ld_buf16(r, koff + rd * 8 * kD * 2 + 128);
+      }
     }
   };
   auto load_v = [&](int i, uint4 (&buf)[4]) {
     const auto r = rsrc(a.v_cache, i);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) buf[d] = ld_buf16(r, voff + d * 1024);
+    for (int d = 0; d < 4; ++d) {
+      if constexpr (F8) {
+        const uint2 c = ld_buf8(r, voff + d * 32 * kBlk);
+        buf[d] = make_uint4(c.x, c.y, 0u, 0u);
+      } else {
+        buf[d] = ld_buf16(r, voff + d * 1024);
+      }
+    }
   };
 
   // ---------------- phase 1: raw scores q.k ----------------
@@ -166,18 +203,25 @@ void decode_partial_kernel(DecodeKArgs a) {
   {
     uint4 qa[G], qb[G];
     const uint16_t* qp = a.q + static_cast<int64_t>(s) * a.q_stride +
-                         static_cast<int64_t>(g * G) * kD + u * 8;
+                         static_cast<int64_t>(g * G) * kD + (F8 ? u * 16 : u * 8);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       qa[h] = *reinterpret_cast<const uint4*>(qp + h * kD);
-      qb[h] = *reinterpret_cast<const uint4*>(qp + h * kD + 64);
+      qb[h] = *reinterpret_cast<const uint4*>(qp + h * kD + (F8 ? 8 : 64));
     }
     auto scores = [&](int i, const uint4 (&kbuf)[4]) {
       const int b = wave + kNW * i;
       const bool full = (b + 1) * kBlk <= ntok;
 #pragma unroll
       for (int rd = 0; rd < 2; ++rd) {
-        const uint4 k0 = kbuf[2 * rd], k1 = kbuf[2 * rd + 1];
+        uint4 k0, k1;
+        if constexpr (F8) {
+          k0 = fp8x8_to_bf16x8(make_uint2(kbuf[rd].x, kbuf[rd].y));
+          k1 = fp8x8_to_bf16x8(make_uint2(kbuf[rd].z, kbuf[rd].w));
+        } else {
+          k0 = kbuf[2 * rd];
+          k1 = kbuf[2 * rd + 1];
+        }
         float acc[8];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -279,6 +323,10 @@ void decode_partial_kernel(DecodeKArgs a) {
       for (int i = 0; i < 4; ++i) acc[h][i] = 0.0f;
     auto pv = [&](int i, uint4 (&vr)[4]) {
       const int b = wave + kNW * i;
+      if constexpr (F8) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) vr[d] = fp8x8_to_bf16x8(make_uint2(vr[d].x, vr[d].y));
+      }
       const int pair0 = (b * kBlk + kh * 8) / 2;     // first token pair of this lane half
       if ((b + 1) * kBlk > ntok) {                   // last block: tail slots may hold NaN
 #pragma unroll
@@ -336,7 +384,7 @@ void decode_partial_kernel(DecodeKArgs a) {
     const int qh = g * G + h;
     if (nparts == 1) {
       a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
-          f32_to_bf16(v / sL[h]);
+          f32_to_bf16(v * a.out_scale / sL[h]);
     } else {
       a.ws_acc[((static_cast<int64_t>(s) * a.num_heads + qh) * a.max_parts + r) * kD + e] = v;
     }
@@ -403,11 +451,12 @@ __global__ __launch_bounds__(128) void decode_reduce_kernel(DecodeKArgs a) {
     __syncthreads();                             // sm/sl reused by the next batch
   }
   a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
-      f32_to_bf16(ctx_bad ? __builtin_nanf("") : o / L);
+      f32_to_bf16(ctx_bad ? __builtin_nanf("") : o * a.out_scale / L);
 }
 
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
-                       int head_dim, int block_size, int dtype) {
+                       int head_dim, int block_size, int dtype, int cache_fp8) {
+  (void)cache_fp8;                    // both cache formats have the split-K kernel
   DecodePlan p{};
   const int G = num_heads / num_kv_heads;
   p.fast = dtype == kBF16 && head_dim == kD && block_size == kBlk && G >= 1 && G <= kMaxG;
@@ -430,7 +479,10 @@ template <int G>
 static void launch_partial(const DecodeKArgs& k, const AttnArgs& a, const DecodePlan& p,
                            hipStream_t stream) {
   const dim3 grid(p.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL(decode_partial_kernel<G>, grid, dim3(kThreads), 0, stream, k);
+  if (a.cache_fp8)
+    hipLaunchKernelGGL((decode_partial_kernel<G, true>), grid, dim3(kThreads), 0, stream, k);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<G, false>), grid, dim3(kThreads), 0, stream, k);
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t stream) {
@@ -438,8 +490,8 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
   DecodeKArgs k{};
   k.q = static_cast<const uint16_t*>(a.q);
   k.q_stride = a.q_stride;
-  k.k_cache = static_cast<const uint16_t*>(a.k_cache);
-  k.v_cache = static_cast<const uint16_t*>(a.v_cache);
+  k.k_cache = static_cast<const uint8_t*>(a.k_cache);
+  k.v_cache = static_cast<const uint8_t*>(a.v_cache);
   k.num_blocks = a.num_blocks;
   k.block_tables = a.block_tables;
   k.max_blocks = a.max_blocks;
@@ -450,7 +502,8 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
   k.num_kv_heads = a.num_kv_heads;
   k.max_parts = p.max_parts;
   k.max_context_len = a.max_context_len;
-  k.scale_log2 = a.scale * kLog2e;
+  k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
+  k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
   if (p.max_parts > 1) {
     const size_t rows = static_cast<size_t>(a.num_seqs) * a.num_heads * p.max_parts;
     k.ws_acc = static_cast<float*>(a.workspace);

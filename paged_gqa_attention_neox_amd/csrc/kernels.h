@@ -21,6 +21,8 @@ struct RopeWriteArgs {
   void* k_cache; void* v_cache; int num_blocks;
   int num_tokens, num_heads, num_kv_heads, head_dim, block_size;
   int dtype;
+  int cache_fp8;                 // caches hold E4M3FN codes of value / scale
+  float k_scale, v_scale;
 };
 
 struct AttnArgs {
@@ -35,6 +37,8 @@ struct AttnArgs {
   float scale;
   int dtype;
   void* workspace; size_t workspace_bytes;
+  int cache_fp8;                 // caches hold E4M3FN codes; value = code * scale
+  float k_scale, v_scale;
 };
 
 // decode plan: which kernel runs and how much workspace it needs
@@ -46,7 +50,7 @@ struct DecodePlan {
 };
 
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
-                       int head_dim, int block_size, int dtype);
+                       int head_dim, int block_size, int dtype, int cache_fp8);
 
 hipError_t launch_rope_table(double* tab, int max_position, int rotary_dim, double theta,
                              hipStream_t stream);

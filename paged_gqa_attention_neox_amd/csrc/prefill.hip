@@ -43,7 +43,7 @@
 //   * key tiles past the causal limit of the query tile are skipped; the
 //     grid is issued longest tile level first, XCD- and shader-engine-aware
 //     (see the work-item mapping at the top of the kernel).
-// Other shapes and fp32 use the generic kernel.
+// Other shapes, fp32 and FP8 caches use the generic kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -526,8 +526,8 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   const int KG = key_groups(a);
   const int ids = 2 * KG * ((a.max_context_len + KG * kBK - 1) / (KG * kBK));
-  const bool mfma = a.dtype == kBF16 && a.head_dim == kD && a.block_size == kB && G >= 1 &&
-                    G <= 8 && ids <= kMaxIds;
+  const bool mfma = a.dtype == kBF16 && !a.cache_fp8 && a.head_dim == kD && a.block_size == kB &&
+                    G >= 1 && G <= 8 && ids <= kMaxIds;
   if (!mfma) return launch_attn_generic(a, stream);
   PrefillKArgs k{};
   k.q = static_cast<const uint16_t*>(a.q);

@@ -95,14 +95,22 @@ int qwen2_rope_table_init(double* cos_sin, int max_position, int rotary_dim, dou
   return launched(qw::launch_rope_table(cos_sin, max_position, rotary_dim, rope_theta, stream));
 }
 
-int qwen2_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int64_t q_out_row_stride,
+static int check_fp8_scales(float k_scale, float v_scale) {
+  if (!(k_scale > 0.0f) || !(k_scale < 1e30f) || !(v_scale > 0.0f) || !(v_scale < 1e30f))
+    return fail(QW_ERR_SHAPE, "k_scale and v_scale must be finite and > 0");
+  return QW_OK;
+}
+
+static int rope_write_impl(const void* q, int64_t q_row_stride, void* q_out, int64_t q_out_row_stride,
                            const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
                            const int32_t* positions, const int32_t* slot_mapping,
                            const double* cos_sin, int max_position, void* k_cache, void* v_cache,
                            int num_blocks, int num_tokens, int num_heads, int num_kv_heads,
-                           int head_dim, int block_size, int dtype, hipStream_t stream) {
+                           int head_dim, int block_size, int dtype, int cache_fp8, float k_scale,
+                           float v_scale, hipStream_t stream) {
   int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st) return st;
+  if (cache_fp8 && (st = check_fp8_scales(k_scale, v_scale))) return st;
   if (num_tokens < 0) return fail(QW_ERR_SHAPE, "num_tokens=%d < 0", num_tokens);
   if (num_blocks < 0) return fail(QW_ERR_SHAPE, "num_blocks=%d < 0", num_blocks);
   if (max_position < 1) return fail(QW_ERR_SHAPE, "max_position=%d < 1", max_position);
@@ -139,7 +147,33 @@ int qwen2_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int
   a.k_cache = k_cache; a.v_cache = v_cache; a.num_blocks = num_blocks;
   a.num_tokens = num_tokens; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim; a.block_size = block_size; a.dtype = dtype;
+  a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
   return launched(qw::launch_rope_cache_write(a, stream));
+}
+
+int qwen2_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int64_t q_out_row_stride,
+                           const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                           const int32_t* positions, const int32_t* slot_mapping,
+                           const double* cos_sin, int max_position, void* k_cache, void* v_cache,
+                           int num_blocks, int num_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int dtype, hipStream_t stream) {
+  return rope_write_impl(q, q_row_stride, q_out, q_out_row_stride, k, k_row_stride, v, v_row_stride,
+                         positions, slot_mapping, cos_sin, max_position, k_cache, v_cache,
+                         num_blocks, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                         dtype, 0, 1.0f, 1.0f, stream);
+}
+
+int qwen2_rope_cache_write_fp8(const void* q, int64_t q_row_stride, void* q_out,
+                               int64_t q_out_row_stride, const void* k, int64_t k_row_stride,
+                               const void* v, int64_t v_row_stride, const int32_t* positions,
+                               const int32_t* slot_mapping, const double* cos_sin, int max_position,
+                               void* k_cache, void* v_cache, int num_blocks, int num_tokens,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int dtype, float k_scale, float v_scale, hipStream_t stream) {
+  return rope_write_impl(q, q_row_stride, q_out, q_out_row_stride, k, k_row_stride, v, v_row_stride,
+                         positions, slot_mapping, cos_sin, max_position, k_cache, v_cache,
+                         num_blocks, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                         dtype, 1, k_scale, v_scale, stream);
 }
 
 static int check_attn_common(const void* q, int64_t q_row_stride, const void* k_cache,
@@ -169,13 +203,17 @@ static int check_attn_common(const void* q, int64_t q_row_stride, const void* k_
   return QW_OK;
 }
 
-int qwen2_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k_cache,
-                              const void* v_cache, int num_blocks, const int32_t* cu_seqlens_q,
-                              const int32_t* context_lens, const int32_t* block_tables,
-                              int max_blocks_per_seq, void* out, int64_t out_row_stride,
-                              int num_seqs, int num_tokens, int max_query_len, int max_context_len,
-                              int num_heads, int num_kv_heads, int head_dim, int block_size,
-                              float scale, int dtype, hipStream_t stream) {
+static int prefill_impl(const void* q, int64_t q_row_stride, const void* k_cache,
+                        const void* v_cache, int num_blocks, const int32_t* cu_seqlens_q,
+                        const int32_t* context_lens, const int32_t* block_tables,
+                        int max_blocks_per_seq, void* out, int64_t out_row_stride, int num_seqs,
+                        int num_tokens, int max_query_len, int max_context_len, int num_heads,
+                        int num_kv_heads, int head_dim, int block_size, float scale, int dtype,
+                        int cache_fp8, float k_scale, float v_scale, hipStream_t stream) {
+  if (cache_fp8) {
+    const int st = check_fp8_scales(k_scale, v_scale);
+    if (st) return st;
+  }
   if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0)
     return fail(QW_ERR_SHAPE, "negative size (num_seqs=%d num_tokens=%d max_query_len=%d)",
                 num_seqs, num_tokens, max_query_len);
@@ -202,7 +240,35 @@ int qwen2_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k
   a.max_query_len = max_query_len; a.max_context_len = max_context_len;
   a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
   a.block_size = block_size; a.scale = scale; a.dtype = dtype;
+  a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
   return launched(qw::launch_prefill(a, stream));
+}
+
+int qwen2_attn_prefill_varlen(const void* q, int64_t q_row_stride, const void* k_cache,
+                              const void* v_cache, int num_blocks, const int32_t* cu_seqlens_q,
+                              const int32_t* context_lens, const int32_t* block_tables,
+                              int max_blocks_per_seq, void* out, int64_t out_row_stride,
+                              int num_seqs, int num_tokens, int max_query_len, int max_context_len,
+                              int num_heads, int num_kv_heads, int head_dim, int block_size,
+                              float scale, int dtype, hipStream_t stream) {
+  return prefill_impl(q, q_row_stride, k_cache, v_cache, num_blocks, cu_seqlens_q, context_lens,
+                      block_tables, max_blocks_per_seq, out, out_row_stride, num_seqs, num_tokens,
+                      max_query_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                      block_size, scale, dtype, 0, 1.0f, 1.0f, stream);
+}
+
+int qwen2_attn_prefill_varlen_fp8(const void* q, int64_t q_row_stride, const void* k_cache,
+                                  const void* v_cache, int num_blocks, const int32_t* cu_seqlens_q,
+                                  const int32_t* context_lens, const int32_t* block_tables,
+                                  int max_blocks_per_seq, void* out, int64_t out_row_stride,
+                                  int num_seqs, int num_tokens, int max_query_len,
+                                  int max_context_len, int num_heads, int num_kv_heads,
+                                  int head_dim, int block_size, float scale, int dtype,
+                                  float k_scale, float v_scale, hipStream_t stream) {
+  return prefill_impl(q, q_row_stride, k_cache, v_cache, num_blocks, cu_seqlens_q, context_lens,
+                      block_tables, max_blocks_per_seq, out, out_row_stride, num_seqs, num_tokens,
+                      max_query_len, max_context_len, num_heads, num_kv_heads, head_dim,
+                      block_size, scale, dtype, 1, k_scale, v_scale, stream);
 }
 
 size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int num_heads,
@@ -210,16 +276,20 @@ size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int n
   if (num_seqs < 0 || max_context_len < 1) return static_cast<size_t>(-1);
   if (check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype)) return static_cast<size_t>(-1);
   return qw::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
-                         dtype).ws_bytes;
+                         dtype, 0).ws_bytes;
 }
 
-int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride, const void* k_cache,
-                            const void* v_cache, int num_blocks, const int32_t* block_tables,
-                            int max_blocks_per_seq, const int32_t* context_lens, void* out,
-                            int64_t out_row_stride, void* workspace, size_t workspace_bytes,
-                            int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
-                            int head_dim, int block_size, float scale, int dtype,
-                            hipStream_t stream) {
+static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
+                       const void* v_cache, int num_blocks, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                       int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                       int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
+                       int head_dim, int block_size, float scale, int dtype, int cache_fp8,
+                       float k_scale, float v_scale, hipStream_t stream) {
+  if (cache_fp8) {
+    const int st = check_fp8_scales(k_scale, v_scale);
+    if (st) return st;
+  }
   if (num_seqs < 0) return fail(QW_ERR_SHAPE, "num_seqs=%d < 0", num_seqs);
   if (num_seqs > 65535) return fail(QW_ERR_UNSUPPORTED, "num_seqs=%d > 65535", num_seqs);
   if (num_seqs == 0) {
@@ -232,7 +302,7 @@ int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride, const void* k_c
                              scale, dtype);
   if (st) return st;
   const qw::DecodePlan plan = qw::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads,
-                                              head_dim, block_size, dtype);
+                                              head_dim, block_size, dtype, cache_fp8);
   if (plan.ws_bytes > 0) {
     if (!workspace) return fail(QW_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.ws_bytes);
     if (workspace_bytes < plan.ws_bytes)
@@ -250,7 +320,34 @@ int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride, const void* k_c
   a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
   a.block_size = block_size; a.scale = scale; a.dtype = dtype;
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
   return launched(qw::launch_decode(a, plan, stream));
+}
+
+int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride, const void* k_cache,
+                            const void* v_cache, int num_blocks, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                            int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                            int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
+                            int head_dim, int block_size, float scale, int dtype,
+                            hipStream_t stream) {
+  return decode_impl(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, out, out_row_stride, workspace,
+                     workspace_bytes, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
+                     block_size, scale, dtype, 0, 1.0f, 1.0f, stream);
+}
+
+int qwen2_attn_decode_paged_fp8(const void* q, int64_t q_row_stride, const void* k_cache,
+                                const void* v_cache, int num_blocks, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                                int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                                int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
+                                int head_dim, int block_size, float scale, int dtype,
+                                float k_scale, float v_scale, hipStream_t stream) {
+  return decode_impl(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, out, out_row_stride, workspace,
+                     workspace_bytes, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
+                     block_size, scale, dtype, 1, k_scale, v_scale, stream);
 }
 
 int qwen2_check_metadata_host(const int32_t* positions, const int32_t* slot_mapping, int num_tokens,

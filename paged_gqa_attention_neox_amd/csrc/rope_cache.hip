@@ -12,7 +12,10 @@
 // here rotation and cache scatter are one pass over the fused QKV rows.
 //
 // The kernel is HBM-bound: per token it reads (H + 2 Hkv) * d elements and
-// writes H * d (q_out) + 2 Hkv * d (cache) elements.  Each work item moves
+// writes H * d (q_out) + 2 Hkv * d (cache) elements.  With an FP8 cache
+// ("Qwen2大模型架构解析与vLLM优化实践", §4.1-4.2 FP8 KV-cache quantization with
+// cache scales; §6.3 the E4M3FN format) the cache entries are E4M3FN codes of
+// the exact rotated k (or v) divided by the tensor's scale, rounded once.  Each work item moves
 // 16-byte vectors: 8 rotation pairs (x[i..i+8], x[i+d/2..]) of one head, or
 // 8 elements of one v head.
 #include "common.h"
@@ -58,6 +61,26 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double y) {
   uint32_t u = __float_as_uint(t);
   if (static_cast<double>(t) != y) u |= 1u;
   return f32_to_bf16(__uint_as_float(u));
+}
+
+// float64 -> E4M3FN code with ONE rounding (nearest even), saturated at
+// +-448: round to odd into fp32 (21 spare bits), clamp, then gfx950's
+// v_cvt_pk_fp8_f32 (round to nearest even; it would turn magnitudes past the
+// last rounding boundary into NaN, hence the clamp).
+__device__ __forceinline__ float f64_to_f32_odd(double y) {
+  const float t = __double2float_rz(y);
+  uint32_t u = __float_as_uint(t);
+  if (static_cast<double>(t) != y) u |= 1u;
+  return fminf(fmaxf(__uint_as_float(u), -448.0f), 448.0f);
+}
+// eight codes from eight float64 values, as two little-endian words
+__device__ __forceinline__ uint2 f64x8_to_fp8(const double (&y)[8]) {
+  uint2 r;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(f64_to_f32_odd(y[0]), f64_to_f32_odd(y[1]), 0, false);
+  r.x = __builtin_amdgcn_cvt_pk_fp8_f32(f64_to_f32_odd(y[2]), f64_to_f32_odd(y[3]), w, true);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(f64_to_f32_odd(y[4]), f64_to_f32_odd(y[5]), 0, false);
+  r.y = __builtin_amdgcn_cvt_pk_fp8_f32(f64_to_f32_odd(y[6]), f64_to_f32_odd(y[7]), w, true);
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -138,7 +161,8 @@ template <> struct Vec8<float> {
 // ---------------------------------------------------------------------------
 // fused rotate + scatter
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+// CF8: the caches hold E4M3FN codes of (rotated) k / k_scale and v / v_scale.
+template <typename T, int D, bool CF8>
 __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) {
   constexpr int HALF = D / 2;
   constexpr int RCH = HALF / 8;   // rotation items per head (8 pairs each)
@@ -155,6 +179,9 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
   T* q_out = static_cast<T*>(a.q_out);
   T* __restrict__ kc = static_cast<T*>(a.k_cache);
   T* __restrict__ vc = static_cast<T*>(a.v_cache);
+  uint8_t* __restrict__ kc8 = static_cast<uint8_t*>(a.k_cache);
+  uint8_t* __restrict__ vc8 = static_cast<uint8_t*>(a.v_cache);
+  const double ks = a.k_scale, vs = a.v_scale;
 
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -187,7 +214,7 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
         }
       } else {
         const int gk = head - H;
-        dst = kc + ((blk * Hkv + gk) * B + off) * D;
+        dst = CF8 ? nullptr : kc + ((blk * Hkv + gk) * B + off) * D;
       }
       const T* src = is_q ? q + static_cast<int64_t>(t) * a.q_stride + static_cast<int64_t>(head) * D
                           : k + static_cast<int64_t>(t) * a.k_stride + static_cast<int64_t>(head - H) * D;
@@ -212,6 +239,20 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
         y1[j] = fma(x1[j], cv[j], -(x2[j] * sv[j]));
         y2[j] = fma(x2[j], cv[j], x1[j] * sv[j]);
       }
+      if (CF8 && !is_q) {
+        // the code of the rotation divided by the scale: a correctly rounded
+        // float64 quotient, then one rounding to the code
+        double z1[8], z2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          z1[j] = y1[j] / ks;
+          z2[j] = y2[j] / ks;
+        }
+        uint8_t* d8 = kc8 + ((blk * Hkv + (head - H)) * B + off) * D;
+        *reinterpret_cast<uint2*>(d8 + i0) = f64x8_to_fp8(z1);
+        *reinterpret_cast<uint2*>(d8 + HALF + i0) = f64x8_to_fp8(z2);
+        continue;
+      }
       Vec8<T> o1, o2;
       o1.from_f64(y1);
       o2.from_f64(y2);
@@ -224,6 +265,17 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       const int e0 = (w - gv * VCH) * 8;
       Vec8<T> x;
       x.load(v + static_cast<int64_t>(t) * a.v_stride + static_cast<int64_t>(gv) * D + e0);
+      if (CF8) {
+        double xv[8];
+        x.to_f64(xv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] /= vs;
+        const uint2 c8 = f64x8_to_fp8(xv);
+        uint8_t* d8 = vc8 + ((blk * Hkv + gv) * D + e0) * B + off;   // V tile is [d][B]
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d8[j * B] = static_cast<uint8_t>(((j < 4 ? c8.x : c8.y) >> (8 * (j & 3))) & 0xff);
+        continue;
+      }
       T* dst = vc + ((blk * Hkv + gv) * D + e0) * B + off;     // V tile is [d][B]
 #pragma unroll
       for (int j = 0; j < 8; ++j) dst[j * B] = x.elem(j);
@@ -239,13 +291,20 @@ hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream) {
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 1 << 20) blocks = 1 << 20;
   const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
-  if (a.dtype == kBF16) {
-    if (d == 128) hipLaunchKernelGGL((rope_cache_write_kernel<uint16_t, 128>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((rope_cache_write_kernel<uint16_t, 64>), grid, block, 0, stream, a);
+#define QW_ROPE_LAUNCH(T, D, F8) \
+  hipLaunchKernelGGL((rope_cache_write_kernel<T, D, F8>), grid, block, 0, stream, a)
+  if (a.cache_fp8) {
+    if (a.dtype == kBF16) {
+      if (d == 128) QW_ROPE_LAUNCH(uint16_t, 128, true); else QW_ROPE_LAUNCH(uint16_t, 64, true);
+    } else {
+      if (d == 128) QW_ROPE_LAUNCH(float, 128, true); else QW_ROPE_LAUNCH(float, 64, true);
+    }
+  } else if (a.dtype == kBF16) {
+    if (d == 128) QW_ROPE_LAUNCH(uint16_t, 128, false); else QW_ROPE_LAUNCH(uint16_t, 64, false);
   } else {
-    if (d == 128) hipLaunchKernelGGL((rope_cache_write_kernel<float, 128>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((rope_cache_write_kernel<float, 64>), grid, block, 0, stream, a);
+    if (d == 128) QW_ROPE_LAUNCH(float, 128, false); else QW_ROPE_LAUNCH(float, 64, false);
   }
+#undef QW_ROPE_LAUNCH
   return hipGetLastError();
 }
 

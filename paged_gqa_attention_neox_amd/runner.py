@@ -17,9 +17,11 @@ _TABLES = {}
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    """Storage array (uint16 bf16 bits or float32) -> device tensor."""
+    """Storage array (uint16 bf16 bits, float32, or uint8 FP8 codes) -> device tensor."""
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
@@ -60,8 +62,10 @@ class DeviceStep:
         self.out = torch.full((T, H, d), float("nan"), dtype=self.tdtype, device=device)
         self.positions = i32(batch.positions)
         self.slots = i32(batch.slot_mapping)
-        self.k_cache = k_cache if k_cache is not None else to_device(batch.k_cache, sh.dtype, device)
-        self.v_cache = v_cache if v_cache is not None else to_device(batch.v_cache, sh.dtype, device)
+        cdt = sh.cache_storage
+        self.fp8 = cdt == "fp8"
+        self.k_cache = k_cache if k_cache is not None else to_device(batch.k_cache, cdt, device)
+        self.v_cache = v_cache if v_cache is not None else to_device(batch.v_cache, cdt, device)
         self.cos_sin = rope_table(d, sh.rope_theta, sh.max_position, device)
         P = batch.num_prefill
         self.Tp = batch.num_prefill_tokens
@@ -81,27 +85,37 @@ class DeviceStep:
     # --- the three calls ---
     def rope_write(self, stream=None):
         sh = self.sh
-        B.qwen2_rope_cache_write(self.q, self.q_out, self.k, self.v, self.positions, self.slots,
-                                 self.cos_sin, self.k_cache, self.v_cache, sh.num_heads,
-                                 sh.num_kv_heads, sh.head_dim, sh.block_size, stream)
+        args = (self.q, self.q_out, self.k, self.v, self.positions, self.slots, self.cos_sin,
+                self.k_cache, self.v_cache, sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                sh.block_size)
+        if self.fp8:
+            B.qwen2_rope_cache_write_fp8(*args, sh.k_scale, sh.v_scale, stream)
+        else:
+            B.qwen2_rope_cache_write(*args, stream)
 
     def prefill(self, stream=None):
         if not self.batch.num_prefill:
             return
         sh = self.sh
-        B.qwen2_attn_prefill_varlen(self.q_out[: self.Tp], self.k_cache, self.v_cache, self.p_cu,
-                                    self.p_ctx, self.p_bt, self.out[: self.Tp], self.p_max_q,
-                                    self.p_max_c, sh.num_heads, sh.num_kv_heads, sh.head_dim,
-                                    sh.block_size, sh.scale, stream)
+        args = (self.q_out[: self.Tp], self.k_cache, self.v_cache, self.p_cu, self.p_ctx,
+                self.p_bt, self.out[: self.Tp], self.p_max_q, self.p_max_c, sh.num_heads,
+                sh.num_kv_heads, sh.head_dim, sh.block_size, sh.scale)
+        if self.fp8:
+            B.qwen2_attn_prefill_varlen_fp8(*args, sh.k_scale, sh.v_scale, stream)
+        else:
+            B.qwen2_attn_prefill_varlen(*args, stream)
 
     def decode(self, stream=None):
         if not self.batch.num_decode:
             return
         sh = self.sh
-        B.qwen2_attn_decode_paged(self.q_out[self.Tp:], self.k_cache, self.v_cache, self.d_bt,
-                                  self.d_ctx, self.out[self.Tp:], self.workspace, self.d_max_c,
-                                  sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
-                                  sh.scale, stream)
+        args = (self.q_out[self.Tp:], self.k_cache, self.v_cache, self.d_bt, self.d_ctx,
+                self.out[self.Tp:], self.workspace, self.d_max_c, sh.num_heads, sh.num_kv_heads,
+                sh.head_dim, sh.block_size, sh.scale)
+        if self.fp8:
+            B.qwen2_attn_decode_paged_fp8(*args, sh.k_scale, sh.v_scale, stream)
+        else:
+            B.qwen2_attn_decode_paged(*args, stream)
 
     def step(self, stream=None):
         self.rope_write(stream)

@@ -38,9 +38,10 @@ def run_oracle(batch, seqs=None):
     """Oracle step.  ``seqs`` restricts the attention to those sequence ids
     (the cache write always covers every token)."""
     sh = batch.shape
+    fp8 = dict(cache_dtype=sh.cache_dtype, k_scale=sh.k_scale, v_scale=sh.v_scale)
     q_out, kc, vc = R.rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
                                        batch.k_cache, batch.v_cache, sh.num_heads, sh.num_kv_heads,
-                                       sh.head_dim, sh.block_size, sh.rope_theta)
+                                       sh.head_dim, sh.block_size, sh.rope_theta, **fp8)
     cu = batch.cu_seqlens_q
     out = np.full((batch.num_tokens, sh.num_heads, sh.head_dim), np.nan)
     ids = range(batch.num_seqs) if seqs is None else seqs
@@ -48,7 +49,8 @@ def run_oracle(batch, seqs=None):
         r0, r1 = int(cu[s]), int(cu[s + 1])
         o = R.attention_varlen(q_out[r0:r1], kc, vc, np.array([0, r1 - r0]),
                                batch.context_lens[s:s + 1], batch.block_tables[s:s + 1],
-                               sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, sh.dtype)
+                               sh.num_heads, sh.num_kv_heads, sh.head_dim, sh.block_size, sh.dtype,
+                               **fp8)
         out[r0:r1] = o
     return {"q_out": q_out, "k_cache": kc, "v_cache": vc, "out": out}
 
@@ -110,8 +112,25 @@ def written_mask(batch):
 
 def check_caches(batch, res, ora):
     """V cache bitwise equal everywhere; K cache bitwise equal at every slot
-    the step does not write and within rounding at the written ones."""
+    the step does not write and within rounding at the written ones.  FP8
+    caches: every code equal, except that at most one written K code in a
+    million may be its neighbour (the float64 rotation can differ in the last
+    place between device and host, which moves a value across a rounding
+    boundary with a probability of order 1e-13)."""
     dt = batch.shape.dtype
+    if batch.shape.cache_dtype == "fp8":
+        assert np.array_equal(res["v_cache"], ora["v_cache"]), "V codes differ"
+        wm = written_mask(batch)
+        kg, ko = res["k_cache"], ora["k_cache"]
+        diff = np.nonzero(kg != ko)
+        assert wm[diff[0], diff[2]].all(), "K codes changed at slots the step does not write"
+        n_bad = len(diff[0])
+        assert n_bad <= kg.size // 1_000_000, f"K codes: {n_bad} differ"
+        if n_bad:
+            a = kg[diff].astype(np.int64)
+            b = ko[diff].astype(np.int64)
+            assert np.all((np.abs(a - b) == 1) & ((a ^ b) < 128)), "K codes differ by more than a step"
+        return
     assert np.array_equal(bits(res["v_cache"]), bits(ora["v_cache"])), "V cache differs"
     wm = written_mask(batch)
     kc_g, kc_o = res["k_cache"], ora["k_cache"]

@@ -1,0 +1,96 @@
+"""GPU parity with an FP8 (E4M3FN) KV cache, through the *_fp8 C entry points,
+against the float64 oracle reading the same codes.
+
+The cache codes are compared exactly (one rounding of the same float64 value
+on both sides); the attention outputs to the bf16 tolerance (the arithmetic
+differs only in accumulation order and the bf16 probabilities).  Scales are
+not powers of two, so a missing or swapped scale shows up.
+"""
+import numpy as np
+import pytest
+
+from paged_gqa_attention_neox_amd import runner
+from paged_gqa_attention_neox_amd import workloads as W
+from gpu_common import check_caches, check_out, check_rotated, require_gpu, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+KS, VS = W.FP8_K_SCALE, W.FP8_V_SCALE
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def fp8_check(b, label, seqs=None):
+    say(f"{label}: GPU step")
+    res, _ = run_gpu(b)
+    say(f"{label}: oracle")
+    ora = run_oracle(b, seqs=seqs)
+    check_rotated(res["q_out"], ora["q_out"], b.shape.dtype, "q_out")
+    check_caches(b, res, ora)
+    rows = None
+    if seqs is not None:
+        cu = b.cu_seqlens_q
+        rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    mx, mean = check_out(res["out"], ora["out"], b.shape.dtype, rows=rows)
+    say(f"{label}: out max abs {mx:.3e} mean abs {mean:.3e}")
+
+
+CASES = [
+    # (name, H, Hkv, contexts, query lens, num_prefill)
+    ("decode_partition_edges", 28, 4, [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 1600], [1] * 10, 0),
+    ("decode_g1", 4, 4, [300, 700, 3], [1] * 3, 0),
+    ("decode_g2", 16, 8, [129, 2048, 1], [1] * 3, 0),
+    ("decode_g4", 16, 4, [1000, 33], [1] * 2, 0),
+    ("decode_g8", 32, 4, [777, 1500], [1] * 2, 0),
+    ("prefill_chunks", 14, 2, [100, 700, 48], [37, 300, 48], 3),
+    ("mixed", 28, 4, [90, 300, 2000, 1, 513], [90, 44, 1, 1, 1], 2),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_small_cases(case):
+    name, H, Hkv, ctx, ql, npf = case
+    b = W.small_case(401 + CASES.index(case), "bf16", H, Hkv, 128, context_lens=ctx,
+                     query_lens=ql, num_prefill=npf, keep_logical=False, cache_dtype="fp8",
+                     k_scale=KS, v_scale=VS)
+    fp8_check(b, f"fp8_{name}")
+
+
+def test_fp8_prefix_sharing():
+    b = W.small_case(420, "bf16", 14, 2, 128, context_lens=[96, 200, 65, 300],
+                     query_lens=[32, 1, 1, 1], num_prefill=1,
+                     shares_prefix=[True, True, True, False], shared_prefix_len=64,
+                     keep_logical=False, cache_dtype="fp8", k_scale=KS, v_scale=VS)
+    fp8_check(b, "fp8_prefix_sharing")
+
+
+def test_fp8_long_decode_full_sampled():
+    """The Qwen2-7B long-context decode with an FP8 cache at full size; the
+    oracle attention on 6 sequences (shortest, longest, and 4 between)."""
+    b = W.qwen2_long_decode_fp8()
+    order = np.argsort(b.context_lens)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[16]), int(order[32]),
+                   int(order[48]), 7})
+    fp8_check(b, "fp8_long_decode", seqs=seqs)
+
+
+def test_fp8_halves_decode_bytes_and_tracks_bf16():
+    """Same draws with a bf16 cache and an FP8 cache: the FP8 outputs stay
+    within the quantisation error of the bf16 ones (a property, not parity:
+    E4M3FN keeps 3 mantissa bits)."""
+    bb = W.small_case(430, "bf16", 28, 4, 128, context_lens=[900, 2000, 33], query_lens=[1] * 3,
+                      num_prefill=0, keep_logical=False)
+    b8 = W.small_case(430, "bf16", 28, 4, 128, context_lens=[900, 2000, 33], query_lens=[1] * 3,
+                      num_prefill=0, keep_logical=False, cache_dtype="fp8", k_scale=KS,
+                      v_scale=VS)
+    assert b8.decode_kv_bytes() * 2 == bb.decode_kv_bytes()
+    rb, _ = run_gpu(bb)
+    r8, _ = run_gpu(b8)
+    ob = runner.to_host(runner.to_device(rb["out"], "bf16")).astype(np.uint32) << 16
+    o8 = runner.to_host(runner.to_device(r8["out"], "bf16")).astype(np.uint32) << 16
+    fb, f8 = ob.view(np.float32), o8.view(np.float32)
+    assert np.all(np.isfinite(f8))
+    assert np.abs(fb - f8).mean() < 0.05 * np.abs(fb).mean() + 1e-3
