@@ -31,6 +31,12 @@ with the function that uses it):
   * softmax is base e, max-subtracted, masked keys excluded;
   * rotated q and k, and the output, are rounded once from float64 to the
     storage dtype (round to nearest even); v is copied bit for bit.
+  * Qwen3 q/k norm ([P5] §5: the attention module holds q_norm and k_norm
+    RMSNorm modules; §3.2 passes rms_norm_eps): each q and k head is
+    RMS-normalised over head_dim with a learned [head_dim] weight,
+    y = x / sqrt(mean(x^2) + eps) * w, after the QKV split and before the
+    rotation (the pages print the modules, not their order of use), in
+    float64 together with the rotation, rounded once;
   * FP8 KV cache ([P2] §4.1 and §4.2 list FP8 KV-cache quantization with
     per-layer cache scale parameters; §6.3 names the E4M3FN format): the
     cache holds E4M3FN codes of the exact rotated key (or the value) divided
@@ -53,6 +59,7 @@ __all__ = [
     "bf16_bits_to_f64", "rope_cache_write", "gather_kv", "causal_visible",
     "softmax_rows", "kv_head_for", "default_scale", "attention_varlen",
     "attention_decode", "run_step", "fp8_e4m3_decode", "fp8_e4m3_encode", "E4M3_MAX",
+    "rms_norm_heads",
 ]
 
 
@@ -192,11 +199,23 @@ def fp8_e4m3_encode(x: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Qwen3 per-head RMSNorm of q and k
+# ---------------------------------------------------------------------------
+def rms_norm_heads(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis (head_dim): x / sqrt(mean(x^2) + eps) * w,
+    float64.  ([P5] §5 q_norm / k_norm RMSNorm modules; §3.2 rms_norm_eps.)"""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * np.asarray(weight, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
 # 1-3. split fused QKV, rotate, write the paged cache
 # ---------------------------------------------------------------------------
 def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
                      num_heads, num_kv_heads, head_dim, block_size, theta,
-                     cache_dtype=None, k_scale=1.0, v_scale=1.0):
+                     cache_dtype=None, k_scale=1.0, v_scale=1.0,
+                     q_norm_weight=None, k_norm_weight=None, rms_eps=1e-6):
     """Split the fused QKV rows, rotate q and k, scatter k and v into the cache.
 
     qkv: storage [T][(H + 2 Hkv) * d]; columns [0, H d) are q, then Hkv k
@@ -207,14 +226,21 @@ def rope_cache_write(qkv, dtype, positions, slot_mapping, k_cache, v_cache,
         K[block][g][offset][:] = rot(k[t][g]);  V[block][g][:][offset] = v[t][g]
     Slots not named keep their previous bits ([P3] §2.1 paged blocks).
     cache_dtype "fp8": the caches hold E4M3FN codes, K = code(rot(k) /
-    k_scale), V = code(v / v_scale), each one rounding from float64."""
+    k_scale), V = code(v / v_scale), each one rounding from float64.
+    q_norm_weight / k_norm_weight ([head_dim], storage dtype): Qwen3 q/k norm,
+    rot(rms_norm(q)) and rot(rms_norm(k)) instead of rot(q), rot(k)."""
     H, Hkv, d, B = num_heads, num_kv_heads, head_dim, block_size
     qkv = np.asarray(qkv)
     T = qkv.shape[0]
     heads = qkv.reshape(T, H + 2 * Hkv, d)
     x = to_f64(heads, dtype)
-    q_rot = rope_neox(x[:, :H], positions, theta)
-    k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)
+    xq, xk = x[:, :H], x[:, H:H + Hkv]
+    if q_norm_weight is not None:
+        xq = rms_norm_heads(xq, to_f64(q_norm_weight, dtype), rms_eps)
+    if k_norm_weight is not None:
+        xk = rms_norm_heads(xk, to_f64(k_norm_weight, dtype), rms_eps)
+    q_rot = rope_neox(xq, positions, theta)
+    k_rot = rope_neox(xk, positions, theta)
     q_out = from_f64(q_rot, dtype)
     if cache_dtype == "fp8":
         k_store = fp8_e4m3_encode(k_rot / float(k_scale))
@@ -353,9 +379,11 @@ def run_step(batch, k_cache=None, v_cache=None):
     vc0 = batch.v_cache if v_cache is None else v_cache
     cd = getattr(sh, "cache_dtype", None)
     ks, vs = getattr(sh, "k_scale", 1.0), getattr(sh, "v_scale", 1.0)
+    qn, kn = getattr(batch, "q_norm_weight", None), getattr(batch, "k_norm_weight", None)
     q_out, kc, vc = rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
                                      kc0, vc0, sh.num_heads, sh.num_kv_heads, sh.head_dim,
-                                     sh.block_size, sh.rope_theta, cd, ks, vs)
+                                     sh.block_size, sh.rope_theta, cd, ks, vs, qn, kn,
+                                     getattr(sh, "rms_eps", 1e-6))
     out = attention_varlen(q_out, kc, vc, batch.cu_seqlens_q, batch.context_lens,
                            batch.block_tables, sh.num_heads, sh.num_kv_heads, sh.head_dim,
                            sh.block_size, sh.dtype, cache_dtype=cd, k_scale=ks, v_scale=vs)

@@ -114,6 +114,7 @@ class AttnShape:
     cache_dtype: Optional[str] = None   # None: the caches use `dtype`; "fp8": E4M3FN codes
     k_scale: float = 1.0                # FP8 cache: value = code * scale
     v_scale: float = 1.0
+    rms_eps: float = 1e-6               # Qwen3 q/k norm epsilon (when the batch has weights)
 
     @property
     def group(self) -> int:
@@ -166,6 +167,9 @@ class Batch:
     pre_k: Optional[List[np.ndarray]] = None
     pre_v: Optional[List[np.ndarray]] = None
     notes: dict = field(default_factory=dict)
+    # Qwen3 q/k norm weights ([head_dim], step dtype), or None
+    q_norm_weight: Optional[np.ndarray] = None
+    k_norm_weight: Optional[np.ndarray] = None
 
     # ---- derived views ----
     @property
@@ -481,11 +485,31 @@ def mixed_tp2(seed: int = 5, keep_logical: bool = False) -> Batch:
                   keep_logical=keep_logical)
 
 
+def with_qk_norm(b: Batch, seed: int) -> Batch:
+    """Attach Qwen3 q/k norm weights: N(1, 0.1^2) per element (learned RMSNorm
+    weights sit around 1), drawn from their own generator so the batch's
+    other draws are unchanged."""
+    rng = np.random.default_rng([seed, 0x51CE])
+    d, dt = b.shape.head_dim, b.shape.dtype
+    b.q_norm_weight = normal_storage(rng, (d,), 0.1, "f32") + np.float32(1.0)
+    b.k_norm_weight = normal_storage(rng, (d,), 0.1, "f32") + np.float32(1.0)
+    if dt == "bf16":
+        b.q_norm_weight = f32_to_bf16_bits(b.q_norm_weight)
+        b.k_norm_weight = f32_to_bf16_bits(b.k_norm_weight)
+    return b
+
+
+def qwen3_decode_qknorm(seed: int = 2, num_seqs: int = 32, keep_logical: bool = False) -> Batch:
+    """The Qwen3-0.6B decode with its q/k RMSNorm (weights N(1, 0.1^2), eps
+    1e-6) fused into the cache write."""
+    return with_qk_norm(qwen3_decode(seed, num_seqs, keep_logical), seed)
+
+
 def small_case(seed: int, dtype: str, num_heads: int, num_kv_heads: int, head_dim: int,
                context_lens, query_lens, num_prefill: int, block_size: int = 16,
                value_scale: float = 1.0, keep_logical: bool = True, shares_prefix=None,
                shared_prefix_len: int = 0, cache_dtype=None, k_scale: float = 1.0,
-               v_scale: float = 1.0) -> Batch:
+               v_scale: float = 1.0, qk_norm: bool = False) -> Batch:
     """A custom small batch (tests): explicit lengths, any head layout."""
     shape = AttnShape(num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                       block_size=block_size, dtype=dtype, cache_dtype=cache_dtype,
@@ -494,8 +518,9 @@ def small_case(seed: int, dtype: str, num_heads: int, num_kv_heads: int, head_di
     ctx = np.asarray(context_lens, np.int32)
     ql = np.asarray(query_lens, np.int32)
     sh = np.zeros(len(ctx), bool) if shares_prefix is None else np.asarray(shares_prefix, bool)
-    return _build(f"small_{dtype}_s{seed}", shape, seed, rng, ctx, ql, num_prefill, sh,
-                  shared_prefix_len, value_scale, keep_logical=keep_logical)
+    b = _build(f"small_{dtype}_s{seed}", shape, seed, rng, ctx, ql, num_prefill, sh,
+               shared_prefix_len, value_scale, keep_logical=keep_logical)
+    return with_qk_norm(b, seed) if qk_norm else b
 
 
 WORKLOADS = {
@@ -505,4 +530,5 @@ WORKLOADS = {
     "qwen2_long_decode": qwen2_long_decode,
     "mixed_tp2": mixed_tp2,
     "qwen2_long_decode_fp8": qwen2_long_decode_fp8,
+    "qwen3_decode_qknorm": qwen3_decode_qknorm,
 }

@@ -41,7 +41,9 @@ def run_oracle(batch, seqs=None):
     fp8 = dict(cache_dtype=sh.cache_dtype, k_scale=sh.k_scale, v_scale=sh.v_scale)
     q_out, kc, vc = R.rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
                                        batch.k_cache, batch.v_cache, sh.num_heads, sh.num_kv_heads,
-                                       sh.head_dim, sh.block_size, sh.rope_theta, **fp8)
+                                       sh.head_dim, sh.block_size, sh.rope_theta, **fp8,
+                                       q_norm_weight=batch.q_norm_weight,
+                                       k_norm_weight=batch.k_norm_weight, rms_eps=sh.rms_eps)
     cu = batch.cu_seqlens_q
     out = np.full((batch.num_tokens, sh.num_heads, sh.head_dim), np.nan)
     ids = range(batch.num_seqs) if seqs is None else seqs

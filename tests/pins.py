@@ -515,7 +515,64 @@ def pin_fp8_attention_reads_dequantized_cache(R):
     assert np.array_equal(got, want)
 
 
+# ---------------------------------------------------------------------------
+# Qwen3 q/k RMSNorm
+# ---------------------------------------------------------------------------
+def pin_rms_norm_matches_torch(R):
+    """torch.nn.functional.rms_norm (float64) on random heads and weights."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((5, 3, 128)) * rng.uniform(0.01, 10, (5, 3, 1))
+    w = rng.standard_normal(128) * 0.2 + 1.0
+    for eps in (1e-6, 1e-2, 0.0):
+        want = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w),
+                                            eps).numpy()
+        np.testing.assert_allclose(R.rms_norm_heads(x, w, eps), want, rtol=1e-13, atol=1e-15)
+
+
+def pin_rms_norm_closed_forms(R):
+    """With w = 1 and eps = 0 the output has RMS exactly 1 (norm sqrt(d)) and
+    is invariant to scaling x; a constant head c maps to sign(c) c / sqrt(c^2
+    + eps) per element; eps keeps a zero head at zero."""
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((4, 64))
+    y = R.rms_norm_heads(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.sqrt((y * y).mean(-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(R.rms_norm_heads(37.5 * x, np.ones(64), 0.0), y, rtol=1e-13)
+    for c, eps in ((0.5, 1e-6), (-3.0, 0.25)):
+        got = R.rms_norm_heads(np.full((1, 16), c), np.ones(16), eps)
+        np.testing.assert_allclose(got, c / math.sqrt(c * c + eps), rtol=1e-15)
+    assert np.all(R.rms_norm_heads(np.zeros((2, 8)), np.ones(8), 1e-6) == 0.0)
+
+
+def pin_qk_norm_in_cache_write(R):
+    """The cache write with q/k norm weights: stored q/k have the norm of the
+    normalised head times the weight (the rotation preserves norms), v is
+    untouched, and unit weights with eps 0 leave every stored head with RMS 1
+    up to the storage rounding."""
+    b = W.small_case(73, "f32", 4, 2, 32, context_lens=[9, 4], query_lens=[9, 4], num_prefill=2,
+                     keep_logical=True)
+    sh = b.shape
+    T, H, Hkv, d = b.num_tokens, sh.num_heads, sh.num_kv_heads, sh.head_dim
+    args = (b.qkv, sh.dtype, b.positions, b.slot_mapping, b.k_cache, b.v_cache, H, Hkv, d,
+            sh.block_size, sh.rope_theta)
+    one = np.ones(d, np.float32)
+    q_out, kc, vc = R.rope_cache_write(*args, q_norm_weight=one, k_norm_weight=one, rms_eps=0.0)
+    assert np.allclose(np.sqrt((q_out.astype(np.float64) ** 2).mean(-1)), 1.0, rtol=1e-6)
+    B = sh.block_size
+    for t in range(T):
+        blk, off = divmod(int(b.slot_mapping[t]), B)
+        k = kc[blk, :, off, :].astype(np.float64)
+        assert np.allclose(np.sqrt((k * k).mean(-1)), 1.0, rtol=1e-6)
+        assert np.array_equal(vc[blk, :, :, off], b.qkv[t].reshape(H + 2 * Hkv, d)[H + Hkv:])
+    w = np.linspace(0.5, 1.5, d).astype(np.float32)
+    q2, _, _ = R.rope_cache_write(*args, q_norm_weight=w, k_norm_weight=one, rms_eps=0.0)
+    x = b.qkv.reshape(T, H + 2 * Hkv, d)[:, :H].astype(np.float64)
+    want = np.sqrt(((x / np.sqrt((x * x).mean(-1, keepdims=True)) * w) ** 2).sum(-1))
+    assert np.allclose(np.sqrt((q2.astype(np.float64) ** 2).sum(-1)), want, rtol=1e-6)
+
+
 ALL_PINS = [
+    pin_rms_norm_matches_torch, pin_rms_norm_closed_forms, pin_qk_norm_in_cache_write,
     pin_fp8_decode_table, pin_fp8_matches_torch, pin_fp8_roundtrip_ties_saturation,
     pin_fp8_cache_write, pin_fp8_attention_reads_dequantized_cache,
     pin_bf16_rounding_values, pin_bf16_rounding_matches_torch,

@@ -34,10 +34,10 @@ MUTATIONS = [
     ("rope_cache_write", "blk, off = divmod(slot, B)", "off, blk = divmod(slot, B)"),
     ("rope_cache_write", "v_store = heads[:, H + Hkv:]",
      "v_store = from_f64(rope_neox(x[:, H + Hkv:], positions, theta), dtype)"),  # v rotated
-    ("rope_cache_write", "k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)",
-     "k_rot = x[:, H:H + Hkv]"),                                            # k not rotated
-    ("rope_cache_write", "k_rot = rope_neox(x[:, H:H + Hkv], positions, theta)",
-     "k_rot = rope_neox(x[:, H + Hkv:], positions, theta)"),                # k from v columns
+    ("rope_cache_write", "k_rot = rope_neox(xk, positions, theta)",
+     "k_rot = xk"),                                                         # k not rotated
+    ("rope_cache_write", "xq, xk = x[:, :H], x[:, H:H + Hkv]",
+     "xq, xk = x[:, :H], x[:, H + Hkv:]"),                                  # k from v columns
     ("gather_kv", "off = j % B", "off = (j + 1) % B"),
     ("gather_kv", "V = to_f64(np.asarray(v_cache)[blk, :, :, off], dtype)",
      "V = to_f64(np.asarray(v_cache)[blk, :, off % np.asarray(v_cache).shape[2], :], dtype)"),
@@ -52,6 +52,13 @@ MUTATIONS = [
     ("attention_varlen", "z = scale * (qf[r0:r1, h, :] @ K[:, g, :].T)",
      "z = scale * (qf[r0:r1, h, :] @ V[:, g, :].T)"),
     ("attention_varlen", "n, c = r1 - r0, int(context_lens[s])", "n, c = r1 - r0, int(context_lens[s]) - 1"),
+    # Qwen3 q/k norm
+    ("rms_norm_heads", "np.sqrt(ms + float(eps))", "np.sqrt(ms)"),          # eps dropped
+    ("rms_norm_heads", "ms = np.mean(x * x, axis=-1, keepdims=True)",
+     "ms = np.sum(x * x, axis=-1, keepdims=True)"),                         # sum, not mean
+    ("rms_norm_heads", "* np.asarray(weight, dtype=np.float64)", "* 1.0"),  # weight ignored
+    ("rope_cache_write", "xq = rms_norm_heads(xq, to_f64(q_norm_weight, dtype), rms_eps)",
+     "xq = rms_norm_heads(xq, to_f64(k_norm_weight, dtype), rms_eps)"),     # weights swapped
     # FP8 cache codes and scales
     ("fp8_e4m3_decode", "(1.0 + m / 8.0)", "(m / 8.0)"),                  # implicit one dropped
     ("fp8_e4m3_decode", "np.exp2((e - 7)", "np.exp2((e - 8)"),            # wrong bias
