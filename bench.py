@@ -123,6 +123,18 @@ def bench_decode_fp8(steps, warmup):
                 alg_bytes=b.decode_bytes(), seqs=b.num_seqs)
 
 
+def bench_qknorm(steps, warmup):
+    """Qwen3 q/k RMSNorm fused into the rope + cache write, on the prefill
+    batch (the largest token count): its cost over the plain write."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    b = W.with_qk_norm(W.qwen2_prefill(), 3)
+    dev = runner.DeviceStep(b)
+    ms, _ = _time(dev.rope_write, steps, warmup)
+    return dict(tokens=b.num_tokens, ms=ms, bytes=b.rope_write_bytes())
+
+
 def bench_prefill(steps, warmup):
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
@@ -238,6 +250,8 @@ def main():
         log(f"mixed: {res['mixed']['step_ms']:.3f} ms")
         res["fp8"] = bench_decode_fp8(args.steps, args.warmup)
         log(f"fp8 decode: step {res['fp8']['step_ms']:.3f} ms (decode {res['fp8']['decode_ms']:.3f})")
+        res["qknorm"] = bench_qknorm(args.steps, args.warmup)
+        log(f"q/k-norm rope + cache write: {res['qknorm']['ms']:.4f} ms")
 
     b = dec["batch"]
     value = dec["kv_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
@@ -313,6 +327,16 @@ def main():
             "hbm_frac": round(f["alg_bytes"] / (f["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(f["seqs"] / (f["step_ms"] * 1e-3), 1),
             "speedup_vs_bf16_cache": round(dec["step_ms"] / f["step_ms"], 3),
+        }
+    if "qknorm" in res:
+        qn = res["qknorm"]
+        out["qk_norm_cache_write"] = {
+            "workload": "the qwen2-7b prefill batch (seed 3) through the Qwen3 q/k RMSNorm + rope "
+                        "+ cache write (weights N(1, 0.1^2), eps 1e-6)",
+            "tokens": qn["tokens"],
+            "ms": round(qn["ms"], 4),
+            "GB/s": round(qn["bytes"] / (qn["ms"] * 1e-3) / 1e9, 2),
+            "plain_write_ms": round(res["prefill"]["rope_ms"], 4),
         }
     if not args.no_cpu:
         log("CPU oracle baseline")

@@ -250,6 +250,41 @@ int qwen2_attn_decode_paged_fp8(const void* q, int64_t q_row_stride,
                                 int dtype, float k_scale, float v_scale, hipStream_t stream);
 
 /*
+ * Qwen3 q/k norm.  As qwen2_rope_cache_write (resp. _fp8), with every q and k
+ * head RMS-normalised over head_dim before the rotation:
+ *   x <- x / sqrt(mean_i(x_i^2) + rms_eps) * w     (w = q_norm_weight or
+ *   k_norm_weight, device [head_dim] of `dtype`, 16-byte aligned)
+ * computed in float64 together with the rotation and rounded once (FP8: the
+ * cache code of the normalised, rotated k divided by k_scale).  v is not
+ * normalised.  rms_eps must be finite and >= 0 (Qwen3: 1e-6).
+ * "nano-vllm: Qwen3 骨架", §5 (the q_norm / k_norm RMSNorm modules of the
+ * attention) and §3.2 (rms_norm_eps).
+ */
+int qwen3_rope_cache_write(const void* q, int64_t q_row_stride,
+                           void* q_out, int64_t q_out_row_stride,
+                           const void* k, int64_t k_row_stride,
+                           const void* v, int64_t v_row_stride,
+                           const int32_t* positions, const int32_t* slot_mapping,
+                           const double* cos_sin, int max_position,
+                           void* k_cache, void* v_cache, int num_blocks,
+                           int num_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int dtype,
+                           const void* q_norm_weight, const void* k_norm_weight, double rms_eps,
+                           hipStream_t stream);
+
+int qwen3_rope_cache_write_fp8(const void* q, int64_t q_row_stride,
+                               void* q_out, int64_t q_out_row_stride,
+                               const void* k, int64_t k_row_stride,
+                               const void* v, int64_t v_row_stride,
+                               const int32_t* positions, const int32_t* slot_mapping,
+                               const double* cos_sin, int max_position,
+                               void* k_cache, void* v_cache, int num_blocks,
+                               int num_tokens, int num_heads, int num_kv_heads,
+                               int head_dim, int block_size, int dtype,
+                               const void* q_norm_weight, const void* k_norm_weight,
+                               double rms_eps, float k_scale, float v_scale, hipStream_t stream);
+
+/*
  * Verify the device-metadata contract on HOST copies (tests, debugging).
  * positions, slot_mapping: HOST int32 [num_tokens] (either may be NULL to
  * skip it).  cu_seqlens_q: HOST int32 [num_seqs + 1], or NULL for a decode

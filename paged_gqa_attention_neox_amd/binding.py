@@ -42,6 +42,11 @@ SIGNATURES = {
                                            _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _f, _p]),
     "qwen2_attn_decode_paged_fp8": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _i64, _p, _sz,
                                          _i, _i, _i, _i, _i, _i, _f, _i, _f, _f, _p]),
+    "qwen3_rope_cache_write": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
+                                    _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _d, _p]),
+    "qwen3_rope_cache_write_fp8": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
+                                        _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _d, _f, _f,
+                                        _p]),
     "qwen2_check_metadata_host": (_i, [_p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i]),
     "qwen2_status_string": (ctypes.c_char_p, [_i]),
     "qwen2_last_error": (ctypes.c_char_p, []),
@@ -266,6 +271,39 @@ def qwen2_attn_decode_paged_fp8(q, k_cache, v_cache, block_tables, context_lens,
                                              num_kv_heads, head_dim, block_size, float(scale),
                                              _dtype(q), float(k_scale), float(v_scale),
                                              _stream(stream)))
+
+
+def qwen3_rope_cache_write(q, q_out, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,
+                           num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                           q_norm_weight, k_norm_weight, rms_eps: float = 1e-6,
+                           k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+                           stream=None) -> None:
+    """Qwen3: per-head RMSNorm of q and k (weights [head_dim] of the q dtype)
+    before the rotation; with k_scale/v_scale the caches are FP8 code tensors
+    (qwen3_rope_cache_write_fp8)."""
+    T = q.shape[0]
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != head_dim or cos_sin.dtype != torch.float64:
+        raise ValueError("cos_sin must be float64 [max_position][head_dim]")
+    for name, w in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if w.dtype != q.dtype or w.numel() != head_dim or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [head_dim] tensor of the q dtype")
+    fp8 = k_scale is not None
+    if fp8:
+        _fp8_caches(k_cache, v_cache, num_kv_heads)
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(q_out, num_heads * head_dim)
+    kp, ks = _rows(k, num_kv_heads * head_dim)
+    vp, vs = _rows(v, num_kv_heads * head_dim)
+    common = (qp, qs, op, os_, kp, ks, vp, vs, _i32(positions), _i32(slot_mapping),
+              cos_sin.data_ptr(), cos_sin.shape[0], k_cache.data_ptr(), v_cache.data_ptr(),
+              k_cache.shape[0], T, num_heads, num_kv_heads, head_dim, block_size, _dtype(q),
+              q_norm_weight.data_ptr(), k_norm_weight.data_ptr(), float(rms_eps))
+    if fp8:
+        _check("qwen3_rope_cache_write_fp8",
+               lib().qwen3_rope_cache_write_fp8(*common, float(k_scale), float(v_scale),
+                                                _stream(stream)))
+    else:
+        _check("qwen3_rope_cache_write", lib().qwen3_rope_cache_write(*common, _stream(stream)))
 
 
 def qwen2_check_metadata_host(positions, slot_mapping, cu_seqlens_q, context_lens, block_tables,

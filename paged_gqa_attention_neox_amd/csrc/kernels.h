@@ -23,6 +23,9 @@ struct RopeWriteArgs {
   int dtype;
   int cache_fp8;                 // caches hold E4M3FN codes of value / scale
   float k_scale, v_scale;
+  const void* q_norm_w;          // Qwen3 q/k RMSNorm weights [head_dim] (dtype), or null
+  const void* k_norm_w;
+  double rms_eps;
 };
 
 struct AttnArgs {

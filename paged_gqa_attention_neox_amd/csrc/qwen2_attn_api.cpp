@@ -107,10 +107,17 @@ static int rope_write_impl(const void* q, int64_t q_row_stride, void* q_out, int
                            const double* cos_sin, int max_position, void* k_cache, void* v_cache,
                            int num_blocks, int num_tokens, int num_heads, int num_kv_heads,
                            int head_dim, int block_size, int dtype, int cache_fp8, float k_scale,
-                           float v_scale, hipStream_t stream) {
+                           float v_scale, const void* q_norm_w, const void* k_norm_w,
+                           double rms_eps, hipStream_t stream) {
   int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (st) return st;
   if (cache_fp8 && (st = check_fp8_scales(k_scale, v_scale))) return st;
+  if ((q_norm_w != nullptr) != (k_norm_w != nullptr))
+    return fail(QW_ERR_NULL, "q_norm_weight and k_norm_weight must both be given");
+  if (q_norm_w && (!aligned16(q_norm_w) || !aligned16(k_norm_w)))
+    return fail(QW_ERR_ALIGN, "q/k norm weights are not 16-byte aligned");
+  if (q_norm_w && !(rms_eps >= 0.0 && rms_eps < 1e300))
+    return fail(QW_ERR_SHAPE, "rms_eps must be finite and >= 0");
   if (num_tokens < 0) return fail(QW_ERR_SHAPE, "num_tokens=%d < 0", num_tokens);
   if (num_blocks < 0) return fail(QW_ERR_SHAPE, "num_blocks=%d < 0", num_blocks);
   if (max_position < 1) return fail(QW_ERR_SHAPE, "max_position=%d < 1", max_position);
@@ -148,6 +155,7 @@ static int rope_write_impl(const void* q, int64_t q_row_stride, void* q_out, int
   a.num_tokens = num_tokens; a.num_heads = num_heads; a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim; a.block_size = block_size; a.dtype = dtype;
   a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.q_norm_w = q_norm_w; a.k_norm_w = k_norm_w; a.rms_eps = rms_eps;
   return launched(qw::launch_rope_cache_write(a, stream));
 }
 
@@ -160,7 +168,7 @@ int qwen2_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int
   return rope_write_impl(q, q_row_stride, q_out, q_out_row_stride, k, k_row_stride, v, v_row_stride,
                          positions, slot_mapping, cos_sin, max_position, k_cache, v_cache,
                          num_blocks, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
-                         dtype, 0, 1.0f, 1.0f, stream);
+                         dtype, 0, 1.0f, 1.0f, nullptr, nullptr, 0.0, stream);
 }
 
 int qwen2_rope_cache_write_fp8(const void* q, int64_t q_row_stride, void* q_out,
@@ -173,7 +181,36 @@ int qwen2_rope_cache_write_fp8(const void* q, int64_t q_row_stride, void* q_out,
   return rope_write_impl(q, q_row_stride, q_out, q_out_row_stride, k, k_row_stride, v, v_row_stride,
                          positions, slot_mapping, cos_sin, max_position, k_cache, v_cache,
                          num_blocks, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
-                         dtype, 1, k_scale, v_scale, stream);
+                         dtype, 1, k_scale, v_scale, nullptr, nullptr, 0.0, stream);
+}
+
+int qwen3_rope_cache_write(const void* q, int64_t q_row_stride, void* q_out, int64_t q_out_row_stride,
+                           const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                           const int32_t* positions, const int32_t* slot_mapping,
+                           const double* cos_sin, int max_position, void* k_cache, void* v_cache,
+                           int num_blocks, int num_tokens, int num_heads, int num_kv_heads,
+                           int head_dim, int block_size, int dtype, const void* q_norm_weight,
+                           const void* k_norm_weight, double rms_eps, hipStream_t stream) {
+  if (!q_norm_weight || !k_norm_weight) return fail(QW_ERR_NULL, "q/k norm weight is NULL");
+  return rope_write_impl(q, q_row_stride, q_out, q_out_row_stride, k, k_row_stride, v, v_row_stride,
+                         positions, slot_mapping, cos_sin, max_position, k_cache, v_cache,
+                         num_blocks, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                         dtype, 0, 1.0f, 1.0f, q_norm_weight, k_norm_weight, rms_eps, stream);
+}
+
+int qwen3_rope_cache_write_fp8(const void* q, int64_t q_row_stride, void* q_out,
+                               int64_t q_out_row_stride, const void* k, int64_t k_row_stride,
+                               const void* v, int64_t v_row_stride, const int32_t* positions,
+                               const int32_t* slot_mapping, const double* cos_sin, int max_position,
+                               void* k_cache, void* v_cache, int num_blocks, int num_tokens,
+                               int num_heads, int num_kv_heads, int head_dim, int block_size,
+                               int dtype, const void* q_norm_weight, const void* k_norm_weight,
+                               double rms_eps, float k_scale, float v_scale, hipStream_t stream) {
+  if (!q_norm_weight || !k_norm_weight) return fail(QW_ERR_NULL, "q/k norm weight is NULL");
+  return rope_write_impl(q, q_row_stride, q_out, q_out_row_stride, k, k_row_stride, v, v_row_stride,
+                         positions, slot_mapping, cos_sin, max_position, k_cache, v_cache,
+                         num_blocks, num_tokens, num_heads, num_kv_heads, head_dim, block_size,
+                         dtype, 1, k_scale, v_scale, q_norm_weight, k_norm_weight, rms_eps, stream);
 }
 
 static int check_attn_common(const void* q, int64_t q_row_stride, const void* k_cache,

@@ -162,7 +162,13 @@ template <> struct Vec8<float> {
 // fused rotate + scatter
 // ---------------------------------------------------------------------------
 // CF8: the caches hold E4M3FN codes of (rotated) k / k_scale and v / v_scale.
-template <typename T, int D, bool CF8>
+// QKN: Qwen3 q/k norm before the rotation ("nano-vllm: Qwen3 骨架", §5 the
+// q_norm / k_norm RMSNorm modules of the attention; §3.2 rms_norm_eps): each
+// q and k head becomes x / sqrt(mean(x^2) + eps) * w in float64.  The RCH
+// items of a head sit in RCH consecutive lanes aligned to RCH (the item index
+// is idx, and per-token and per-head item counts are multiples of RCH), so
+// the head's sum of squares needs log2(RCH) lane exchanges.
+template <typename T, int D, bool CF8, bool QKN>
 __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) {
   constexpr int HALF = D / 2;
   constexpr int RCH = HALF / 8;   // rotation items per head (8 pairs each)
@@ -224,6 +230,26 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       double x1[8], x2[8], y1[8], y2[8];
       x1v.to_f64(x1);
       x2v.to_f64(x2);
+      if constexpr (QKN) {
+        double ss = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fma(x1[j], x1[j], fma(x2[j], x2[j], ss));
+#pragma unroll
+        for (int o = 1; o < RCH; o <<= 1) ss += __shfl_xor(ss, o);
+        const double rms = sqrt(ss / D + a.rms_eps);
+        const T* wp = static_cast<const T*>(is_q ? a.q_norm_w : a.k_norm_w);
+        Vec8<T> w1v, w2v;
+        w1v.load(wp + i0);
+        w2v.load(wp + HALF + i0);
+        double w1[8], w2[8];
+        w1v.to_f64(w1);
+        w2v.to_f64(w2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x1[j] = x1[j] / rms * w1[j];
+          x2[j] = x2[j] / rms * w2[j];
+        }
+      }
       const double* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
       double cv[8], sv[8];
 #pragma unroll
@@ -291,19 +317,19 @@ hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream) {
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 1 << 20) blocks = 1 << 20;
   const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
-#define QW_ROPE_LAUNCH(T, D, F8) \
-  hipLaunchKernelGGL((rope_cache_write_kernel<T, D, F8>), grid, block, 0, stream, a)
-  if (a.cache_fp8) {
-    if (a.dtype == kBF16) {
-      if (d == 128) QW_ROPE_LAUNCH(uint16_t, 128, true); else QW_ROPE_LAUNCH(uint16_t, 64, true);
-    } else {
-      if (d == 128) QW_ROPE_LAUNCH(float, 128, true); else QW_ROPE_LAUNCH(float, 64, true);
-    }
-  } else if (a.dtype == kBF16) {
-    if (d == 128) QW_ROPE_LAUNCH(uint16_t, 128, false); else QW_ROPE_LAUNCH(uint16_t, 64, false);
+#define QW_ROPE_LAUNCH(T, D, F8, N) \
+  hipLaunchKernelGGL((rope_cache_write_kernel<T, D, F8, N>), grid, block, 0, stream, a)
+#define QW_ROPE_D(T, F8, N) \
+  do { if (d == 128) QW_ROPE_LAUNCH(T, 128, F8, N); else QW_ROPE_LAUNCH(T, 64, F8, N); } while (0)
+#define QW_ROPE_N(T, F8) \
+  do { if (a.q_norm_w) QW_ROPE_D(T, F8, true); else QW_ROPE_D(T, F8, false); } while (0)
+  if (a.dtype == kBF16) {
+    if (a.cache_fp8) QW_ROPE_N(uint16_t, true); else QW_ROPE_N(uint16_t, false);
   } else {
-    if (d == 128) QW_ROPE_LAUNCH(float, 128, false); else QW_ROPE_LAUNCH(float, 64, false);
+    if (a.cache_fp8) QW_ROPE_N(float, true); else QW_ROPE_N(float, false);
   }
+#undef QW_ROPE_N
+#undef QW_ROPE_D
 #undef QW_ROPE_LAUNCH
   return hipGetLastError();
 }

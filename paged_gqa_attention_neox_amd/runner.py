@@ -67,6 +67,10 @@ class DeviceStep:
         self.k_cache = k_cache if k_cache is not None else to_device(batch.k_cache, cdt, device)
         self.v_cache = v_cache if v_cache is not None else to_device(batch.v_cache, cdt, device)
         self.cos_sin = rope_table(d, sh.rope_theta, sh.max_position, device)
+        self.q_norm_w = self.k_norm_w = None
+        if batch.q_norm_weight is not None:
+            self.q_norm_w = to_device(batch.q_norm_weight, sh.dtype, device)
+            self.k_norm_w = to_device(batch.k_norm_weight, sh.dtype, device)
         P = batch.num_prefill
         self.Tp = batch.num_prefill_tokens
         if P:
@@ -88,7 +92,11 @@ class DeviceStep:
         args = (self.q, self.q_out, self.k, self.v, self.positions, self.slots, self.cos_sin,
                 self.k_cache, self.v_cache, sh.num_heads, sh.num_kv_heads, sh.head_dim,
                 sh.block_size)
-        if self.fp8:
+        if self.q_norm_w is not None:
+            B.qwen3_rope_cache_write(*args, self.q_norm_w, self.k_norm_w, sh.rms_eps,
+                                     sh.k_scale if self.fp8 else None,
+                                     sh.v_scale if self.fp8 else None, stream)
+        elif self.fp8:
             B.qwen2_rope_cache_write_fp8(*args, sh.k_scale, sh.v_scale, stream)
         else:
             B.qwen2_rope_cache_write(*args, stream)

@@ -140,6 +140,37 @@ def test_rope_validation(lib, kw, status):
     assert _rope(lib, **kw) == status
 
 
+def _rope_qkn(lib, fp8=False, **kw):
+    W_ = (28 + 8) * 128
+    a = dict(q=P, qs=W_, qo=P2, qos=28 * 128, k=P + 28 * 256, ks=W_, v=P + 32 * 256, vs=W_, pos=P,
+             slot=P, cs=P3, maxp=32768, kc=P, vc=P2, nb=10, T=5, H=28, Hkv=4, d=128, B=16, dt=1,
+             qw=P3, kw=P3 + 256, eps=1e-6, ksc=0.03, vsc=0.03)
+    a.update(kw)
+    args = (a["q"], a["qs"], a["qo"], a["qos"], a["k"], a["ks"], a["v"], a["vs"], a["pos"],
+            a["slot"], a["cs"], a["maxp"], a["kc"], a["vc"], a["nb"], a["T"], a["H"], a["Hkv"],
+            a["d"], a["B"], a["dt"], a["qw"], a["kw"], a["eps"])
+    if fp8:
+        return lib.qwen3_rope_cache_write_fp8(*args, a["ksc"], a["vsc"], None)
+    return lib.qwen3_rope_cache_write(*args, None)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(qw=0), QW_ERR_NULL), (dict(kw=0), QW_ERR_NULL), (dict(qw=0, kw=0), QW_ERR_NULL),
+    (dict(qw=MIS), QW_ERR_ALIGN), (dict(kw=MIS), QW_ERR_ALIGN),
+    (dict(eps=-1e-6), QW_ERR_SHAPE), (dict(eps=float("nan")), QW_ERR_SHAPE),
+    (dict(eps=float("inf")), QW_ERR_SHAPE), (dict(q=0), QW_ERR_NULL), (dict(d=80), QW_ERR_UNSUPPORTED),
+])
+def test_qwen3_rope_validation(lib, fp8, kw, status):
+    assert _rope_qkn(lib, fp8=fp8, **kw) == status
+    assert lib.qwen2_last_error().decode()
+
+
+def test_qwen3_rope_fp8_scale_validation(lib):
+    assert _rope_qkn(lib, fp8=True, ksc=0.0) == QW_ERR_SHAPE
+    assert _rope_qkn(lib, fp8=True, vsc=float("nan")) == QW_ERR_SHAPE
+
+
 def _prefill(lib, **kw):
     a = dict(q=P, qs=28 * 128, kc=P2, vc=P3, nb=100, cu=P, ctx=P, bt=P, mb=64, out=P2, os=28 * 128,
              S=4, T=100, maxq=50, maxc=1024, H=28, Hkv=4, d=128, B=16, scale=0.0884, dt=1)
