@@ -1,9 +1,8 @@
-// Paged single-token GQA decode for bf16, head_dim 128, block 16, with the
-// context split into partitions ("split-K") and an exact log-sum-exp merge.
-// The cache may hold bf16 or FP8 E4M3FN codes ("Qwen2大模型架构解析与vLLM优化
-// 实践", §4.1-4.2 FP8 KV-cache quantization with cache scales, §6.3 E4M3FN):
-// FP8 tiles are half the bytes and are widened to bf16 pairs in registers
-// (exact), k_scale folds into the score scale and v_scale into the output.
+// Paged single-token GQA decode for bf16, head_dim 128, block 16.  The cache
+// may hold bf16 or FP8 E4M3FN codes ("Qwen2大模型架构解析与vLLM优化实践",
+// §4.1-4.2 FP8 KV-cache quantization with cache scales, §6.3 E4M3FN): FP8
+// tiles are half the bytes and are widened to bf16 in registers (exact),
+// k_scale folds into the score scale and v_scale into the output.
 //
 // Attention of one new token over its sequence's paged KV ("vLLM 部署 Qwen",
 // §2.1 PagedAttention; §4.1: access to KV pages is what decode tuning is
@@ -11,50 +10,76 @@
 // ("Qwen2 模型结构代码详解", §2), so each (block, KV head) tile is read from HBM
 // exactly once and used for all G heads.
 //
-// Work decomposition: one 256-thread workgroup (4 waves) per
-// (partition of kPart tokens, KV head, sequence).  The waves take the
-// partition's 16-token blocks round-robin and stream them through kNBuf
-// register buffers, so the next blocks' loads are always in flight.
-//   Phase 1 (scores): K tile [16][128] bf16 = 4 KiB contiguous.  8 lanes per
-//     key, 16 dims (two 128-bit loads) per lane; q.k with v_dot2 bf16
-//     products accumulated in fp32, summed over the 8 lanes with DPP.  Raw
-//     scores go to LDS (the scale is applied in the softmax).
-//   Phase 2 (softmax): per head max over the partition; p = 2^((z - max)
-//     * scale * log2 e) rounded to bf16 and stored as pairs of consecutive tokens; the sum of
-//     the rounded p.  The first V tile is already loading.
-//   Phase 3 (PV): V tile [128][16] bf16 (dims major), so a 32-bit word holds
-//     two consecutive tokens of one dim: acc += v_dot2(p pair, v pair), fp32
-//     accumulation.  Lane = 4 dims x 8 tokens (four 128-bit loads).  Every
-//     128-bit load instruction of a wave reads 1 KiB of a tile contiguously.
-//   Epilogue: combine key halves and waves; a single-partition sequence
-//     writes its normalised output; otherwise the partial (max, sum, acc[d])
-//     goes to the workspace and decode_reduce merges the partitions:
-//       M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
-// The merge order depends only on logical positions, so results are
-// bitwise reproducible and independent of the physical block placement.
+// Work decomposition.  The work units are the (sequence, KV head, block)
+// triples in that order, cut into contiguous ranges by a fixed schedule of
+// shrinking sizes: 75% of the units in kCUs ranges, 15% in kCUs, 10% in
+// 2 kCUs.  One persistent 4-wave workgroup per CU (its LDS reservation
+// admits no second one) claims ranges in order from a device-wide counter,
+// so CUs and XCDs that stream faster (measured: up to ~20% apart) take more
+// of the small ranges at the end and all finish together.  Which ranges a
+// workgroup gets varies; what is computed for each range does not.
+// A range covers whole (sequence, KV head) segments, which its workgroup
+// finishes itself, and at most two pieces of segments that other ranges
+// share: those partial softmax states go to the workspace and decode_merge
+// combines them exactly:
+//   M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
+// Partial states are the only HBM writes besides the output, and while the
+// reads saturate HBM every written byte costs several read bytes, so the
+// schedule keeps them to about one per range.
+// Inside a workgroup the four waves take a piece's blocks round-robin, each
+// with its own softmax state, and merge through LDS when the piece ends.
+//
+// Per block, in a wave:
+//   S^T = K q^T with four 16x16x32 bf16 MFMAs: K tile [16][128] (rows
+//     256 B); lane (j = lane / 16, r = lane % 16) loads key r, 16-byte pieces
+//     at 64 c + 16 j, so every load instruction reads a 64-byte run of each
+//     of the 16 keys; q (the B operand, padded to 16 heads with zeros) uses
+//     the same dim order.  Lane (j, r) receives head r's scores of keys
+//     4j..4j+3.
+//   Online softmax per head (column): p = 2^(z scale log2 e - m) rounded to
+//     bf16 is already the B operand of P V; the reference m moves only when
+//     a block's maximum exceeds it by more than kLazy.
+//   O^T += V^T P^T with eight 16x16x16 bf16 MFMAs (one per 16 dims): V tile
+//     [128][16] dims major; lane (j, r) loads dim 16 t + r, keys 4j..4j+3, so
+//     every load instruction reads 512 contiguous bytes.
+// Results depend only on the logical sizes (never on the physical block
+// placement) and are bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace qw {
 
-#ifndef QW_DECODE_PART
-#define QW_DECODE_PART 512
-#endif
-#ifndef QW_DECODE_NW
-#define QW_DECODE_NW 4
-#endif
-constexpr int kPart = QW_DECODE_PART;   // tokens per partition
-constexpr int kNW = QW_DECODE_NW;       // waves per workgroup
-constexpr int kThreads = kNW * 64;
 constexpr int kBlk = 16;                // tokens per cache block
 constexpr int kD = 128;                 // head_dim
-constexpr int kPartBlocks = kPart / kBlk;
 constexpr int kMaxG = 8;
 #ifndef QW_DECODE_NBUF
-#define QW_DECODE_NBUF 2
+#define QW_DECODE_NBUF 4
 #endif
-constexpr int kNBuf = QW_DECODE_NBUF;   // blocks of K (or V) in flight per wave
+constexpr int kNBuf = QW_DECODE_NBUF;   // blocks (K and V tiles) in flight per wave
+constexpr int kNW = 4;                  // waves per workgroup, one per SIMD
+constexpr int kThreads = kNW * 64;
+constexpr int kCUs = 256;               // workgroups per round of the schedule
+constexpr int kTiers = 3;
+// the schedule: tier t takes units [U pct[t] / 100, U pct[t + 1] / 100) in
+// up to kTierWgs[t] equal ranges of at least kTierMin[t] units (by the bound
+// the host knows)
+__constant__ int kTierPct[kTiers + 1] = {0, 75, 90, 100};
+constexpr int kTierPctHost[kTiers + 1] = {0, 75, 90, 100};
+constexpr int kTierWgs[kTiers] = {kCUs, kCUs, 2 * kCUs};
+constexpr int kMaxRanges = 4 * kCUs;
+static_assert(kTierWgs[0] + kTierWgs[1] + kTierWgs[2] <= kMaxRanges, "ranges");
+constexpr int kTierMin[kTiers] = {16, 8, 8};
+constexpr int kClaimAhead = 6;          // blocks of wave 0 left when the next range is claimed
+// LDS per workgroup: the merge buffer, sized so that a CU holds one
+// workgroup (four waves, one per SIMD)
+constexpr int kLdsFloats = 21504;       // 84 KiB
+static_assert(kLdsFloats >= kNW * kMaxG * kD, "merge buffer");
+constexpr size_t kWsHeader = 256;       // the range counter; then the range descriptors, the partial states
+constexpr int kRangeEmpty = 2, kRangeFirst = 1;   // descriptor flags
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;           // log2-domain slack before the softmax reference moves
 
 // gfx9-family buffer descriptor word 3 (raw 32-bit accesses, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
@@ -64,6 +89,24 @@ __device__ __forceinline__ uint4 ld_buf16(__amdgpu_buffer_rsrc_t r, int byte_off
 }
 __device__ __forceinline__ uint2 ld_buf8(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld_buf4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+// D = A B + C on 16 x 16 tiles.  Lane (j = lane / 16, r = lane % 16) holds
+// row r of A and column r of B with the reduction elements of group j, and
+// receives rows 4j..4j+3 of column r of D.
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_16x16x16_bf16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
 
 // two E4M3FN codes (bytes 2 HI, 2 HI + 1 of w) -> a bf16 pair, exactly
@@ -81,412 +124,492 @@ struct DecodeKArgs {
   const uint16_t* q; int64_t q_stride;
   const uint8_t* k_cache; const uint8_t* v_cache; int num_blocks;   // bf16 or E4M3FN tiles
   const int32_t* block_tables; int max_blocks;
-  const int32_t* context_lens;
+  const int32_t* context_lens; int num_seqs;
   uint16_t* out; int64_t out_stride;
-  float* ws_acc;   // [S][H][max_parts][128]
-  float* ws_ml;    // [S][H][max_parts][2]  (max in log2 domain, sum)
-  int num_heads, num_kv_heads, max_parts, max_context_len;
+  float* ws_acc;   // [2 R][G][128]: partial outputs (range r: slots 2r, 2r + 1)
+  float* ws_ml;    // [2 R][G][2]:   reference max (log2 domain) and sum
+  int num_heads, num_kv_heads, max_context_len;
+  int tier_wgs[kTiers];   // ranges per tier; R = their sum
+  int num_ranges;
+  int* claim;             // range counter, zero at launch
+  int4* desc;             // per range: merge source range (-1: none), flags, segment (s, g)
   float scale_log2;   // scale * log2 e (* k_scale with an FP8 cache)
   float out_scale;    // 1, or v_scale with an FP8 cache
 };
 
-// Context length of sequence s clamped to what the grid and workspace were
-// sized for; *bad is set when the stored value breaks the contract.
-__device__ __forceinline__ int checked_ctx(const DecodeKArgs& a, int s, bool* bad) {
-  const int c = a.context_lens[s];
-  *bad = c < 1 || c > a.max_context_len;
-  return c < 1 ? 1 : (c > a.max_context_len ? a.max_context_len : c);
+// Context lengths are clamped to [1, max_context_len] (what the workspace
+// was sized for); a value outside breaks the contract and makes that
+// sequence's output NaN.
+__device__ __forceinline__ int clamp_ctx(int c, int maxc) { return c < 1 ? 1 : (c > maxc ? maxc : c); }
+__device__ __forceinline__ int nblocks_of(int c) { return (c + kBlk - 1) / kBlk; }
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), l);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
 }
 
-#ifndef QW_DECODE_WAVES
-#define QW_DECODE_WAVES 4
-#endif
+// U = Hkv * sum_s n_s (n_s = blocks of sequence s); the same in every lane
+__device__ int64_t total_units(const DecodeKArgs& a, int lane) {
+  int64_t t = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int s = base + lane;
+    const int n = s < a.num_seqs ? nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len)) : 0;
+    t += readlane64(wave_incl_scan(n, lane), 63);
+  }
+  return t * a.num_kv_heads;
+}
+
+// The unit u as (sequence s, KV head g, block b); n = blocks of s; the
+// segment of (s, g) starts at unit seg0.  Every lane gets the same values.
+struct Cursor {
+  int s, g, b, n;
+  int64_t seg0;
+};
+__device__ Cursor locate(const DecodeKArgs& a, int64_t u, int lane) {
+  const int Hkv = a.num_kv_heads;
+  int64_t run = 0;                   // blocks of the sequences before this chunk
+  Cursor c{0, 0, 0, 1, 0};
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int s = base + lane;
+    const bool in = s < a.num_seqs;
+    const int n = in ? nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len)) : 0;
+    const int64_t incl = run + wave_incl_scan(n, lane);        // blocks up to and with s
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(in && static_cast<int64_t>(Hkv) * incl > u);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      c.s = base + l;
+      c.n = __builtin_amdgcn_readlane(n, l);
+      const int64_t first = static_cast<int64_t>(Hkv) * (readlane64(incl, l) - c.n);
+      const int64_t off = u - first;
+      c.g = static_cast<int>(off / c.n);
+      c.b = static_cast<int>(off - static_cast<int64_t>(c.g) * c.n);
+      c.seg0 = first + static_cast<int64_t>(c.g) * c.n;
+      return c;
+    }
+    run = readlane64(incl, 63);
+  }
+  return c;   // not reached for u < U
+}
+
+// First unit of range r (r = R gives U).
+__device__ int64_t range_begin(const DecodeKArgs& a, int64_t r, int64_t U) {
+  int64_t first = 0;
+  for (int t = 0; t < kTiers; ++t) {
+    const int n = a.tier_wgs[t];
+    const int64_t b0 = U * kTierPct[t] / 100, b1 = U * kTierPct[t + 1] / 100;
+    if (r < first + n) return b0 + (r - first) * (b1 - b0) / n;
+    first += n;
+  }
+  return U;
+}
+// The range that holds unit u < U (ranges may be empty; this is the one
+// whose [begin, end) contains u).
+__device__ int64_t range_of(const DecodeKArgs& a, int64_t u, int64_t U) {
+  int64_t first = 0;
+  for (int t = 0; t < kTiers; ++t) {
+    const int n = a.tier_wgs[t];
+    const int64_t b0 = U * kTierPct[t] / 100, b1 = U * kTierPct[t + 1] / 100;
+    if (u < b1) return first + ((u - b0 + 1) * n - 1) / (b1 - b0);
+    first += n;
+  }
+  return first - 1;
+}
 
 // F8: the caches hold E4M3FN codes (K tile 2 KiB, V tile 2 KiB); they are
-// widened to bf16 pairs in registers and the same arithmetic follows.
+// widened to bf16 in registers and the same arithmetic follows.
 template <int G, bool F8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QW_DECODE_WAVES)))
-void decode_partial_kernel(DecodeKArgs a) {
+__global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) {
   constexpr int kEl = F8 ? 1 : 2;                 // bytes per cache element
   constexpr int kTileBytes = kBlk * kD * kEl;
-  const int r = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  bool ctx_bad;
-  const int ctx = checked_ctx(a, s, &ctx_bad);
-  const int p0 = r * kPart;
-  if (p0 >= ctx) return;
-  const int ntok = min(kPart, ctx - p0);
-  const int nblk = (ntok + kBlk - 1) / kBlk;
-  const int nparts = (ctx + kPart - 1) / kPart;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int Hkv = a.num_kv_heads;
+  const int64_t U = total_units(a, lane);
 
-  // scores [token][8 heads] (fp32); after the softmax the same space holds
-  // the per-wave partial outputs of the merge
-  __shared__ __attribute__((aligned(16))) float sc[kPart * 8];
-  // probabilities as bf16 pairs of consecutive tokens: [token pair][8 heads]
-  __shared__ __attribute__((aligned(16))) uint32_t sp2[kPart / 2 * 8];
-  __shared__ int sblk[kPartBlocks];
-  __shared__ float sred[kNW][8];
-  __shared__ float sM[8], sL[8];
-  __shared__ int sbad;
-  float (*sacc)[kMaxG * kD] = reinterpret_cast<float (*)[kMaxG * kD]>(sc);
-  static_assert(kNW * kMaxG * kD <= kPart * 8, "merge buffer must fit in the score buffer");
+  // per-wave softmax states of a piece, merged at its end
+  __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
+  float (*sacc)[kMaxG * kD] = reinterpret_cast<float (*)[kMaxG * kD]>(lds);
+  __shared__ float sm[kNW][kMaxG], sl[kNW][kMaxG];
+  __shared__ int sbad[kNW];
+  __shared__ int s_next;
 
-  if (tid == 0) sbad = ctx_bad ? 1 : 0;
+  // MFMA lane roles: lane group j4, column (query head, or row of the A
+  // operand) r16
+  const int r16 = lane & 15;
+  const int j4 = lane >> 4;
+  // K: key r16, bytes 64 c + 16 j4 of its row (bf16: c < 4; FP8: c < 2).
+  // V: dim 16 t + r16, keys 4 j4 .. 4 j4 + 3 (bf16: 8 bytes; FP8: 4 bytes).
+  constexpr int kKLoads = F8 ? 2 : 4;
+  const int koff = r16 * kD * kEl + j4 * 16;
+  const int voff = (r16 * kBlk + j4 * 4) * kEl;
+  using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
+  const float c = a.scale_log2;
+
+  // Ranges are claimed in order.  The next claim is made a few blocks before
+  // the current range ends (by thread 0), so its latency is hidden but a
+  // workgroup never holds a range it has not nearly reached.
+  if (tid == 0) s_next = atomicAdd(a.claim, 1);
   __syncthreads();
-  for (int i = tid; i < nblk; i += kThreads) {
-    int b = a.block_tables[static_cast<int64_t>(s) * a.max_blocks + (p0 / kBlk) + i];
-    if (static_cast<unsigned>(b) >= static_cast<unsigned>(a.num_blocks)) {
-      sbad = 1;
-      b = 0;
+  int rg = s_next;
+  __syncthreads();                       // every thread has read s_next
+  while (rg < a.num_ranges) {
+  int next = 0;
+  bool claimed = false;
+  const int64_t u0 = range_begin(a, rg, U), u1 = range_begin(a, rg + 1, U);
+  if (u0 >= u1) {
+    if (tid == 0) a.desc[rg] = make_int4(-1, kRangeEmpty, 0, 0);
+  } else {
+  Cursor cur = locate(a, u0, lane);
+  if (tid == 0) {
+    // the segment of this range's first piece: does this range end it after
+    // it began in an earlier range?  Then the merge combines ranges ra..rg.
+    int4 d = make_int4(-1, 0, cur.s, cur.g);
+    if (u0 > cur.seg0 && cur.seg0 + cur.n <= u1) {
+      const int64_t ra = range_of(a, cur.seg0, U);
+      d.x = static_cast<int>(ra);
+      d.y = range_begin(a, ra, U) == cur.seg0 ? kRangeFirst : 0;
     }
-    sblk[i] = b;
+    a.desc[rg] = d;
   }
-  __syncthreads();
+  int64_t u = u0;
+  bool first_piece = true;
+  while (true) {
+    // ---- one piece: blocks [b0, b0 + cnt) of segment (s, g); this wave
+    // takes blocks b0 + wave + kNW i, i < nbw ----
+    const int s = cur.s, g = cur.g, b0 = cur.b, n = cur.n;
+    const int cnt = static_cast<int>(min(static_cast<int64_t>(n - b0), u1 - u));
+    const int nbw = cnt > wave ? (cnt - wave + kNW - 1) / kNW : 0;
+    const int ctx_raw = a.context_lens[s];
+    bool bad = ctx_raw < 1 || ctx_raw > a.max_context_len;
+    const int ctx = clamp_ctx(ctx_raw, a.max_context_len);
+    const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks + b0 + wave;
 
-  // Blocks of this wave: b = wave + kNW i, i < nbw.
-  const int nbw = nblk > wave ? (nblk - wave + kNW - 1) / kNW : 0;
-  // Lane roles.  Each 128-bit load instruction of a wave reads 1 KiB of one
-  // tile contiguously.
-  //   phase 1: key kr of an 8-key round; dims 8u..8u+7 and 64+8u..64+8u+7
-  //            (FP8: dims 16u..16u+15, one 16-byte load)
-  //   phase 3: dims d0 + 32 i (i < 4); keys 8 kh .. 8 kh + 7 of the block
-  const int kr = lane >> 3;
-  const int u = lane & 7;
-  const int d0 = lane >> 1;
-  const int kh = lane & 1;
-  // Tiles are read with buffer loads through a per-tile descriptor (uniform,
-  // in SGPRs).  Every pipeline load is issued unconditionally so the number
-  // of loads in flight is static and each wait covers exactly one block; a
-  // prefetch past the wave's last block gets a zero-size descriptor, which
-  // returns zeros without touching memory.
-  auto rsrc = [&](const uint8_t* base, int i) {
-    const bool live = i < nbw;
-    const int b = uniform(sblk[wave + kNW * (live ? i : 0)]);
-    const uint8_t* t = base + (static_cast<int64_t>(b) * Hkv + g) * kTileBytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(t), static_cast<short>(0),
-                                             live ? kTileBytes : 0, kBufferFlags);
-  };
-  // byte offsets within a tile (bf16 K: key kr, dims 8u.. and 64+8u..; FP8 K:
-  // key kr, dims 16u..16u+15; V: dims d0 + 32 i, keys 8 kh..8 kh+7)
-  const int koff = F8 ? kr * kD + u * 16 : (kr * kD + u * 8) * 2;
-  const int voff = F8 ? d0 * kBlk + kh * 8 : lane * 16;
-  auto load_k = [&](int i, uint4 (&buf)[4]) {
-    const auto r = rsrc(a.k_cache, i);
+    // this wave's block ids, 64 at a time: lane i of ids_c holds its block
+    // cbase + i, of ids_n its block cbase + 64 + i
+    int cbase = 0;
+    int ids_c = lane < nbw ? bt[kNW * lane] : 0;
+    int ids_n = 64 + lane < nbw ? bt[kNW * (64 + lane)] : 0;
+
+    // q as the B operand in the dim order of the K pieces: chunk cc (32
+    // dims) of lane (j4, head r16) holds dims 32 cc + 8 j4 .. (bf16 cache) or
+    // 64 (cc / 2) + 16 j4 + 8 (cc % 2) .. (FP8 cache); padding heads are zero
+    uint4 qf[4];
+    {
+      const uint16_t* qp = a.q + static_cast<int64_t>(s) * a.q_stride +
+                           static_cast<int64_t>(g * G + r16) * kD;
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      if constexpr (F8) {
-        buf[rd] = ld_buf16(r, koff + rd * 8 * kD);
-      } else {
-        buf[2 * rd] = ld_buf16(r, koff + rd * 8 * kD * 2);
-        buf[2 * rd + 1] = ld_buf16(r, koff + rd * 8 * kD * 2 + 128);
+      for (int cc = 0; cc < 4; ++cc) {
+        const int d = F8 ? (cc >> 1) * 64 + j4 * 16 + (cc & 1) * 8 : cc * 32 + j4 * 8;
+        qf[cc] = r16 < G ? *reinterpret_cast<const uint4*>(qp + d) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
-  };
-  auto load_v = [&](int i, uint4 (&buf)[4]) {
-    const auto r = rsrc(a.v_cache, i);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      if constexpr (F8) {
-        const uint2 c = ld_buf8(r, voff + d * 32 * kBlk);
-        buf[d] = make_uint4(c.x, c.y, 0u, 0u);
-      } else {
-        buf[d] = ld_buf16(r, voff + d * 1024);
-      }
-    }
-  };
 
-  // ---------------- phase 1: raw scores q.k ----------------
-  uint4 vbuf[kNBuf][4];
-  {
-    uint4 qa[G], qb[G];
-    const uint16_t* qp = a.q + static_cast<int64_t>(s) * a.q_stride +
-                         static_cast<int64_t>(g * G) * kD + (F8 ? u * 16 : u * 8);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      qa[h] = *reinterpret_cast<const uint4*>(qp + h * kD);
-      qb[h] = *reinterpret_cast<const uint4*>(qp + h * kD + (F8 ? 8 : 64));
-    }
-    auto scores = [&](int i, const uint4 (&kbuf)[4]) {
-      const int b = wave + kNW * i;
-      const bool full = (b + 1) * kBlk <= ntok;
-#pragma unroll
-      for (int rd = 0; rd < 2; ++rd) {
-        uint4 k0, k1;
-        if constexpr (F8) {
-          k0 = fp8x8_to_bf16x8(make_uint2(kbuf[rd].x, kbuf[rd].y));
-          k1 = fp8x8_to_bf16x8(make_uint2(kbuf[rd].z, kbuf[rd].w));
-        } else {
-          k0 = kbuf[2 * rd];
-          k1 = kbuf[2 * rd + 1];
+    // Tiles are read with buffer loads through a per-tile descriptor
+    // (uniform, in SGPRs).  Every pipeline load is issued unconditionally so
+    // the number of loads in flight is static; a prefetch past the wave's
+    // last block gets a zero-size descriptor, which returns zeros without
+    // touching memory.  An id outside the pool marks the piece bad and
+    // reads block 0 instead.
+    auto issue = [&](int i, uint4 (&kb)[kKLoads], VWord (&vb)[8]) {
+      const bool live = i < nbw;
+      int id = 0;
+      if (live) {
+        const int k = i - cbase;
+        id = k < 64 ? __builtin_amdgcn_readlane(ids_c, k) : __builtin_amdgcn_readlane(ids_n, k - 64);
+        if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) {
+          bad = true;
+          id = 0;
         }
-        float acc[8];
+      }
+      const int64_t tile = (static_cast<int64_t>(id) * Hkv + g) * kTileBytes;
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
+                                                        static_cast<short>(0),
+                                                        live ? kTileBytes : 0, kBufferFlags);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
+                                                        static_cast<short>(0),
+                                                        live ? kTileBytes : 0, kBufferFlags);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float x = dot2_bf16_first(qa[h].x, k0.x);
-          x = dot2_bf16(qa[h].y, k0.y, x);
-          x = dot2_bf16(qa[h].z, k0.z, x);
-          x = dot2_bf16(qa[h].w, k0.w, x);
-          x = dot2_bf16(qb[h].x, k1.x, x);
-          x = dot2_bf16(qb[h].y, k1.y, x);
-          x = dot2_bf16(qb[h].z, k1.z, x);
-          x = dot2_bf16(qb[h].w, k1.w, x);
-          acc[h] = sum8(x);
-        }
+      for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16(rk, koff + cc * 64);
 #pragma unroll
-        for (int h = G; h < 8; ++h) acc[h] = -INFINITY;
-        const int t = b * kBlk + rd * 8 + kr;
-        if (!full) {                      // the partition's last block: keys past the context
-          if (t >= ntok) {                // (slots there may hold NaN) are excluded by select
-#pragma unroll
-            for (int h = 0; h < 8; ++h) acc[h] = -INFINITY;
-          }
-        }
-        if (u == 0) {
-          *reinterpret_cast<float4*>(&sc[t * 8]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-          *reinterpret_cast<float4*>(&sc[t * 8 + 4]) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        }
+      for (int t = 0; t < 8; ++t) {
+        if constexpr (F8)
+          vb[t] = ld_buf4(rv, voff + t * 16 * kBlk);
+        else
+          vb[t] = ld_buf8(rv, voff + t * 16 * kBlk * 2);
       }
     };
-    uint4 kbuf[kNBuf][4];
-#pragma unroll
-    for (int j = 0; j < kNBuf - 1; ++j) load_k(j, kbuf[j]);
-    for (int i = 0; i < nbw; i += kNBuf) {
-#pragma unroll
-      for (int j = 0; j < kNBuf; ++j) {
-        load_k(i + j + kNBuf - 1, kbuf[(j + kNBuf - 1) % kNBuf]);
-        if (i + j < nbw) scores(i + j, kbuf[j]);
-      }
-    }
-    // the first V tiles of this wave: in flight across the softmax phase
-#pragma unroll
-    for (int j = 0; j < kNBuf - 1; ++j) load_v(j, vbuf[j]);
-  }
-  __syncthreads();
 
-  // ---------------- phase 2: max, p (bf16 pairs), sum ----------------
-  {
-    const int h = tid & 7;
-    const int ch = tid >> 3;           // kNW * 8 chunks
-    constexpr int kCh = kNW * 8;
-    const int tend = nblk * kBlk;
-    float m = -INFINITY;
-    for (int t = ch; t < tend; t += kCh) m = fmaxf(m, sc[t * 8 + h]);
-    m = fmaxf(m, __shfl_xor(m, 8));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    if (lane < 8) sred[wave][h] = m;
-    __syncthreads();
-    if (tid < 8) {
-      float mm = sred[0][tid];
+    // Online softmax state per query head (column r16): ms is the reference
+    // maximum in the log2 domain (raw max * scale * log2 e), l the lane's
+    // share of the sum of the rounded p, acc the 16 x 128 output tile
+    // (lane: head r16, dims 16 t + 4 j4 + e).
+    float ms = -INFINITY, l = 0.0f;
+    f32x4_t acc[8];
 #pragma unroll
-      for (int w = 1; w < kNW; ++w) mm = fmaxf(mm, sred[w][tid]);
-      sM[tid] = mm;
-    }
-    __syncthreads();
-    // p = 2^((z - max) * scale * log2 e): the raw-score max is the scaled max
-    const float c = a.scale_log2;
-    const float mc = -sM[h] * c;
-    float l = 0.0f;
-    if (h < G) {
-      // the normaliser sums the rounded weights that P V will use
-      for (int j = ch; j < tend / 2; j += kCh) {
-        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[(2 * j) * 8 + h], c, mc)),
-                                       __builtin_amdgcn_exp2f(fmaf(sc[(2 * j + 1) * 8 + h], c, mc)));
-        sp2[j * 8 + h] = w;
-        l += bf16_lo(w) + bf16_hi(w);
+    for (int t = 0; t < 8; ++t) acc[t] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto block = [&](int i, const uint4 (&kb)[kKLoads], VWord (&vb)[8]) {
+      // S^T = K q^T: lane (j4, r16) gets head r16's scores of keys 4 j4 + e
+      f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        uint4 kf;
+        if constexpr (F8)
+          kf = fp8x8_to_bf16x8((cc & 1) ? make_uint2(kb[cc >> 1].z, kb[cc >> 1].w)
+                                        : make_uint2(kb[cc >> 1].x, kb[cc >> 1].y));
+        else
+          kf = kb[cc];
+        sc = mfma_16x16x32_bf16(kf, qf[cc], sc);
+      }
+      // keys past the context (slots there may hold NaN) are excluded by select
+      const int t0 = (b0 + wave + kNW * i) * kBlk + j4 * 4;
+      float z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = t0 + e < ctx ? sc[e] : -INFINITY;
+      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      // every block has a key inside the context, so bm is finite
+      const float bms = bm * c;
+      const bool up = bms > ms + kLazy;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(ms - bms) : 1.0f;
+        ms = up ? bms : ms;
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+      }
+      // p = 2^(z * scale * log2 e - ms), rounded to bf16: the B operand of
+      // P V (keys 4 j4 + e, head r16); the normaliser sums the rounded values
+      const float nm = -ms;
+      uint2 p;
+      p.x = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(z[0], c, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(z[1], c, nm)));
+      p.y = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(z[2], c, nm)),
+                        __builtin_amdgcn_exp2f(fmaf(z[3], c, nm)));
+      l += (bf16_lo(p.x) + bf16_hi(p.x)) + (bf16_lo(p.y) + bf16_hi(p.y));
+      // O^T += V^T P^T, 16 dims per MFMA
+      uint2 vf[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if constexpr (F8)
+          vf[t] = make_uint2(fp8x2_to_bf16x2<false>(vb[t]), fp8x2_to_bf16x2<true>(vb[t]));
+        else
+          vf[t] = vb[t];
+      }
+      if (t0 + 4 > ctx) {                // last block: tail slots may hold NaN
+        const uint32_t m0 = t0 >= ctx ? 0u : (t0 + 1 >= ctx ? 0xffffu : 0xffffffffu);
+        const uint32_t m1 = t0 + 2 >= ctx ? 0u : (t0 + 3 >= ctx ? 0xffffu : 0xffffffffu);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) vf[t] = make_uint2(vf[t].x & m0, vf[t].y & m1);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] = mfma_16x16x16_bf16(vf[t], p, acc[t]);
+    };
+
+    {
+      // wave 0 claims the next range kClaimAhead of its blocks before the
+      // end of the range's last piece
+      const int claim_at = u + cnt >= u1 && wave == 0 ? max(0, nbw - kClaimAhead) : -1;
+      uint4 kb[kNBuf][kKLoads];
+      VWord vb[kNBuf][8];
+#pragma unroll
+      for (int j = 0; j < kNBuf - 1; ++j) issue(j, kb[j], vb[j]);
+      for (int i = 0; i < nbw; i += kNBuf) {
+#pragma unroll
+        for (int j = 0; j < kNBuf; ++j) {
+          if (i + j == claim_at) {
+            if (lane == 0) next = atomicAdd(a.claim, 1);
+            claimed = true;
+          }
+          if (i + j == cbase + 64 && i + j < nbw) {   // next 64 ids; the window covers the prefetch
+            cbase += 64;
+            ids_c = ids_n;
+            ids_n = cbase + 64 + lane < nbw ? bt[kNW * (cbase + 64 + lane)] : 0;
+          }
+          issue(i + j + kNBuf - 1, kb[(j + kNBuf - 1) % kNBuf], vb[(j + kNBuf - 1) % kNBuf]);
+          if (i + j < nbw) block(i + j, kb[j], vb[j]);
+        }
       }
     }
-    l += __shfl_xor(l, 8);
+
+    // ---- merge of the waves' states: the piece's result ----
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (lane < 8) sred[wave][h] = l;
+    if (r16 < G) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<float4*>(&sacc[wave][r16 * kD + t * 16 + j4 * 4]) =
+            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+      if (j4 == 0) {
+        sm[wave][r16] = ms;              // -inf for a wave without blocks
+        sl[wave][r16] = l;
+      }
+    }
+    if (lane == 0) sbad[wave] = bad;
     __syncthreads();
-    if (tid < 8) {
-      float ll = 0.0f;
+    bool pbad = false;
 #pragma unroll
-      for (int w = 0; w < kNW; ++w) ll += sred[w][tid];
-      sL[tid] = ll;
-      sM[tid] *= c;                    // partition max in the log2 domain for the merge
-    }
-    // (sp2 is complete: the barrier above came after every write)
-  }
-
-  // ---------------- phase 3: P V with bf16 pairs ----------------
-  {
-    float acc[G][4];
+    for (int w = 0; w < kNW; ++w) pbad = pbad || sbad[w] != 0;
+    const bool whole = b0 == 0 && cnt == n;
+    const int64_t slot = 2 * static_cast<int64_t>(rg) + (first_piece ? 0 : 1);
+    for (int idx = tid; idx < G * kD; idx += kThreads) {
+      const int h = idx / kD, e = idx % kD;
+      float M = sm[0][h];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int w = 1; w < kNW; ++w) M = fmaxf(M, sm[w][h]);
+      float v = 0.0f, L = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[h][i] = 0.0f;
-    auto pv = [&](int i, uint4 (&vr)[4]) {
-      const int b = wave + kNW * i;
-      if constexpr (F8) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) vr[d] = fp8x8_to_bf16x8(make_uint2(vr[d].x, vr[d].y));
+      for (int w = 0; w < kNW; ++w) {
+        const float wt = __builtin_amdgcn_exp2f(sm[w][h] - M);   // 0 for a wave without blocks
+        v = fmaf(sacc[w][idx], wt, v);
+        L = fmaf(sl[w][h], wt, L);
       }
-      const int pair0 = (b * kBlk + kh * 8) / 2;     // first token pair of this lane half
-      if ((b + 1) * kBlk > ntok) {                   // last block: tail slots may hold NaN
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint32_t* w = reinterpret_cast<uint32_t*>(&vr[d]);
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const int t0 = 2 * (pair0 + pp);
-            w[pp] = t0 >= ntok ? 0u : (t0 + 1 >= ntok ? (w[pp] & 0xffffu) : w[pp]);
-          }
+      if (whole) {                       // the whole segment: final output
+        const int qh = g * G + h;
+        a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
+            f32_to_bf16(pbad ? __builtin_nanf("") : v * a.out_scale / L);
+      } else {                           // a share of the segment: partial state
+        a.ws_acc[(slot * G + h) * kD + e] = v;
+        if (e == 0) {
+          a.ws_ml[(slot * G + h) * 2] = M;
+          a.ws_ml[(slot * G + h) * 2 + 1] = pbad ? __builtin_nanf("") : L;
         }
       }
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const uint4 plo = *reinterpret_cast<const uint4*>(&sp2[(pair0 + pp) * 8]);
-        const uint4 phi = *reinterpret_cast<const uint4*>(&sp2[(pair0 + pp) * 8 + 4]);
-        const uint32_t p[8] = {plo.x, plo.y, plo.z, plo.w, phi.x, phi.y, phi.z, phi.w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t w = pp == 0 ? vr[d].x : pp == 1 ? vr[d].y : pp == 2 ? vr[d].z : vr[d].w;
-#pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][d] = dot2_bf16(p[h], w, acc[h][d]);
-        }
-      }
-    };
-    for (int i = 0; i < nbw; i += kNBuf) {
-#pragma unroll
-      for (int j = 0; j < kNBuf; ++j) {
-        load_v(i + j + kNBuf - 1, vbuf[(j + kNBuf - 1) % kNBuf]);
-        if (i + j < nbw) pv(i + j, vbuf[j]);
-      }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[h][i] += dpp<kDppXor1>(acc[h][i]);   // the other key half
-    // sc (aliased by sacc) is no longer read by anyone: phase 2 ended with a barrier
-    if (kh == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[wave][h * kD + d0 + 32 * i] = acc[h][i];
+    u += cnt;
+    if (u >= u1) break;
+    __syncthreads();                     // the merge buffers are reused by the next piece
+    first_piece = false;
+    cur.b = 0;
+    if (++cur.g == Hkv) {
+      cur.g = 0;
+      ++cur.s;
+      cur.n = nblocks_of(clamp_ctx(a.context_lens[cur.s], a.max_context_len));
     }
   }
-  __syncthreads();
-
-  // ---------------- epilogue ----------------
-  const bool bad = sbad != 0;
-  for (int idx = tid; idx < G * kD; idx += kThreads) {
-    const int h = idx / kD, e = idx % kD;
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) v += sacc[w][idx];
-    if (bad) v = __builtin_nanf("");
-    const int qh = g * G + h;
-    if (nparts == 1) {
-      a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
-          f32_to_bf16(v * a.out_scale / sL[h]);
-    } else {
-      a.ws_acc[((static_cast<int64_t>(s) * a.num_heads + qh) * a.max_parts + r) * kD + e] = v;
-    }
   }
-  if (nparts > 1 && tid < G) {
-    const int qh = g * G + tid;
-    float* ml = a.ws_ml + ((static_cast<int64_t>(s) * a.num_heads + qh) * a.max_parts + r) * 2;
-    ml[0] = sM[tid];
-    ml[1] = bad ? __builtin_nanf("") : sL[tid];
+  if (tid == 0) s_next = claimed ? next : atomicAdd(a.claim, 1);
+  __syncthreads();                       // s_next is written; the merge buffers are free
+  rg = s_next;
+  __syncthreads();                       // every thread has read s_next
   }
 }
 
-// Merge of the partitions: one 128-thread workgroup per (query head,
-// sequence), one output element per thread.  Partitions are taken 64 at a
-// time: their (m, l) pairs go to LDS in one round of loads, the weights
-// 2^(m_r - M) follow from the running maximum, and every thread issues the
-// loads of its 64 partial sums back to back, so the merge pays a few memory
-// latencies instead of one per partition.
-constexpr int kMergeBatch = 64;
-
-__global__ __launch_bounds__(128) void decode_reduce_kernel(DecodeKArgs a) {
-  const int qh = blockIdx.x, s = blockIdx.y, e = threadIdx.x;
-  bool ctx_bad;
-  const int ctx = checked_ctx(a, s, &ctx_bad);
-  const int nparts = (ctx + kPart - 1) / kPart;
-  if (nparts <= 1) return;
-  __shared__ float sm[kMergeBatch], sl[kMergeBatch];
-  __shared__ float sred[2];
-  const int64_t base = static_cast<int64_t>(s) * a.num_heads + qh;
-  const float* ml = a.ws_ml + base * a.max_parts * 2;
-  const float* acc = a.ws_acc + base * a.max_parts * kD + e;
-
-  float M = -INFINITY, L = 0.0f, o = 0.0f;      // running over batches (uniform)
-  for (int c0 = 0; c0 < nparts; c0 += kMergeBatch) {
-    const int cn = min(kMergeBatch, nparts - c0);
-    float x[kMergeBatch];
+// Merge of the shared segments.  Range r's descriptor names, when r's first
+// piece ends a segment that began in an earlier range r_a, that segment and
+// r_a.  Its pieces are the partial states of ranges r_a..r: r_a's piece is
+// in slot 2 r_a if the segment is r_a's first, else 2 r_a + 1; every later
+// non-empty range's piece is its first (slot 2 r'); empty ranges have none.
+//   M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
+// Workgroup r, one thread per (head, dim).  The merge is bound by memory
+// latency, so pieces are taken 16 at a time with every load of a batch (the
+// ranges' empty flags, (m, l), the partial outputs) in flight together, and
+// the running sums are rescaled when the maximum moves.
+constexpr int kMergeBatch = 16;
+template <int G>
+__global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int4 d = a.desc[r];
+  if (d.x < 0) return;
+  const int ra = d.x;
+  const bool ra_first = (d.y & kRangeFirst) != 0;
+  const int np = r - ra + 1;
+  const int h = tid / kD, e = tid % kD;
+  float M = -INFINITY, L = 0.0f, o = 0.0f;
+  for (int x0 = 0; x0 < np; x0 += kMergeBatch) {
+    float pm[kMergeBatch], pl[kMergeBatch], v[kMergeBatch];
+    bool live[kMergeBatch];
 #pragma unroll
-    for (int r = 0; r < kMergeBatch; ++r) x[r] = r < cn ? acc[static_cast<int64_t>(c0 + r) * kD] : 0.0f;
-    if (e < cn) {
-      sm[e] = ml[2 * (c0 + e)];
-      sl[e] = ml[2 * (c0 + e) + 1];
+    for (int q = 0; q < kMergeBatch; ++q) {
+      const int x = x0 + q;
+      const int rx = ra + (x < np ? x : 0);
+      const int64_t sb = static_cast<int64_t>(2 * rx + (x == 0 && !ra_first ? 1 : 0)) * G + h;
+      live[q] = x < np && (x == 0 || (a.desc[rx].y & kRangeEmpty) == 0);
+      pm[q] = a.ws_ml[sb * 2];
+      pl[q] = a.ws_ml[sb * 2 + 1];
+      v[q] = a.ws_acc[sb * kD + e];
     }
-    __syncthreads();
-    if (e < 64) {                                // wave 0: batch max
-      float mb = e < cn ? sm[e] : -INFINITY;
-      mb = wave_max(mb);
-      if (e == 0) sred[0] = mb;
-    }
-    __syncthreads();
-    const float Mn = fmaxf(M, sred[0]);
-    const float alpha = M > -INFINITY ? __builtin_amdgcn_exp2f(M - Mn) : 0.0f;
-    float lb = 0.0f, ob = 0.0f;
+    float Mc = M;
 #pragma unroll
-    for (int r = 0; r < kMergeBatch; ++r) {
-      if (r < cn) {
-        const float w = __builtin_amdgcn_exp2f(sm[r] - Mn);
-        lb = fmaf(sl[r], w, lb);
-        ob = fmaf(x[r], w, ob);
+    for (int q = 0; q < kMergeBatch; ++q)
+      if (live[q]) Mc = fmaxf(Mc, pm[q]);
+    if (Mc > M) {                        // rescale the running sums (M = -inf: they are 0)
+      const float f = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+      L *= f;
+      o *= f;
+      M = Mc;
+    }
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      if (live[q]) {
+        const float wt = __builtin_amdgcn_exp2f(pm[q] - M);
+        L = fmaf(pl[q], wt, L);
+        o = fmaf(v[q], wt, o);
       }
     }
-    L = fmaf(L, alpha, lb);
-    o = fmaf(o, alpha, ob);
-    M = Mn;
-    __syncthreads();                             // sm/sl reused by the next batch
   }
-  a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
-      f32_to_bf16(ctx_bad ? __builtin_nanf("") : o * a.out_scale / L);
+  a.out[static_cast<int64_t>(d.z) * a.out_stride + static_cast<int64_t>(d.w * G + h) * kD + e] =
+      f32_to_bf16(o * a.out_scale / L);
+}
+
+// zero the range counter
+__global__ void decode_claim_reset_kernel(int* claim) {
+  if (threadIdx.x == 0) *claim = 0;
+}
+
+static size_t desc_bytes(int num_ranges) { return (static_cast<size_t>(num_ranges) * 16 + 255) / 256 * 256; }
+
+// ranges per tier for a batch of at most umax units
+static void decode_schedule(int num_seqs, int max_context_len, int num_kv_heads, int (&wgs)[kTiers]) {
+  const int64_t umax = static_cast<int64_t>(num_kv_heads) * num_seqs *
+                       ((static_cast<int64_t>(max_context_len) + kBlk - 1) / kBlk);
+  for (int t = 0; t < kTiers; ++t) {
+    const int64_t share = umax * (kTierPctHost[t + 1] - kTierPctHost[t]) / 100;
+    const int64_t n = (share + kTierMin[t] - 1) / kTierMin[t];
+    wgs[t] = static_cast<int>(n < 1 ? 1 : (n > kTierWgs[t] ? kTierWgs[t] : n));
+  }
 }
 
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
                        int head_dim, int block_size, int dtype, int cache_fp8) {
-  (void)cache_fp8;                    // both cache formats have the split-K kernel
+  (void)cache_fp8;                    // both cache formats have the stream kernel
   DecodePlan p{};
   const int G = num_heads / num_kv_heads;
   p.fast = dtype == kBF16 && head_dim == kD && block_size == kBlk && G >= 1 && G <= kMaxG;
-  if (!p.fast) {
-    p.ws_bytes = 0;
-    return p;
-  }
-  p.part_tokens = kPart;
-  p.max_parts = (max_context_len + kPart - 1) / kPart;
-  if (p.max_parts <= 1) {
-    p.ws_bytes = 0;
-    return p;
-  }
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * p.max_parts;
-  p.ws_bytes = rows * kD * sizeof(float) + rows * 2 * sizeof(float);
+  if (!p.fast) return p;
+  int wgs[kTiers];
+  decode_schedule(num_seqs, max_context_len, num_kv_heads, wgs);
+  p.num_ranges = wgs[0] + wgs[1] + wgs[2];
+  p.ws_bytes = kWsHeader + desc_bytes(p.num_ranges) +
+               static_cast<size_t>(2) * p.num_ranges * G * (kD + 2) * sizeof(float);
   return p;
 }
 
 template <int G>
-static void launch_partial(const DecodeKArgs& k, const AttnArgs& a, const DecodePlan& p,
-                           hipStream_t stream) {
-  const dim3 grid(p.max_parts, a.num_kv_heads, a.num_seqs);
+static void launch_stream(const DecodeKArgs& k, const AttnArgs& a, hipStream_t stream) {
+  const int grid = k.num_ranges < kCUs ? k.num_ranges : kCUs;
+  hipLaunchKernelGGL(decode_claim_reset_kernel, dim3(1), dim3(64), 0, stream, k.claim);
   if (a.cache_fp8)
-    hipLaunchKernelGGL((decode_partial_kernel<G, true>), grid, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_stream_kernel<G, true>), dim3(grid), dim3(kThreads), 0, stream, k);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<G, false>), grid, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_stream_kernel<G, false>), dim3(grid), dim3(kThreads), 0, stream, k);
+  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(k.num_ranges), dim3(G * kD), 0, stream, k);
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t stream) {
   if (!p.fast) return launch_attn_generic(a, stream);
+  const int G = a.num_heads / a.num_kv_heads;
   DecodeKArgs k{};
   k.q = static_cast<const uint16_t*>(a.q);
   k.q_stride = a.q_stride;
@@ -496,33 +619,31 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
   k.block_tables = a.block_tables;
   k.max_blocks = a.max_blocks;
   k.context_lens = a.context_lens;
+  k.num_seqs = a.num_seqs;
   k.out = static_cast<uint16_t*>(a.out);
   k.out_stride = a.out_stride;
   k.num_heads = a.num_heads;
   k.num_kv_heads = a.num_kv_heads;
-  k.max_parts = p.max_parts;
   k.max_context_len = a.max_context_len;
+  decode_schedule(a.num_seqs, a.max_context_len, a.num_kv_heads, k.tier_wgs);
+  k.num_ranges = k.tier_wgs[0] + k.tier_wgs[1] + k.tier_wgs[2];
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
-  if (p.max_parts > 1) {
-    const size_t rows = static_cast<size_t>(a.num_seqs) * a.num_heads * p.max_parts;
-    k.ws_acc = static_cast<float*>(a.workspace);
-    k.ws_ml = k.ws_acc + rows * kD;
-  }
-  const int G = a.num_heads / a.num_kv_heads;
+  k.claim = static_cast<int*>(a.workspace);
+  k.desc = reinterpret_cast<int4*>(static_cast<uint8_t*>(a.workspace) + kWsHeader);
+  k.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + kWsHeader +
+                                      desc_bytes(k.num_ranges));
+  k.ws_ml = k.ws_acc + static_cast<size_t>(2) * k.num_ranges * G * kD;
   switch (G) {
-    case 1: launch_partial<1>(k, a, p, stream); break;
-    case 2: launch_partial<2>(k, a, p, stream); break;
-    case 3: launch_partial<3>(k, a, p, stream); break;
-    case 4: launch_partial<4>(k, a, p, stream); break;
-    case 5: launch_partial<5>(k, a, p, stream); break;
-    case 6: launch_partial<6>(k, a, p, stream); break;
-    case 7: launch_partial<7>(k, a, p, stream); break;
-    default: launch_partial<8>(k, a, p, stream); break;
+    case 1: launch_stream<1>(k, a, stream); break;
+    case 2: launch_stream<2>(k, a, stream); break;
+    case 3: launch_stream<3>(k, a, stream); break;
+    case 4: launch_stream<4>(k, a, stream); break;
+    case 5: launch_stream<5>(k, a, stream); break;
+    case 6: launch_stream<6>(k, a, stream); break;
+    case 7: launch_stream<7>(k, a, stream); break;
+    default: launch_stream<8>(k, a, stream); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_parts <= 1) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.num_heads, a.num_seqs), dim3(kD), 0, stream, k);
   return hipGetLastError();
 }
 

@@ -46,9 +46,8 @@ struct AttnArgs {
 
 // decode plan: which kernel runs and how much workspace it needs
 struct DecodePlan {
-  bool fast;          // split-K bf16 kernel (else the generic kernel)
-  int part_tokens;    // tokens per partition
-  int max_parts;      // partitions of the longest context
+  bool fast;          // stream-split bf16 kernel (else the generic kernel)
+  int num_ranges;     // workgroups (ranges of work units) of the stream kernel
   size_t ws_bytes;
 };
 

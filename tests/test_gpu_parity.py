@@ -105,6 +105,11 @@ SMALL = [
     ("decode_g2", "bf16", 16, 8, 128, [129, 2048, 1], [1] * 3, 0),
     ("decode_g4", "bf16", 16, 4, 128, [1000, 33], [1] * 2, 0),
     ("decode_g8", "bf16", 32, 4, 128, [777, 1500], [1] * 2, 0),
+    # one 32k-token sequence on one KV head: its segment is cut into more
+    # than 128 pieces, so their merge runs in several chunks
+    ("decode_one_long_segment", "bf16", 8, 1, 128, [32768], [1], 0),
+    # many short sequences: most ranges hold several whole segments
+    ("decode_many_short", "bf16", 28, 4, 128, list(range(1, 400, 7)), [1] * 57, 0),
     ("decode_g16_generic", "bf16", 32, 2, 128, [600, 40], [1] * 2, 0),
     ("decode_d64_generic", "bf16", 8, 2, 64, [70, 530], [1] * 2, 0),
     ("decode_f32", "f32", 8, 2, 128, [70, 530], [1] * 2, 0),
