@@ -63,14 +63,16 @@ constexpr int kThreads = kNW * 64;
 constexpr int kCUs = 256;               // workgroups per round of the schedule
 constexpr int kTiers = 3;
 // the schedule: tier t takes units [U pct[t] / 100, U pct[t + 1] / 100) in
-// up to kTierWgs[t] equal ranges of at least kTierMin[t] units (by the bound
-// the host knows)
+// equal ranges of at least kTierMin[t] units, at most kTierWgs[t] of them
+// (the host sizes the workspace for the bound it knows; the kernels count
+// the ranges for the actual U)
 __constant__ int kTierPct[kTiers + 1] = {0, 75, 90, 100};
 constexpr int kTierPctHost[kTiers + 1] = {0, 75, 90, 100};
 constexpr int kTierWgs[kTiers] = {kCUs, kCUs, 2 * kCUs};
 constexpr int kMaxRanges = 4 * kCUs;
 static_assert(kTierWgs[0] + kTierWgs[1] + kTierWgs[2] <= kMaxRanges, "ranges");
-constexpr int kTierMin[kTiers] = {16, 8, 8};
+__constant__ int kTierMin[kTiers] = {64, 32, 24};
+constexpr int kTierMinHost[kTiers] = {64, 32, 24};
 constexpr int kClaimAhead = 6;          // blocks of wave 0 left when the next range is claimed
 // LDS per workgroup: the merge buffer, sized so that a CU holds one
 // workgroup (four waves, one per SIMD)
@@ -129,7 +131,7 @@ struct DecodeKArgs {
   float* ws_acc;   // [2 R][G][128]: partial outputs (range r: slots 2r, 2r + 1)
   float* ws_ml;    // [2 R][G][2]:   reference max (log2 domain) and sum
   int num_heads, num_kv_heads, max_context_len;
-  int tier_wgs[kTiers];   // ranges per tier; R = their sum
+  int tier_wgs[kTiers];   // most ranges per tier (for the host's bound on U); R = their sum
   int num_ranges;
   int* claim;             // range counter, zero at launch
   int4* desc;             // per range: merge source range (-1: none), flags, segment (s, g)
@@ -200,11 +202,27 @@ __device__ Cursor locate(const DecodeKArgs& a, int64_t u, int lane) {
   return c;   // not reached for u < U
 }
 
+// The ranges per tier for the batch's U units.
+struct Schedule {
+  int n[kTiers];
+  int R;
+};
+__device__ Schedule schedule_for(const DecodeKArgs& a, int64_t U) {
+  Schedule sc;
+  sc.R = 0;
+  for (int t = 0; t < kTiers; ++t) {
+    const int64_t share = U * kTierPct[t + 1] / 100 - U * kTierPct[t] / 100;
+    const int64_t n = (share + kTierMin[t] - 1) / kTierMin[t];
+    sc.n[t] = static_cast<int>(n < 1 ? 1 : (n > a.tier_wgs[t] ? a.tier_wgs[t] : n));
+    sc.R += sc.n[t];
+  }
+  return sc;
+}
 // First unit of range r (r = R gives U).
-__device__ int64_t range_begin(const DecodeKArgs& a, int64_t r, int64_t U) {
+__device__ int64_t range_begin(const Schedule& sc, int64_t r, int64_t U) {
   int64_t first = 0;
   for (int t = 0; t < kTiers; ++t) {
-    const int n = a.tier_wgs[t];
+    const int n = sc.n[t];
     const int64_t b0 = U * kTierPct[t] / 100, b1 = U * kTierPct[t + 1] / 100;
     if (r < first + n) return b0 + (r - first) * (b1 - b0) / n;
     first += n;
@@ -213,10 +231,10 @@ __device__ int64_t range_begin(const DecodeKArgs& a, int64_t r, int64_t U) {
 }
 // The range that holds unit u < U (ranges may be empty; this is the one
 // whose [begin, end) contains u).
-__device__ int64_t range_of(const DecodeKArgs& a, int64_t u, int64_t U) {
+__device__ int64_t range_of(const Schedule& sc, int64_t u, int64_t U) {
   int64_t first = 0;
   for (int t = 0; t < kTiers; ++t) {
-    const int n = a.tier_wgs[t];
+    const int n = sc.n[t];
     const int64_t b0 = U * kTierPct[t] / 100, b1 = U * kTierPct[t + 1] / 100;
     if (u < b1) return first + ((u - b0 + 1) * n - 1) / (b1 - b0);
     first += n;
@@ -235,6 +253,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   const int wave = uniform(tid >> 6);
   const int Hkv = a.num_kv_heads;
   const int64_t U = total_units(a, lane);
+  const Schedule sched = schedule_for(a, U);
+  if (blockIdx.x == 0 && tid == 0) a.claim[1] = sched.R;   // for the merge kernel
 
   // per-wave softmax states of a piece, merged at its end
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
@@ -262,10 +282,10 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   __syncthreads();
   int rg = s_next;
   __syncthreads();                       // every thread has read s_next
-  while (rg < a.num_ranges) {
+  while (rg < sched.R) {
   int next = 0;
   bool claimed = false;
-  const int64_t u0 = range_begin(a, rg, U), u1 = range_begin(a, rg + 1, U);
+  const int64_t u0 = range_begin(sched, rg, U), u1 = range_begin(sched, rg + 1, U);
   if (u0 >= u1) {
     if (tid == 0) a.desc[rg] = make_int4(-1, kRangeEmpty, 0, 0);
   } else {
@@ -275,9 +295,9 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
     // it began in an earlier range?  Then the merge combines ranges ra..rg.
     int4 d = make_int4(-1, 0, cur.s, cur.g);
     if (u0 > cur.seg0 && cur.seg0 + cur.n <= u1) {
-      const int64_t ra = range_of(a, cur.seg0, U);
+      const int64_t ra = range_of(sched, cur.seg0, U);
       d.x = static_cast<int>(ra);
-      d.y = range_begin(a, ra, U) == cur.seg0 ? kRangeFirst : 0;
+      d.y = range_begin(sched, ra, U) == cur.seg0 ? kRangeFirst : 0;
     }
     a.desc[rg] = d;
   }
@@ -520,6 +540,7 @@ constexpr int kMergeBatch = 16;
 template <int G>
 __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
   const int r = blockIdx.x, tid = threadIdx.x;
+  if (r >= a.claim[1]) return;           // ranges of this batch: written by the stream kernel
   const int4 d = a.desc[r];
   if (d.x < 0) return;
   const int ra = d.x;
@@ -576,7 +597,7 @@ static void decode_schedule(int num_seqs, int max_context_len, int num_kv_heads,
                        ((static_cast<int64_t>(max_context_len) + kBlk - 1) / kBlk);
   for (int t = 0; t < kTiers; ++t) {
     const int64_t share = umax * (kTierPctHost[t + 1] - kTierPctHost[t]) / 100;
-    const int64_t n = (share + kTierMin[t] - 1) / kTierMin[t];
+    const int64_t n = (share + kTierMinHost[t] - 1) / kTierMinHost[t];
     wgs[t] = static_cast<int>(n < 1 ? 1 : (n > kTierWgs[t] ? kTierWgs[t] : n));
   }
 }
