@@ -282,7 +282,7 @@ def main():
         "tokens_per_s": round(b.num_seqs / (dec["step_ms"] * 1e-3), 1),
         "wall_ms_per_step": round(dec["wall_ms"], 4),
         "roofline": {
-            "kernel": "qwen2_attn_decode_paged (split-K partial + merge)",
+            "kernel": "qwen2_attn_decode_paged (counter reset + stream + merge)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

@@ -55,7 +55,7 @@ constexpr int kBlk = 16;                // tokens per cache block
 constexpr int kD = 128;                 // head_dim
 constexpr int kMaxG = 8;
 #ifndef QW_DECODE_NBUF
-#define QW_DECODE_NBUF 4
+#define QW_DECODE_NBUF 3
 #endif
 constexpr int kNBuf = QW_DECODE_NBUF;   // blocks (K and V tiles) in flight per wave
 constexpr int kNW = 4;                  // waves per workgroup, one per SIMD
@@ -611,7 +611,8 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   if (!p.fast) return p;
   int wgs[kTiers];
   decode_schedule(num_seqs, max_context_len, num_kv_heads, wgs);
-  p.num_ranges = wgs[0] + wgs[1] + wgs[2];
+  p.num_ranges = 0;
+  for (int t = 0; t < kTiers; ++t) p.num_ranges += wgs[t];
   p.ws_bytes = kWsHeader + desc_bytes(p.num_ranges) +
                static_cast<size_t>(2) * p.num_ranges * G * (kD + 2) * sizeof(float);
   return p;
@@ -647,7 +648,8 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
   k.num_kv_heads = a.num_kv_heads;
   k.max_context_len = a.max_context_len;
   decode_schedule(a.num_seqs, a.max_context_len, a.num_kv_heads, k.tier_wgs);
-  k.num_ranges = k.tier_wgs[0] + k.tier_wgs[1] + k.tier_wgs[2];
+  k.num_ranges = 0;
+  for (int t = 0; t < kTiers; ++t) k.num_ranges += k.tier_wgs[t];
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
   k.claim = static_cast<int*>(a.workspace);
