@@ -5,8 +5,8 @@
 Headline workload: Qwen2-7B-shaped long-context paged decode, bf16 (28 query
 heads, 4 KV heads, head_dim 128, block 16, batch 64, contexts log-uniform in
 [2048, 32768]).  One step = qwen2_rope_cache_write of the 64 new tokens (rotate
-q/k, write k/v into the paged cache) + qwen2_attn_decode_paged (split-K
-partial kernel + merge kernel).  ``value`` is KV bytes read per step divided
+q/k, write k/v into the paged cache) + qwen2_attn_decode_paged (counter
+reset + stream kernel + merge kernel).  ``value`` is KV bytes read per step divided
 by the step time (GB/s), inputs resident in HBM.  The K timed steps are
 captured in one HIP graph and replayed once between HIP events on the
 launching stream, so the figures are GPU time without the Python call cost;
@@ -14,8 +14,9 @@ per-call figures come from graphs of K calls of that call alone.  The KV pool (~
 larger than the 256 MB last-level cache, so every step streams KV from HBM.
 
 Also reported on the same line: Qwen2-7B varlen causal prefill (8 sequences
-of 128..512 tokens) TFLOP/s, and the mixed TP=2-share batch in tokens/s, plus
-the roofline of the dominant decode kernel and the CPU oracle baseline.
+of 128..512 tokens) TFLOP/s, the mixed TP=2-share batch in tokens/s, the long
+decode over an FP8 E4M3FN cache, the Qwen3 q/k-norm cache write, plus the
+roofline of the decode call and the CPU oracle baseline.
 Prints one JSON line.
 """
 from __future__ import annotations

@@ -173,11 +173,14 @@ size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int n
  * (q_row_stride) sits at position context_lens[s] - 1 and attends to all
  * context_lens[s] keys of sequence s (its own key included: write it with
  * qwen2_rope_cache_write first).  out [num_seqs][num_heads][head_dim]
- * (out_row_stride) is written.  Long contexts are split into partitions
- * whose partial softmax states are merged exactly (log-sum-exp) in a second
- * pass; workspace (device, workspace_bytes >=
- * qwen2_attn_decode_workspace_size(...)) holds those partial states and is
- * scratch: its contents on entry do not matter.
+ * (out_row_stride) is written.  The batch's (sequence, KV head, block)
+ * units are spread evenly over the GPU: a sequence may be cut into pieces
+ * whose partial softmax states are merged exactly (log-sum-exp, in a fixed
+ * order, so results are bitwise reproducible) by a second kernel; workspace
+ * (device, 16-byte aligned, workspace_bytes >=
+ * qwen2_attn_decode_workspace_size(...)) holds a work counter and those
+ * partial states and is scratch: its contents on entry do not matter.
+ * Calls that share one workspace must not overlap.
  * "vLLM 部署 Qwen", §2.1 and §4.1 (paged KV access dominates decode).
  */
 int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride,

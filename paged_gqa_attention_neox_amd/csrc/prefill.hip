@@ -8,18 +8,20 @@
 // Qwen", §2.1).
 //
 // bf16, head_dim 128, block 16, group G <= 8:
-//   * one workgroup per (KV head, 16-row query tile, sequence).  A wave owns
-//     32 query columns = 2 heads of the group x 16 rows (an odd group pads
-//     its last wave with a copy of the last head, whose output is dropped);
-//     the workgroup holds two such sets of ceil(G/2) waves, the two key
-//     groups;
-//   * keys stream in super-tiles of 64 (four cache blocks): key group k takes
-//     keys 32k .. 32k + 31 of each.  The two groups' online-softmax states
-//     are merged through LDS at the end, so a query tile's keys are covered
-//     in half the steps of a single group;
-//   * super-tiles (32 KiB of K and V^T) go through a ring of four LDS stages
-//     with direct-to-LDS buffer loads (no register staging), two super-tiles
-//     ahead.  Each wave issues the same number of 1 KiB loads per super-tile
+//   * one workgroup per (KV head, query tile, sequence), in one of two
+//     layouts chosen per launch by a cost estimate (key_groups below):
+//     - one key group: G waves, a wave owns 32 query columns = one head of
+//       the group x 32 rows, keys in steps of 32;
+//     - two key groups: a wave owns 32 columns = 2 heads x 16 rows (an odd
+//       group pads its last wave with a copy of the last head, whose output
+//       is dropped); the workgroup holds two sets of ceil(G/2) waves, and
+//       keys stream in steps of 64 (four cache blocks) of which key group k
+//       takes keys 32k .. 32k + 31.  The two groups' online-softmax states
+//       are merged through LDS at the end, so a query tile's keys are
+//       covered in half the steps (short tiles, long contexts);
+//   * steps (16 or 32 KiB of K and V^T) go through a ring of four LDS stages
+//     with direct-to-LDS buffer loads (no register staging), three steps
+//     ahead.  Each wave issues the same number of 1 KiB loads per step
 //     (surplus ones have an empty range and land in a scratch line), so its
 //     outstanding-load count at every wait is a compile-time constant;
 //   * the block ids the workgroup needs are staged in LDS once, so no load
