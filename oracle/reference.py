@@ -25,6 +25,8 @@ Where the pages are silent the plainest reading is taken (each one is listed
 with the function that uses it):
   * NeoX pairing: element i is rotated with element i + d/2 (half split);
   * frequency law f_i = theta ** (-2 i / d), i < d/2;
+  * dynamic-NTK rope scaling ([P2] §7.1, [P1] §3): a larger base for a
+    table of factor * original_max_position positions (rope_dynamic_ntk);
   * slot = physical_block * block_size + offset, slot < 0 means "skip";
   * query row i of a sequence with n new rows and context c sits at
     position c - n + i and sees keys 0..c-n+i (bottom-right causal);
@@ -55,7 +57,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "rope_inv_freq", "rope_neox", "to_f64", "from_f64", "f64_to_bf16_bits",
+    "rope_inv_freq", "rope_dynamic_ntk", "rope_neox", "to_f64", "from_f64", "f64_to_bf16_bits",
     "bf16_bits_to_f64", "rope_cache_write", "gather_kv", "causal_visible",
     "softmax_rows", "kv_head_for", "default_scale", "attention_varlen",
     "attention_decode", "run_step", "fp8_e4m3_decode", "fp8_e4m3_encode", "E4M3_MAX",
@@ -126,6 +128,28 @@ def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
     one for a given base."""
     i = np.arange(head_dim // 2, dtype=np.float64)
     return np.power(float(theta), -2.0 * i / float(head_dim))
+
+
+def rope_dynamic_ntk(theta: float, head_dim: int, factor: float, original_max_position: int):
+    """Dynamic-NTK rope scaling: (scaled base, table length).
+
+    [P2] §7.1 gives the setting {"type": "dynamic", "factor": 2.0,
+    "original_max_position": 4096} and says it raises the RoPE base
+    frequency so that longer contexts fit while short ones keep their
+    behaviour; [P1] §3: vLLM hands rope_scaling to get_rope, and Qwen2 needs
+    it past its native 32768 positions.  The pages print no formula.  Reading
+    taken (the published NTK-aware rule, as vLLM's get_rope uses it): one
+    table covers L = factor * original_max_position positions, and the base
+    becomes
+        theta' = theta * (factor * L / original - (factor - 1)) ** (d / (d - 2))
+    so the slowest rotation (i = d/2 - 1) turns factor * L / original -
+    (factor - 1) times slower while the fastest (i = 0) is unchanged.  With
+    factor 1 nothing changes."""
+    s = float(factor)
+    L = int(s * int(original_max_position))
+    d = float(head_dim)
+    base = float(theta) * (s * L / float(original_max_position) - (s - 1.0)) ** (d / (d - 2.0))
+    return base, L
 
 
 def rope_neox(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:

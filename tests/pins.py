@@ -570,8 +570,29 @@ def pin_qk_norm_in_cache_write(R):
     want = np.sqrt(((x / np.sqrt((x * x).mean(-1, keepdims=True)) * w) ** 2).sum(-1))
     assert np.allclose(np.sqrt((q2.astype(np.float64) ** 2).sum(-1)), want, rtol=1e-6)
 
+def pin_dynamic_ntk_closed_forms(R):
+    """Dynamic-NTK scaling: factor 1 changes nothing; the table spans factor x
+    original positions; the fastest frequency is unchanged and the slowest
+    one is divided by exactly factor * L / original - (factor - 1) =
+    factor^2 - factor + 1 (the d / (d - 2) exponent makes it exact); the
+    [P2] §7.1 setting (factor 2 over 4096) gives base 1e6 * 3^(128/126)."""
+    for d in (64, 128):
+        base, L = R.rope_dynamic_ntk(1e6, d, 1.0, 32768)
+        assert base == 1e6 and L == 32768
+        for s, L0 in ((2.0, 4096), (4.0, 32768), (3.0, 1000)):
+            base, L = R.rope_dynamic_ntk(1e6, d, s, L0)
+            assert L == int(s * L0)
+            f0, f1 = R.rope_inv_freq(d, 1e6), R.rope_inv_freq(d, base)
+            assert f1[0] == f0[0] == 1.0
+            np.testing.assert_allclose(f0[-1] / f1[-1], s * s - s + 1.0, rtol=1e-12)
+            assert np.all(f1[1:] < f0[1:])
+    base, L = R.rope_dynamic_ntk(1e6, 128, 2.0, 4096)
+    assert L == 8192
+    np.testing.assert_allclose(base, 1e6 * 3.0 ** (128.0 / 126.0), rtol=1e-15)
+
 
 ALL_PINS = [
+    pin_dynamic_ntk_closed_forms,
     pin_rms_norm_matches_torch, pin_rms_norm_closed_forms, pin_qk_norm_in_cache_write,
     pin_fp8_decode_table, pin_fp8_matches_torch, pin_fp8_roundtrip_ties_saturation,
     pin_fp8_cache_write, pin_fp8_attention_reads_dequantized_cache,

@@ -26,6 +26,11 @@ MUTATIONS = [
     ("rope_neox", "c = np.cos(a)[:, None, :]", "c = np.cos(a)[:, None, :] * 0 + 1"),  # dropped cos
     ("rope_inv_freq", "-2.0 * i / float(head_dim)", "-1.0 * i / float(head_dim)"),
     ("rope_inv_freq", "np.power(float(theta),", "np.power(10000.0,"),      # base ignored
+    # dynamic-NTK rope scaling
+    ("rope_dynamic_ntk", "** (d / (d - 2.0))", "** (d / (d - 1.0))"),       # wrong exponent
+    ("rope_dynamic_ntk", "(s * L / float(original_max_position) - (s - 1.0))",
+     "(s * L / float(original_max_position))"),                            # (factor - 1) dropped
+    ("rope_dynamic_ntk", "L = int(s * int(original_max_position))", "L = int(original_max_position)"),
     # rounding
     ("f64_to_bf16_bits", "r = np.rint(xf / ulp) * ulp", "r = np.trunc(xf / ulp) * ulp"),
     ("f64_to_bf16_bits", "r = np.rint(xf / ulp) * ulp",
