@@ -136,6 +136,27 @@ def bench_qknorm(steps, warmup):
     return dict(tokens=b.num_tokens, ms=ms, bytes=b.rope_write_bytes())
 
 
+def bench_decode_131k(steps, warmup):
+    """Qwen2-7B decode at 65k-131k contexts with the dynamic-NTK (factor 4)
+    rope table: the same kernels over positions past the native window."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    log("generating the 131k-context decode workload")
+    b = W.qwen2_131k_decode()
+    dev = runner.DeviceStep(b)
+
+    def step():
+        dev.rope_write()
+        dev.decode()
+    step_ms, _ = _time(step, steps, warmup)
+    dec_ms, _ = _time(dev.decode, steps, warmup)
+    res = dict(step_ms=step_ms, decode_ms=dec_ms, kv_bytes=b.decode_kv_bytes(),
+               alg_bytes=b.decode_bytes(), seqs=b.num_seqs, mean_ctx=float(b.context_lens.mean()))
+    del dev
+    return res
+
+
 def bench_prefill(steps, warmup):
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
@@ -253,6 +274,8 @@ def main():
         log(f"fp8 decode: step {res['fp8']['step_ms']:.3f} ms (decode {res['fp8']['decode_ms']:.3f})")
         res["qknorm"] = bench_qknorm(args.steps, args.warmup)
         log(f"q/k-norm rope + cache write: {res['qknorm']['ms']:.4f} ms")
+        res["ctx131k"] = bench_decode_131k(args.steps, args.warmup)
+        log(f"131k decode: step {res['ctx131k']['step_ms']:.3f} ms (decode {res['ctx131k']['decode_ms']:.3f})")
 
     b = dec["batch"]
     value = dec["kv_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
@@ -338,6 +361,18 @@ def main():
             "ms": round(qn["ms"], 4),
             "GB/s": round(qn["bytes"] / (qn["ms"] * 1e-3) / 1e9, 2),
             "plain_write_ms": round(res["prefill"]["rope_ms"], 4),
+        }
+    if "ctx131k" in res:
+        c = res["ctx131k"]
+        out["dynamic_ntk_131k_decode"] = {
+            "workload": "qwen2-7b decode, batch 8, contexts U[65536, 131072], dynamic-NTK rope "
+                        "table (factor 4 over 32768 positions), seed 6",
+            "mean_context": round(c["mean_ctx"], 1),
+            "kv_bytes_per_step": int(c["kv_bytes"]),
+            "ms_per_step": round(c["step_ms"], 4),
+            "decode_ms": round(c["decode_ms"], 4),
+            "kv_read_GB/s": round(c["kv_bytes"] / (c["step_ms"] * 1e-3) / 1e9, 2),
+            "hbm_frac": round(c["alg_bytes"] / (c["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
     if not args.no_cpu:
         log("CPU oracle baseline")

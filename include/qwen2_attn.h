@@ -98,6 +98,27 @@ int qwen2_rope_table_init(double* cos_sin, int max_position, int rotary_dim,
                           double rope_theta, hipStream_t stream);
 
 /*
+ * Dynamic-NTK rope scaling: the table for a context longer than the model's
+ * original window.  It has L = qwen2_rope_dynamic_ntk_positions(original,
+ * factor) = floor(factor * original_max_position) rows and is the table of
+ * qwen2_rope_table_init with the base
+ *   rope_theta * (factor * L / original_max_position - (factor - 1))^(d / (d - 2))
+ * (d = rotary_dim; the base is formed in float64 on the host): the fastest
+ * frequency is unchanged and the slowest turns factor^2 - factor + 1 times
+ * slower.  Every other call takes the table (and max_position = L) as usual.
+ * "Qwen2大模型架构解析与vLLM优化实践", §7.1 (rope_scaling {"type": "dynamic",
+ * "factor", "original_max_position"} raising the RoPE base); "Qwen2 模型结构
+ * 代码详解", §3 (rope_scaling handed to get_rope past 32768 positions).
+ * cos_sin: device, float64 [L][rotary_dim], written.  Requires
+ * original_max_position >= 1, factor >= 1, rotary_dim even in [4, 256],
+ * rope_theta > 0.  qwen2_rope_dynamic_ntk_positions returns -1 for invalid
+ * arguments.
+ */
+int qwen2_rope_dynamic_ntk_positions(int original_max_position, double factor);
+int qwen2_rope_table_init_dynamic_ntk(double* cos_sin, int original_max_position, double factor,
+                                      int rotary_dim, double rope_theta, hipStream_t stream);
+
+/*
  * Rotate q and k of num_tokens tokens and write k, v into the paged cache.
  *   q  [T][num_heads][head_dim]     (q_row_stride elements between tokens)
  *   k  [T][num_kv_heads][head_dim]  (k_row_stride)

@@ -29,6 +29,8 @@ _p, _i, _i64, _f, _d, _sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctyp
                             ctypes.c_double, ctypes.c_size_t)
 SIGNATURES = {
     "qwen2_rope_table_init": (_i, [_p, _i, _i, _d, _p]),
+    "qwen2_rope_dynamic_ntk_positions": (_i, [_i, _d]),
+    "qwen2_rope_table_init_dynamic_ntk": (_i, [_p, _i, _d, _i, _d, _p]),
     "qwen2_rope_cache_write": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
                                     _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
     "qwen2_attn_prefill_varlen": (_i, [_p, _i64, _p, _p, _i, _p, _p, _p, _i, _p, _i64, _i, _i,
@@ -130,6 +132,27 @@ def qwen2_rope_table_init(cos_sin: torch.Tensor, rope_theta: float, stream=None)
     _check("qwen2_rope_table_init",
            lib().qwen2_rope_table_init(cos_sin.data_ptr(), cos_sin.shape[0], cos_sin.shape[1],
                                        float(rope_theta), _stream(stream)))
+
+
+def qwen2_rope_dynamic_ntk_positions(original_max_position: int, factor: float) -> int:
+    """Rows of the dynamic-NTK table: floor(factor * original_max_position)."""
+    n = lib().qwen2_rope_dynamic_ntk_positions(int(original_max_position), float(factor))
+    if n < 1:
+        raise ValueError("invalid original_max_position / factor")
+    return n
+
+
+def qwen2_rope_table_init_dynamic_ntk(cos_sin: torch.Tensor, original_max_position: int,
+                                      factor: float, rope_theta: float, stream=None) -> None:
+    """cos_sin: float64 [qwen2_rope_dynamic_ntk_positions(...)][rotary_dim], filled."""
+    if cos_sin.dtype != torch.float64 or not cos_sin.is_contiguous() or cos_sin.dim() != 2:
+        raise TypeError("cos_sin must be a contiguous float64 [positions][rotary_dim] tensor")
+    if cos_sin.shape[0] != qwen2_rope_dynamic_ntk_positions(original_max_position, factor):
+        raise ValueError("cos_sin rows must equal qwen2_rope_dynamic_ntk_positions(...)")
+    _check("qwen2_rope_table_init_dynamic_ntk",
+           lib().qwen2_rope_table_init_dynamic_ntk(cos_sin.data_ptr(), int(original_max_position),
+                                                   float(factor), cos_sin.shape[1],
+                                                   float(rope_theta), _stream(stream)))
 
 
 def qwen2_rope_cache_write(q, q_out, k, v, positions, slot_mapping, cos_sin, k_cache, v_cache,

@@ -12,6 +12,8 @@
 
 #include "kernels.h"
 
+#include <cmath>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -93,6 +95,31 @@ int qwen2_rope_table_init(double* cos_sin, int max_position, int rotary_dim, dou
     return fail(QW_ERR_SHAPE, "rotary_dim=%d must be even in [2, 256]", rotary_dim);
   if (!(rope_theta > 0.0)) return fail(QW_ERR_SHAPE, "rope_theta must be > 0");
   return launched(qw::launch_rope_table(cos_sin, max_position, rotary_dim, rope_theta, stream));
+}
+
+int qwen2_rope_dynamic_ntk_positions(int original_max_position, double factor) {
+  if (original_max_position < 1 || !(factor >= 1.0) || !(factor * original_max_position < 2147483647.0))
+    return -1;
+  return static_cast<int>(factor * original_max_position);
+}
+
+int qwen2_rope_table_init_dynamic_ntk(double* cos_sin, int original_max_position, double factor,
+                                      int rotary_dim, double rope_theta, hipStream_t stream) {
+  if (!cos_sin) return fail(QW_ERR_NULL, "cos_sin is NULL");
+  const int L = qwen2_rope_dynamic_ntk_positions(original_max_position, factor);
+  if (L < 1)
+    return fail(QW_ERR_SHAPE, "original_max_position=%d and factor=%g give no table",
+                original_max_position, factor);
+  if (rotary_dim < 4 || rotary_dim > 256 || rotary_dim % 2)
+    return fail(QW_ERR_SHAPE, "rotary_dim=%d must be even in [4, 256]", rotary_dim);
+  if (!(rope_theta > 0.0)) return fail(QW_ERR_SHAPE, "rope_theta must be > 0");
+  // the base grows so that the slowest rotation turns factor L / original -
+  // (factor - 1) times slower over the longer table (d / (d - 2) exponent)
+  const double d = rotary_dim;
+  const double base = rope_theta * std::pow(factor * L / static_cast<double>(original_max_position) -
+                                            (factor - 1.0), d / (d - 2.0));
+  if (!(base > 0.0) || !(base < 1e300)) return fail(QW_ERR_SHAPE, "scaled rope base out of range");
+  return launched(qw::launch_rope_table(cos_sin, L, rotary_dim, base, stream));
 }
 
 static int check_fp8_scales(float k_scale, float v_scale) {

@@ -33,12 +33,24 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def rope_table(head_dim: int, theta: float, max_position: int, device="cuda") -> torch.Tensor:
-    key = (head_dim, float(theta), int(max_position), str(device))
+def rope_table(head_dim: int, theta: float, max_position: int, device="cuda",
+               rope_scaling=None) -> torch.Tensor:
+    """The device cos/sin table; with rope_scaling = (factor, original) the
+    dynamic-NTK table of floor(factor * original) rows."""
+    key = (head_dim, float(theta), int(max_position), str(device),
+           None if rope_scaling is None else tuple(rope_scaling))
     t = _TABLES.get(key)
     if t is None:
-        t = torch.empty(max_position, head_dim, dtype=torch.float64, device=device)
-        B.qwen2_rope_table_init(t, theta)
+        if rope_scaling is None:
+            t = torch.empty(max_position, head_dim, dtype=torch.float64, device=device)
+            B.qwen2_rope_table_init(t, theta)
+        else:
+            factor, original = rope_scaling
+            n = B.qwen2_rope_dynamic_ntk_positions(original, factor)
+            if n != max_position:
+                raise ValueError(f"max_position {max_position} != scaled table rows {n}")
+            t = torch.empty(n, head_dim, dtype=torch.float64, device=device)
+            B.qwen2_rope_table_init_dynamic_ntk(t, original, factor, theta)
         _TABLES[key] = t
     return t
 
@@ -66,7 +78,8 @@ class DeviceStep:
         self.fp8 = cdt == "fp8"
         self.k_cache = k_cache if k_cache is not None else to_device(batch.k_cache, cdt, device)
         self.v_cache = v_cache if v_cache is not None else to_device(batch.v_cache, cdt, device)
-        self.cos_sin = rope_table(d, sh.rope_theta, sh.max_position, device)
+        self.cos_sin = rope_table(d, sh.rope_theta, sh.max_position, device,
+                                  getattr(sh, "rope_scaling", None))
         self.q_norm_w = self.k_norm_w = None
         if batch.q_norm_weight is not None:
             self.q_norm_w = to_device(batch.q_norm_weight, sh.dtype, device)

@@ -115,6 +115,9 @@ class AttnShape:
     k_scale: float = 1.0                # FP8 cache: value = code * scale
     v_scale: float = 1.0
     rms_eps: float = 1e-6               # Qwen3 q/k norm epsilon (when the batch has weights)
+    # dynamic-NTK rope scaling (factor, original_max_position), or None; the
+    # table then has max_position = floor(factor * original) rows
+    rope_scaling: Optional[tuple] = None
 
     @property
     def group(self) -> int:
@@ -485,6 +488,19 @@ def mixed_tp2(seed: int = 5, keep_logical: bool = False) -> Batch:
                   keep_logical=keep_logical)
 
 
+def qwen2_131k_decode(seed: int = 6, num_seqs: int = 8, keep_logical: bool = False) -> Batch:
+    """Qwen2-7B decode past the native window with dynamic-NTK rope scaling
+    (factor 4 over 32768 positions: a 131072-row table), bf16: 28 q heads,
+    4 KV heads, head_dim 128, block 16; batch 8, contexts uniform in
+    [65536, 131072]."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128, rope_scaling=(4.0, 32768),
+                      max_position=131072)
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(65536, 131072, size=num_seqs, endpoint=True).astype(np.int32)
+    return _build("qwen2_7b_131k_decode_b8", shape, seed, rng, ctx, np.ones(num_seqs, np.int32), 0,
+                  np.zeros(num_seqs, bool), 0, 1.0, keep_logical=keep_logical)
+
+
 def with_qk_norm(b: Batch, seed: int) -> Batch:
     """Attach Qwen3 q/k norm weights: N(1, 0.1^2) per element (learned RMSNorm
     weights sit around 1), drawn from their own generator so the batch's
@@ -509,11 +525,14 @@ def small_case(seed: int, dtype: str, num_heads: int, num_kv_heads: int, head_di
                context_lens, query_lens, num_prefill: int, block_size: int = 16,
                value_scale: float = 1.0, keep_logical: bool = True, shares_prefix=None,
                shared_prefix_len: int = 0, cache_dtype=None, k_scale: float = 1.0,
-               v_scale: float = 1.0, qk_norm: bool = False) -> Batch:
+               v_scale: float = 1.0, qk_norm: bool = False, rope_scaling=None) -> Batch:
     """A custom small batch (tests): explicit lengths, any head layout."""
     shape = AttnShape(num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
                       block_size=block_size, dtype=dtype, cache_dtype=cache_dtype,
                       k_scale=k_scale, v_scale=v_scale)
+    if rope_scaling is not None:
+        shape.rope_scaling = (float(rope_scaling[0]), int(rope_scaling[1]))
+        shape.max_position = int(rope_scaling[0] * rope_scaling[1])
     rng = np.random.default_rng(seed)
     ctx = np.asarray(context_lens, np.int32)
     ql = np.asarray(query_lens, np.int32)
@@ -531,4 +550,5 @@ WORKLOADS = {
     "mixed_tp2": mixed_tp2,
     "qwen2_long_decode_fp8": qwen2_long_decode_fp8,
     "qwen3_decode_qknorm": qwen3_decode_qknorm,
+    "qwen2_131k_decode": qwen2_131k_decode,
 }

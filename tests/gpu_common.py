@@ -39,9 +39,13 @@ def run_oracle(batch, seqs=None):
     (the cache write always covers every token)."""
     sh = batch.shape
     fp8 = dict(cache_dtype=sh.cache_dtype, k_scale=sh.k_scale, v_scale=sh.v_scale)
+    theta = sh.rope_theta
+    if sh.rope_scaling is not None:
+        theta, rows = R.rope_dynamic_ntk(sh.rope_theta, sh.head_dim, *sh.rope_scaling)
+        assert rows == sh.max_position
     q_out, kc, vc = R.rope_cache_write(batch.qkv, sh.dtype, batch.positions, batch.slot_mapping,
                                        batch.k_cache, batch.v_cache, sh.num_heads, sh.num_kv_heads,
-                                       sh.head_dim, sh.block_size, sh.rope_theta, **fp8,
+                                       sh.head_dim, sh.block_size, theta, **fp8,
                                        q_norm_weight=batch.q_norm_weight,
                                        k_norm_weight=batch.k_norm_weight, rms_eps=sh.rms_eps)
     cu = batch.cu_seqlens_q

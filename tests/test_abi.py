@@ -196,6 +196,24 @@ def test_prefill_validation(lib, kw, status):
     assert _prefill(lib, **kw) == status
 
 
+def test_dynamic_ntk_positions_and_validation(lib):
+    assert lib.qwen2_rope_dynamic_ntk_positions(4096, 2.0) == 8192
+    assert lib.qwen2_rope_dynamic_ntk_positions(32768, 4.0) == 131072
+    assert lib.qwen2_rope_dynamic_ntk_positions(1000, 1.5) == 1500
+    assert lib.qwen2_rope_dynamic_ntk_positions(0, 2.0) == -1
+    assert lib.qwen2_rope_dynamic_ntk_positions(4096, 0.5) == -1
+    assert lib.qwen2_rope_dynamic_ntk_positions(4096, float("nan")) == -1
+    assert lib.qwen2_rope_dynamic_ntk_positions(1 << 30, 4.0) == -1
+    f = lib.qwen2_rope_table_init_dynamic_ntk
+    assert f(0, 4096, 2.0, 128, 1e6, None) == QW_ERR_NULL
+    assert f(P, 0, 2.0, 128, 1e6, None) == QW_ERR_SHAPE
+    assert f(P, 4096, 0.9, 128, 1e6, None) == QW_ERR_SHAPE
+    assert f(P, 4096, 2.0, 127, 1e6, None) == QW_ERR_SHAPE
+    assert f(P, 4096, 2.0, 2, 1e6, None) == QW_ERR_SHAPE
+    assert f(P, 4096, 2.0, 128, -1.0, None) == QW_ERR_SHAPE
+    assert lib.qwen2_last_error().decode()
+
+
 def test_rope_table_validation(lib):
     assert lib.qwen2_rope_table_init(0, 10, 128, 1e6, None) == QW_ERR_NULL
     assert lib.qwen2_rope_table_init(P, 0, 128, 1e6, None) == QW_ERR_SHAPE
