@@ -69,16 +69,15 @@ constexpr int kTiers = 3;
 __constant__ int kTierPct[kTiers + 1] = {0, 75, 90, 100};
 constexpr int kTierPctHost[kTiers + 1] = {0, 75, 90, 100};
 constexpr int kTierWgs[kTiers] = {kCUs, kCUs, 2 * kCUs};
-constexpr int kMaxRanges = 4 * kCUs;
-static_assert(kTierWgs[0] + kTierWgs[1] + kTierWgs[2] <= kMaxRanges, "ranges");
 __constant__ int kTierMin[kTiers] = {64, 32, 24};
 constexpr int kTierMinHost[kTiers] = {64, 32, 24};
+constexpr int kMaxRanges = 6 * kCUs;
 constexpr int kClaimAhead = 6;          // blocks of wave 0 left when the next range is claimed
 // LDS per workgroup: the merge buffer, sized so that a CU holds one
 // workgroup (four waves, one per SIMD)
 constexpr int kLdsFloats = 21504;       // 84 KiB
 static_assert(kLdsFloats >= kNW * kMaxG * kD, "merge buffer");
-constexpr size_t kWsHeader = 256;       // the range counter; then the range descriptors, the partial states
+constexpr size_t kWsHeader = 256;       // counters; then the range descriptors, the merge jobs, the partial states
 constexpr int kRangeEmpty = 2, kRangeFirst = 1;   // descriptor flags
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;           // log2-domain slack before the softmax reference moves
@@ -135,6 +134,7 @@ struct DecodeKArgs {
   int num_ranges;
   int* claim;             // range counter, zero at launch
   int4* desc;             // per range: merge source range (-1: none), flags, segment (s, g)
+  int* jobs;              // ranges whose first piece ends a shared segment (count in claim[2])
   float scale_log2;   // scale * log2 e (* k_scale with an FP8 cache)
   float out_scale;    // 1, or v_scale with an FP8 cache
 };
@@ -254,7 +254,6 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   const int Hkv = a.num_kv_heads;
   const int64_t U = total_units(a, lane);
   const Schedule sched = schedule_for(a, U);
-  if (blockIdx.x == 0 && tid == 0) a.claim[1] = sched.R;   // for the merge kernel
 
   // per-wave softmax states of a piece, merged at its end
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
@@ -300,6 +299,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
       d.y = range_begin(sched, ra, U) == cur.seg0 ? kRangeFirst : 0;
     }
     a.desc[rg] = d;
+    if (d.x >= 0) a.jobs[atomicAdd(a.claim + 2, 1)] = rg;
   }
   int64_t u = u0;
   bool first_piece = true;
@@ -539,10 +539,11 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
 constexpr int kMergeBatch = 16;
 template <int G>
 __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
-  const int r = blockIdx.x, tid = threadIdx.x;
-  if (r >= a.claim[1]) return;           // ranges of this batch: written by the stream kernel
+  const int tid = threadIdx.x;
+  const int njobs = a.claim[2];          // written by the stream kernel
+  for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
+  const int r = a.jobs[job];
   const int4 d = a.desc[r];
-  if (d.x < 0) return;
   const int ra = d.x;
   const bool ra_first = (d.y & kRangeFirst) != 0;
   const int np = r - ra + 1;
@@ -582,14 +583,19 @@ __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
   }
   a.out[static_cast<int64_t>(d.z) * a.out_stride + static_cast<int64_t>(d.w * G + h) * kD + e] =
       f32_to_bf16(o * a.out_scale / L);
+  }
 }
 
 // zero the range counter
 __global__ void decode_claim_reset_kernel(int* claim) {
-  if (threadIdx.x == 0) *claim = 0;
+  if (threadIdx.x == 0) {
+    claim[0] = 0;                        // range counter
+    claim[2] = 0;                        // merge jobs
+  }
 }
 
 static size_t desc_bytes(int num_ranges) { return (static_cast<size_t>(num_ranges) * 16 + 255) / 256 * 256; }
+static size_t jobs_bytes(int num_ranges) { return (static_cast<size_t>(num_ranges) * 4 + 255) / 256 * 256; }
 
 // ranges per tier for a batch of at most umax units
 static void decode_schedule(int num_seqs, int max_context_len, int num_kv_heads, int (&wgs)[kTiers]) {
@@ -613,7 +619,7 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   decode_schedule(num_seqs, max_context_len, num_kv_heads, wgs);
   p.num_ranges = 0;
   for (int t = 0; t < kTiers; ++t) p.num_ranges += wgs[t];
-  p.ws_bytes = kWsHeader + desc_bytes(p.num_ranges) +
+  p.ws_bytes = kWsHeader + desc_bytes(p.num_ranges) + jobs_bytes(p.num_ranges) +
                static_cast<size_t>(2) * p.num_ranges * G * (kD + 2) * sizeof(float);
   return p;
 }
@@ -626,7 +632,7 @@ static void launch_stream(const DecodeKArgs& k, const AttnArgs& a, hipStream_t s
     hipLaunchKernelGGL((decode_stream_kernel<G, true>), dim3(grid), dim3(kThreads), 0, stream, k);
   else
     hipLaunchKernelGGL((decode_stream_kernel<G, false>), dim3(grid), dim3(kThreads), 0, stream, k);
-  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(k.num_ranges), dim3(G * kD), 0, stream, k);
+  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(grid), dim3(G * kD), 0, stream, k);
 }
 
 hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t stream) {
@@ -654,8 +660,10 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
   k.claim = static_cast<int*>(a.workspace);
   k.desc = reinterpret_cast<int4*>(static_cast<uint8_t*>(a.workspace) + kWsHeader);
+  k.jobs = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) + kWsHeader +
+                                   desc_bytes(k.num_ranges));
   k.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + kWsHeader +
-                                      desc_bytes(k.num_ranges));
+                                      desc_bytes(k.num_ranges) + jobs_bytes(k.num_ranges));
   k.ws_ml = k.ws_acc + static_cast<size_t>(2) * k.num_ranges * G * kD;
   switch (G) {
     case 1: launch_stream<1>(k, a, stream); break;
