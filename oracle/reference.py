@@ -39,6 +39,13 @@ with the function that uses it):
     y = x / sqrt(mean(x^2) + eps) * w, after the QKV split and before the
     rotation (the pages print the modules, not their order of use), in
     float64 together with the rotation, rounded once;
+  * shared-prefix (cascade) decode ([P1] §3 and §4: with prefix caching
+    the attention layer reuses the KV blocks of an identical prefix): the
+    shared prefix blocks are attended once per group of sequences that hold
+    them, each member's private suffix separately, and the two partial
+    softmax states are merged exactly; the result is defined to be the plain
+    decode attention over the member's whole block table
+    (attention_decode_cascade);
   * FP8 KV cache ([P2] §4.1 and §4.2 list FP8 KV-cache quantization with
     per-layer cache scale parameters; §6.3 names the E4M3FN format): the
     cache holds E4M3FN codes of the exact rotated key (or the value) divided
@@ -61,7 +68,7 @@ __all__ = [
     "bf16_bits_to_f64", "rope_cache_write", "gather_kv", "causal_visible",
     "softmax_rows", "kv_head_for", "default_scale", "attention_varlen",
     "attention_decode", "run_step", "fp8_e4m3_decode", "fp8_e4m3_encode", "E4M3_MAX",
-    "rms_norm_heads",
+    "rms_norm_heads", "attention_decode_cascade", "check_prefix_groups",
 ]
 
 
@@ -391,6 +398,95 @@ def attention_decode(q, k_cache, v_cache, block_tables, context_lens,
     return attention_varlen(q, k_cache, v_cache, cu, context_lens, block_tables,
                             num_heads, num_kv_heads, head_dim, block_size, dtype, scale,
                             cache_dtype=cache_dtype, k_scale=k_scale, v_scale=v_scale)
+
+
+def check_prefix_groups(block_tables, context_lens, prefix_indptr, prefix_seqs, prefix_lens,
+                        block_size):
+    """The contract of a shared-prefix grouping: group p's members are
+    prefix_seqs[prefix_indptr[p]:prefix_indptr[p+1]], its prefix is the first
+    prefix_lens[p] tokens (whole blocks) of every member, held in the same
+    physical blocks (prefix caching shares block ids, [P1] §3), and every
+    member has at least one private key after it (its new token).  A sequence
+    belongs to at most one group.  Raises ValueError otherwise."""
+    ind = np.asarray(prefix_indptr, np.int64)
+    seqs = np.asarray(prefix_seqs, np.int64)
+    lens = np.asarray(prefix_lens, np.int64)
+    S, B = len(context_lens), int(block_size)
+    if ind.ndim != 1 or len(ind) != len(lens) + 1 or ind[0] != 0 or np.any(np.diff(ind) < 0) \
+            or ind[-1] != len(seqs):
+        raise ValueError("prefix_indptr must rise from 0 to len(prefix_seqs)")
+    if len(np.unique(seqs)) != len(seqs) or np.any(seqs < 0) or np.any(seqs >= S):
+        raise ValueError("a member is out of range or listed twice")
+    for p in range(len(lens)):
+        members = seqs[ind[p]:ind[p + 1]]
+        L = int(lens[p])
+        if L < 0 or L % B:
+            raise ValueError(f"group {p}: prefix length {L} is not a whole number of blocks")
+        if len(members) == 0:
+            continue
+        ids = np.asarray(block_tables[members[0]])[:L // B]
+        for s in members:
+            if L >= int(context_lens[s]):
+                raise ValueError(f"group {p}: member {s} has no key after the prefix")
+            if not np.array_equal(np.asarray(block_tables[s])[:L // B], ids):
+                raise ValueError(f"group {p}: member {s} does not hold the shared prefix blocks")
+
+
+def _partial_state(q, K, V, scale):
+    """Softmax partial state of one query over a set of keys: reference
+    maximum m, normaliser l = sum_j e^(z_j - m), unnormalised output
+    a = sum_j e^(z_j - m) V_j, with z_j = scale <q, K_j>."""
+    z = scale * (K @ q)
+    m = z.max()
+    w = np.exp(z - m)
+    return m, w.sum(), w @ V
+
+
+def attention_decode_cascade(q, k_cache, v_cache, block_tables, context_lens, prefix_indptr,
+                             prefix_seqs, prefix_lens, num_heads, num_kv_heads, head_dim,
+                             block_size, dtype, scale=None, cache_dtype=None, k_scale=1.0,
+                             v_scale=1.0):
+    """Decode attention evaluated as a two-level cascade.
+
+    For each group p (see check_prefix_groups) the L_p shared prefix keys
+    are gathered once, through the first member's block table, and every
+    member's query heads are attended to them: partial state (m1, l1, a1).
+    Each member's private keys L_p..c-1 give (m2, l2, a2).  Softmax over the
+    union of two disjoint key sets is the merge
+        M = max(m1, m2),  o = (a1 e^(m1-M) + a2 e^(m2-M)) / (l1 e^(m1-M) + l2 e^(m2-M)).
+    Sequences in no group are attended as in attention_decode.  Returns
+    float64 [S][H][d]."""
+    H, Hkv, d, B = num_heads, num_kv_heads, head_dim, int(block_size)
+    if scale is None:
+        scale = default_scale(d)
+    check_prefix_groups(block_tables, context_lens, prefix_indptr, prefix_seqs, prefix_lens, B)
+    out = attention_decode(q, k_cache, v_cache, block_tables, context_lens, H, Hkv, d, B, dtype,
+                           scale, cache_dtype=cache_dtype, k_scale=k_scale, v_scale=v_scale)
+    qf = to_f64(q, dtype).reshape(-1, H, d)
+    ind = np.asarray(prefix_indptr, np.int64)
+    seqs = np.asarray(prefix_seqs, np.int64)
+    for p in range(len(ind) - 1):
+        members = seqs[ind[p]:ind[p + 1]]
+        L = int(prefix_lens[p])
+        if len(members) == 0 or L == 0:
+            continue
+        # the shared prefix, gathered once for the whole group
+        Kp, Vp = gather_kv(k_cache, v_cache, block_tables[members[0]], L, B, dtype,
+                           cache_dtype, k_scale, v_scale)
+        for s in members:
+            c = int(context_lens[s])
+            # the member's own keys after the prefix
+            K, V = gather_kv(k_cache, v_cache, block_tables[s], c, B, dtype, cache_dtype,
+                             k_scale, v_scale)
+            Ks, Vs = K[L:], V[L:]
+            for h in range(H):
+                g = kv_head_for(h, H, Hkv)
+                m1, l1, a1 = _partial_state(qf[s, h], Kp[:, g, :], Vp[:, g, :], scale)
+                m2, l2, a2 = _partial_state(qf[s, h], Ks[:, g, :], Vs[:, g, :], scale)
+                M = max(m1, m2)
+                e1, e2 = np.exp(m1 - M), np.exp(m2 - M)
+                out[s, h] = (a1 * e1 + a2 * e2) / (l1 * e1 + l2 * e2)
+    return out
 
 
 def run_step(batch, k_cache=None, v_cache=None):

@@ -173,6 +173,9 @@ class Batch:
     # Qwen3 q/k norm weights ([head_dim], step dtype), or None
     q_norm_weight: Optional[np.ndarray] = None
     k_norm_weight: Optional[np.ndarray] = None
+    # shared prefixes of the decode sequences: (indptr [P+1], members
+    # (decode-local indices), prefix lengths in tokens [P]), or None
+    prefix_groups: Optional[tuple] = None
 
     # ---- derived views ----
     @property
@@ -231,6 +234,22 @@ class Batch:
         qo = 2 * nd * sh.num_heads * sh.head_dim * sh.elem_bytes
         bt = 4 * int(((c + sh.block_size - 1) // sh.block_size).sum()) + 4 * nd
         return self.decode_kv_bytes() + qo + bt
+
+    def decode_cascade_bytes(self) -> int:
+        """decode_bytes with every group's shared prefix read once per KV head
+        instead of once per member (the block-table entries likewise)."""
+        if self.prefix_groups is None:
+            return self.decode_bytes()
+        sh = self.shape
+        ind, members, lens = self.prefix_groups
+        per_token = 2 * sh.num_kv_heads * sh.head_dim * sh.cache_elem_bytes
+        saved = 0
+        for p in range(len(lens)):
+            m = int(ind[p + 1] - ind[p])
+            if m > 1:
+                L = int(lens[p])
+                saved += (m - 1) * (L * per_token + 4 * (L // sh.block_size))
+        return self.decode_bytes() - saved
 
     def prefill_flops(self) -> int:
         """4*d*H per unmasked (query, key) pair: QK^T and PV, causal entries only."""
@@ -367,7 +386,17 @@ def _build(name: str, shape: AttnShape, seed: int, rng: np.random.Generator,
                  k_cache=k_cache, v_cache=v_cache, block_tables=bt,
                  context_lens=context_lens.astype(np.int32), query_lens=query_lens.astype(np.int32),
                  num_prefill=num_prefill, poison_block=poison, shared_prefix_blocks=spb, seed=seed,
-                 pre_k=pre_k if keep_logical else None, pre_v=pre_v if keep_logical else None)
+                 pre_k=pre_k if keep_logical else None, pre_v=pre_v if keep_logical else None,
+                 prefix_groups=_one_group(shares_prefix[num_prefill:], shared_prefix_len))
+
+
+def _one_group(dec_share: np.ndarray, prefix_len: int):
+    """The decode sequences holding the shared prefix as one prefix group
+    (decode-local indices), or None."""
+    members = np.flatnonzero(np.asarray(dec_share, bool)).astype(np.int32)
+    if prefix_len == 0 or len(members) == 0:
+        return None
+    return (np.array([0, len(members)], np.int32), members, np.array([prefix_len], np.int32))
 
 
 # --------------------------------------------------------------------------
@@ -521,6 +550,49 @@ def qwen3_decode_qknorm(seed: int = 2, num_seqs: int = 32, keep_logical: bool = 
     return with_qk_norm(qwen3_decode(seed, num_seqs, keep_logical), seed)
 
 
+def with_prefix_groups(b: Batch, groups) -> Batch:
+    """Make decode sequences share prefixes, as prefix caching does: groups
+    is a list of (members, prefix_len) with members decode-local indices and
+    prefix_len a multiple of the block size, below every member's context.
+    Each member's first prefix_len / block_size block ids become those of
+    the group's first member (the blocks they named before stay in the pool,
+    unreferenced).  Records the grouping in b.prefix_groups."""
+    B, P = b.shape.block_size, b.num_prefill
+    ind, seqs, lens = [0], [], []
+    for members, L in groups:
+        assert L % B == 0
+        members = [int(m) for m in members]
+        first = b.block_tables[P + members[0], : L // B].copy()
+        for m in members:
+            assert L < int(b.context_lens[P + m])
+            b.block_tables[P + m, : L // B] = first
+        seqs.extend(members)
+        lens.append(L)
+        ind.append(len(seqs))
+    b.prefix_groups = (np.array(ind, np.int32), np.array(seqs, np.int32), np.array(lens, np.int32))
+    b.pre_k = b.pre_v = None
+    return b
+
+
+def shared_prompt_decode(seed: int = 7, num_groups: int = 4, members_per_group: int = 16,
+                         prefix_len: int = 4096, keep_logical: bool = False) -> Batch:
+    """Qwen2-7B decode, bf16, where sequences share long system prompts:
+    num_groups groups of members_per_group sequences, each group holding one
+    prefix_len-token prefix (shared block ids), private suffixes uniform in
+    [256, 2048] tokens after it.  28 q heads, 4 KV heads, head_dim 128,
+    block 16."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128)
+    rng = np.random.default_rng(seed)
+    S = num_groups * members_per_group
+    ctx = (prefix_len + rng.integers(256, 2048, size=S, endpoint=True)).astype(np.int32)
+    b = _build(f"qwen2_7b_shared_prompt_{num_groups}x{members_per_group}_p{prefix_len}", shape,
+               seed, rng, ctx, np.ones(S, np.int32), 0, np.zeros(S, bool), 0, 1.0,
+               keep_logical=keep_logical)
+    groups = [(list(range(g * members_per_group, (g + 1) * members_per_group)), prefix_len)
+              for g in range(num_groups)]
+    return with_prefix_groups(b, groups)
+
+
 def small_case(seed: int, dtype: str, num_heads: int, num_kv_heads: int, head_dim: int,
                context_lens, query_lens, num_prefill: int, block_size: int = 16,
                value_scale: float = 1.0, keep_logical: bool = True, shares_prefix=None,
@@ -551,4 +623,5 @@ WORKLOADS = {
     "qwen2_long_decode_fp8": qwen2_long_decode_fp8,
     "qwen3_decode_qknorm": qwen3_decode_qknorm,
     "qwen2_131k_decode": qwen2_131k_decode,
+    "shared_prompt_decode": shared_prompt_decode,
 }

@@ -591,7 +591,99 @@ def pin_dynamic_ntk_closed_forms(R):
     np.testing.assert_allclose(base, 1e6 * 3.0 ** (128.0 / 126.0), rtol=1e-15)
 
 
+# ---------------------------------------------------------------------------
+# shared-prefix (cascade) decode
+# ---------------------------------------------------------------------------
+def _cascade_case(R, seed, dtype, H, Hkv, d, ctx, groups, B=16, fp8=False):
+    kw = dict(cache_dtype="fp8", k_scale=W.FP8_K_SCALE, v_scale=W.FP8_V_SCALE) if fp8 else {}
+    b = W.small_case(seed, dtype, H, Hkv, d, context_lens=list(ctx), query_lens=[1] * len(ctx),
+                     num_prefill=0, block_size=B, keep_logical=False, **kw)
+    W.with_prefix_groups(b, groups)
+    sh = b.shape
+    cd = "fp8" if fp8 else None
+    q_out, kc, vc = R.rope_cache_write(b.qkv, dtype, b.positions, b.slot_mapping, b.k_cache,
+                                       b.v_cache, H, Hkv, d, B, sh.rope_theta, cd, sh.k_scale,
+                                       sh.v_scale)
+    return b, q_out, kc, vc
+
+
+def _cascade(R, b, q_out, kc, vc, groups=None):
+    sh = b.shape
+    ind, seqs, lens = b.prefix_groups if groups is None else groups
+    cd = sh.cache_dtype
+    return R.attention_decode_cascade(q_out, kc, vc, b.block_tables, b.context_lens, ind, seqs,
+                                      lens, sh.num_heads, sh.num_kv_heads, sh.head_dim,
+                                      sh.block_size, sh.dtype, cache_dtype=cd,
+                                      k_scale=sh.k_scale, v_scale=sh.v_scale)
+
+
+def pin_cascade_equals_plain_decode(R):
+    """The cascade (shared prefix attended once per group, private suffix per
+    member, exact merge) equals softmax attention over each member's whole
+    block table: several groups, a non-member, GQA 2..8, odd block sizes, a
+    one-key suffix, FP8 codes."""
+    cases = [
+        (61, "f32", 4, 2, 16, (40, 70, 33, 90, 17), [([0, 1, 3], 32), ([2], 16)], 16, False),
+        (62, "bf16", 6, 2, 8, (9, 14, 11, 5, 20), [([1, 2, 4], 8)], 4, False),
+        (63, "bf16", 8, 1, 32, (49, 51, 50), [([0, 1, 2], 48)], 16, False),
+        (64, "bf16", 4, 2, 16, (30, 45, 21), [([2, 0], 16), ([1], 32)], 16, True),
+    ]
+    for seed, dt, H, Hkv, d, ctx, groups, B, fp8 in cases:
+        b, q_out, kc, vc = _cascade_case(R, seed, dt, H, Hkv, d, ctx, groups, B, fp8)
+        sh = b.shape
+        plain = R.attention_decode(q_out, kc, vc, b.block_tables, b.context_lens, H, Hkv, d, B,
+                                   dt, cache_dtype=sh.cache_dtype, k_scale=sh.k_scale,
+                                   v_scale=sh.v_scale)
+        cas = _cascade(R, b, q_out, kc, vc)
+        assert np.allclose(cas, plain, rtol=0, atol=1e-12), (seed, np.abs(cas - plain).max())
+
+
+def pin_cascade_needles(R):
+    """Closed forms on each side of the merge: with every query head equal to
+    u, a key 40 u in the shared prefix makes every member's output that key's
+    V row; the same key in one member's private suffix does so for that
+    member only (others keep their plain output)."""
+    H, Hkv, d, B = 4, 2, 16, 16
+    ctx, groups = (40, 37, 50), [([0, 1, 2], 32)]
+    b, q_out, kc, vc = _cascade_case(R, 65, "f32", H, Hkv, d, ctx, groups, B)
+    u = np.linspace(-1.0, 1.0, d).astype(np.float32)
+    q_out[:] = u
+    for where, key in (("prefix", 5), ("suffix", 34)):
+        kc2, vc2 = kc.copy(), vc.copy()
+        seq = 1                                         # the suffix needle sits in member 1
+        blk, off = int(b.block_tables[seq, key // B]), key % B
+        kc2[blk, :, off, :] = 40.0 * u
+        out = _cascade(R, b, q_out, kc2, vc2)
+        want = vc2[blk, :, :, off].astype(np.float64)  # [Hkv][d]
+        for s in range(3):
+            for h in range(H):
+                if where == "prefix" or s == seq:
+                    assert np.allclose(out[s, h], want[h // 2], rtol=0, atol=1e-12), (where, s, h)
+                else:
+                    assert not np.allclose(out[s, h], want[h // 2], rtol=0, atol=1e-3), (where, s, h)
+
+
+def pin_cascade_contract(R):
+    """Groupings that break the sharing contract are refused: members that
+    do not hold the same prefix blocks, a prefix that reaches a member's last
+    key, a partial block, a member listed twice."""
+    b, q_out, kc, vc = _cascade_case(R, 66, "f32", 4, 2, 16, (40, 70, 33), [([0, 1], 32)], 16)
+    bad = [
+        ([0, 2], [0, 2], [32]),          # member 2 holds its own blocks
+        ([0, 2], [0, 1], [48]),          # 48 >= context 40 of member 0
+        ([0, 2], [0, 1], [24]),          # not whole blocks
+        ([0, 2], [0, 0], [16]),          # listed twice
+    ]
+    for ind, seqs, lens in bad:
+        try:
+            _cascade(R, b, q_out, kc, vc, (np.array(ind), np.array(seqs), np.array(lens)))
+        except ValueError:
+            continue
+        raise AssertionError(f"grouping {ind, seqs, lens} accepted")
+
+
 ALL_PINS = [
+    pin_cascade_equals_plain_decode, pin_cascade_needles, pin_cascade_contract,
     pin_dynamic_ntk_closed_forms,
     pin_rms_norm_matches_torch, pin_rms_norm_closed_forms, pin_qk_norm_in_cache_write,
     pin_fp8_decode_table, pin_fp8_matches_torch, pin_fp8_roundtrip_ties_saturation,

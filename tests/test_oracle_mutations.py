@@ -57,6 +57,17 @@ MUTATIONS = [
     ("attention_varlen", "z = scale * (qf[r0:r1, h, :] @ K[:, g, :].T)",
      "z = scale * (qf[r0:r1, h, :] @ V[:, g, :].T)"),
     ("attention_varlen", "n, c = r1 - r0, int(context_lens[s])", "n, c = r1 - r0, int(context_lens[s]) - 1"),
+    # shared-prefix cascade
+    ("attention_decode_cascade", "Ks, Vs = K[L:], V[L:]", "Ks, Vs = K, V"),        # prefix counted twice
+    ("attention_decode_cascade", "Ks, Vs = K[L:], V[L:]", "Ks, Vs = K[L + 1:], V[L + 1:]"),
+    ("attention_decode_cascade", "/ (l1 * e1 + l2 * e2)", "/ (l1 + l2)"),         # normalisers not rescaled
+    ("attention_decode_cascade", "e1, e2 = np.exp(m1 - M), np.exp(m2 - M)",
+     "e1, e2 = np.exp(M - m1), np.exp(M - m2)"),
+    ("attention_decode_cascade", "m1, l1, a1 = _partial_state(qf[s, h],",
+     "m1, l1, a1 = _partial_state(qf[members[0], h],"),                         # first member's q
+    ("_partial_state", "w = np.exp(z - m)", "w = np.exp(z - 2 * m)"),
+    ("check_prefix_groups", "if not np.array_equal(np.asarray(block_tables[s])[:L // B], ids):",
+     "if False:"),
     # Qwen3 q/k norm
     ("rms_norm_heads", "np.sqrt(ms + float(eps))", "np.sqrt(ms)"),          # eps dropped
     ("rms_norm_heads", "ms = np.mean(x * x, axis=-1, keepdims=True)",
