@@ -309,6 +309,93 @@ int qwen3_rope_cache_write_fp8(const void* q, int64_t q_row_stride,
                                double rms_eps, float k_scale, float v_scale, hipStream_t stream);
 
 /*
+ * Shared-prefix (cascade) decode.  With prefix caching, sequences that start
+ * with the same prompt hold the same physical KV blocks for it ("Qwen2 模型
+ * 结构代码详解", §3: enable_prefix_caching makes the attention layer reuse the
+ * KV blocks of an identical prefix; §4 shows the reuse).  These calls compute
+ * exactly what qwen2_attn_decode_paged (resp. _fp8) computes -- softmax
+ * attention of each sequence's query over all keys of its block table -- but
+ * read each group's shared prefix blocks from HBM once for the whole group
+ * instead of once per member: the group's (member, query head) pairs are
+ * attended to the prefix together (16 per MFMA tile, in chunks of blocks),
+ * every member's private keys after the prefix by the decode's stream
+ * kernel, and the partial softmax states merged exactly.
+ *
+ * Prefix groups (DEVICE int32 arrays): group p's members are the sequences
+ * prefix_seqs[prefix_indptr[p] .. prefix_indptr[p + 1]) (indices into this
+ * call's batch); its prefix is the first prefix_lens[p] tokens of each
+ * member, a multiple of block_size, which every member's block table names
+ * with the same block ids (the group's ids are read from its first member's
+ * table).  Contract (not checked on the device; qwen2_check_prefix_groups_host
+ * checks it on host copies): prefix_indptr rises from 0 to num_prefix_members;
+ * each member appears once; 0 < prefix_lens[p] <= max_prefix_len; every
+ * member's context exceeds its prefix; members share the prefix block ids.
+ * A group whose length is not a positive multiple of block_size up to
+ * max_prefix_len, or whose first member is out of range or has no key
+ * after the prefix, is not used, and a member with no key after its prefix
+ * is decoded plainly: those sequences' results stay exact.  Members that do
+ * not hold the ids of the first member's table, or a sequence listed in two
+ * groups, give wrong outputs for those sequences (never out-of-bounds
+ * accesses).
+ *
+ * num_prefixes, num_prefix_members, max_prefix_len: HOST ints (>= 0).  With
+ * no group, no member or max_prefix_len < block_size, and for shapes other
+ * than bf16 / head_dim 128 / block 16 / G <= 8, the call is the plain
+ * decode.  Workspace: qwen2_attn_decode_cascade_workspace_size(...) bytes,
+ * scratch as for the plain decode (it holds, besides the decode's part, the
+ * prefix chunk states: about 16 chunks x num_seqs x num_heads x 520 bytes).
+ * Calls that share one workspace must not overlap.  Errors as for
+ * qwen2_attn_decode_paged, plus QW_ERR_NULL for NULL group arrays with
+ * num_prefixes > 0 and QW_ERR_SHAPE for negative counts or a prefix-level
+ * grid beyond 2^31 - 2 workgroups.
+ */
+size_t qwen2_attn_decode_cascade_workspace_size(int num_seqs, int max_context_len,
+                                                int max_prefix_len, int num_prefixes,
+                                                int num_prefix_members, int num_heads,
+                                                int num_kv_heads, int head_dim, int block_size,
+                                                int dtype);
+
+int qwen2_attn_decode_paged_cascade(const void* q, int64_t q_row_stride,
+                                    const void* k_cache, const void* v_cache, int num_blocks,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens,
+                                    const int32_t* prefix_indptr, const int32_t* prefix_seqs,
+                                    const int32_t* prefix_lens, int num_prefixes,
+                                    int num_prefix_members, int max_prefix_len,
+                                    void* out, int64_t out_row_stride,
+                                    void* workspace, size_t workspace_bytes,
+                                    int num_seqs, int max_context_len, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, float scale,
+                                    int dtype, hipStream_t stream);
+
+int qwen2_attn_decode_paged_cascade_fp8(const void* q, int64_t q_row_stride,
+                                        const void* k_cache, const void* v_cache, int num_blocks,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens,
+                                        const int32_t* prefix_indptr, const int32_t* prefix_seqs,
+                                        const int32_t* prefix_lens, int num_prefixes,
+                                        int num_prefix_members, int max_prefix_len,
+                                        void* out, int64_t out_row_stride,
+                                        void* workspace, size_t workspace_bytes,
+                                        int num_seqs, int max_context_len, int num_heads,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        float scale, int dtype, float k_scale, float v_scale,
+                                        hipStream_t stream);
+
+/*
+ * Verify the prefix-group contract of the cascade calls on HOST copies
+ * (prefix_indptr [num_prefixes + 1], prefix_seqs [num_prefix_members],
+ * prefix_lens [num_prefixes], context_lens [num_seqs], block_tables
+ * [num_seqs][max_blocks_per_seq]).  Returns QW_OK or QW_ERR_METADATA (first
+ * violation in qwen2_last_error()).  No HIP call is made.
+ */
+int qwen2_check_prefix_groups_host(const int32_t* prefix_indptr, const int32_t* prefix_seqs,
+                                   const int32_t* prefix_lens, int num_prefixes,
+                                   int num_prefix_members, int max_prefix_len,
+                                   const int32_t* context_lens, const int32_t* block_tables,
+                                   int num_seqs, int max_blocks_per_seq, int block_size);
+
+/*
  * Verify the device-metadata contract on HOST copies (tests, debugging).
  * positions, slot_mapping: HOST int32 [num_tokens] (either may be NULL to
  * skip it).  cu_seqlens_q: HOST int32 [num_seqs + 1], or NULL for a decode

@@ -49,6 +49,14 @@ SIGNATURES = {
     "qwen3_rope_cache_write_fp8": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
                                         _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _d, _f, _f,
                                         _p]),
+    "qwen2_attn_decode_cascade_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "qwen2_attn_decode_paged_cascade": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _p, _p, _i, _i,
+                                             _i, _p, _i64, _p, _sz, _i, _i, _i, _i, _i, _i, _f,
+                                             _i, _p]),
+    "qwen2_attn_decode_paged_cascade_fp8": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _p, _p, _i,
+                                                 _i, _i, _p, _i64, _p, _sz, _i, _i, _i, _i, _i,
+                                                 _i, _f, _i, _f, _f, _p]),
+    "qwen2_check_prefix_groups_host": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _i, _i, _i]),
     "qwen2_check_metadata_host": (_i, [_p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i]),
     "qwen2_status_string": (ctypes.c_char_p, [_i]),
     "qwen2_last_error": (ctypes.c_char_p, []),
@@ -350,6 +358,68 @@ def qwen2_check_metadata_host(positions, slot_mapping, cu_seqlens_q, context_len
                                            bt.shape[1], num_blocks, block_size, max_position,
                                            max_context_len, max_query_len))
     del keep1, keep2, keep3, keep4
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix (cascade) decode
+def qwen2_attn_decode_cascade_workspace_size(num_seqs: int, max_context_len: int,
+                                             max_prefix_len: int, num_prefixes: int,
+                                             num_prefix_members: int, num_heads: int,
+                                             num_kv_heads: int, head_dim: int, block_size: int,
+                                             dtype: torch.dtype) -> int:
+    n = lib().qwen2_attn_decode_cascade_workspace_size(
+        num_seqs, max_context_len, max_prefix_len, num_prefixes, num_prefix_members, num_heads,
+        num_kv_heads, head_dim, block_size, QW_BF16 if dtype == torch.bfloat16 else QW_F32)
+    if n == ctypes.c_size_t(-1).value:
+        raise QwenAttnError("qwen2_attn_decode_cascade_workspace_size", 3,
+                            lib().qwen2_last_error().decode())
+    return n
+
+
+def qwen2_attn_decode_paged_cascade(q, k_cache, v_cache, block_tables, context_lens,
+                                    prefix_indptr, prefix_seqs, prefix_lens, max_prefix_len: int,
+                                    out, workspace, max_context_len: int, num_heads: int,
+                                    num_kv_heads: int, head_dim: int, block_size: int,
+                                    scale: float, k_scale=None, v_scale=None,
+                                    stream=None) -> None:
+    """As qwen2_attn_decode_paged, with the decode sequences' shared prefixes
+    given as device int32 prefix_indptr [P+1], prefix_seqs [members],
+    prefix_lens [P] (tokens); k_scale and v_scale select the FP8-cache call."""
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(out, num_heads * head_dim)
+    wp = workspace.data_ptr() if workspace is not None else 0
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    P = prefix_lens.shape[0] if prefix_lens is not None else 0
+    M = prefix_seqs.shape[0] if prefix_seqs is not None else 0
+    args = [qp, qs, k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[0], _i32(block_tables),
+            block_tables.shape[1], _i32(context_lens), _i32(prefix_indptr), _i32(prefix_seqs),
+            _i32(prefix_lens), P, M, int(max_prefix_len), op, os_, wp, wb, q.shape[0],
+            max_context_len, num_heads, num_kv_heads, head_dim, block_size, float(scale),
+            _dtype(q)]
+    if k_scale is None:
+        _check("qwen2_attn_decode_paged_cascade",
+               lib().qwen2_attn_decode_paged_cascade(*args, _stream(stream)))
+    else:
+        _fp8_caches(k_cache, v_cache, num_kv_heads)
+        _check("qwen2_attn_decode_paged_cascade_fp8",
+               lib().qwen2_attn_decode_paged_cascade_fp8(*args, float(k_scale), float(v_scale),
+                                                         _stream(stream)))
+
+
+def qwen2_check_prefix_groups_host(prefix_indptr, prefix_seqs, prefix_lens, max_prefix_len: int,
+                                   context_lens, block_tables, block_size: int) -> None:
+    """Host-side check of the cascade's prefix-group contract on numpy int32
+    arrays.  Raises QwenAttnError on a violation."""
+    ind = np.ascontiguousarray(prefix_indptr, dtype=np.int32)
+    seqs = np.ascontiguousarray(prefix_seqs, dtype=np.int32)
+    lens = np.ascontiguousarray(prefix_lens, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    _check("qwen2_check_prefix_groups_host",
+           lib().qwen2_check_prefix_groups_host(ind.ctypes.data, seqs.ctypes.data, lens.ctypes.data,
+                                                len(lens), len(seqs), int(max_prefix_len),
+                                                ctx.ctypes.data, bt.ctypes.data, len(ctx),
+                                                bt.shape[1], block_size))
 
 
 def status_string(status: int) -> str:

@@ -137,6 +137,10 @@ struct DecodeKArgs {
   int* jobs;              // ranges whose first piece ends a shared segment (count in claim[2])
   float scale_log2;   // scale * log2 e (* k_scale with an FP8 cache)
   float out_scale;    // 1, or v_scale with an FP8 cache
+  // shared-prefix cascade (unused by the plain decode)
+  int2* cas;              // per sequence: prefix blocks it skips, prefix chunks to fold in
+  float* pre_ml;          // [chunk][S H][2]: prefix chunk states (reference max, sum)
+  float* pre_acc;         // [chunk][S H][128]: prefix chunk partial outputs
 };
 
 // Context lengths are clamped to [1, max_context_len] (what the workspace
@@ -144,6 +148,14 @@ struct DecodeKArgs {
 // sequence's output NaN.
 __device__ __forceinline__ int clamp_ctx(int c, int maxc) { return c < 1 ? 1 : (c > maxc ? maxc : c); }
 __device__ __forceinline__ int nblocks_of(int c) { return (c + kBlk - 1) / kBlk; }
+// blocks of sequence s that the stream kernel attends: all of them, or in a
+// cascade those after the shared prefix (at least one)
+template <bool CAS>
+__device__ __forceinline__ int seg_blocks(const DecodeKArgs& a, int s) {
+  const int n = nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len));
+  if constexpr (CAS) return n - a.cas[s].x;
+  return n;
+}
 
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), l);
@@ -160,11 +172,12 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 }
 
 // U = Hkv * sum_s n_s (n_s = blocks of sequence s); the same in every lane
+template <bool CAS>
 __device__ int64_t total_units(const DecodeKArgs& a, int lane) {
   int64_t t = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int s = base + lane;
-    const int n = s < a.num_seqs ? nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len)) : 0;
+    const int n = s < a.num_seqs ? seg_blocks<CAS>(a, s) : 0;
     t += readlane64(wave_incl_scan(n, lane), 63);
   }
   return t * a.num_kv_heads;
@@ -176,6 +189,7 @@ struct Cursor {
   int s, g, b, n;
   int64_t seg0;
 };
+template <bool CAS>
 __device__ Cursor locate(const DecodeKArgs& a, int64_t u, int lane) {
   const int Hkv = a.num_kv_heads;
   int64_t run = 0;                   // blocks of the sequences before this chunk
@@ -183,7 +197,7 @@ __device__ Cursor locate(const DecodeKArgs& a, int64_t u, int lane) {
   for (int base = 0; base < a.num_seqs; base += 64) {
     const int s = base + lane;
     const bool in = s < a.num_seqs;
-    const int n = in ? nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len)) : 0;
+    const int n = in ? seg_blocks<CAS>(a, s) : 0;
     const int64_t incl = run + wave_incl_scan(n, lane);        // blocks up to and with s
     const uint64_t hit = __builtin_amdgcn_ballot_w64(in && static_cast<int64_t>(Hkv) * incl > u);
     if (hit) {
@@ -242,9 +256,50 @@ __device__ int64_t range_of(const Schedule& sc, int64_t u, int64_t U) {
   return first - 1;
 }
 
+// Cascade: fold the shared-prefix chunk states of (sequence s, query head
+// qh) into a state (M, L, o) of its private keys (log2 domain, M finite):
+//   M' = max(M, m_c),  L' = L 2^(M - M') + sum_c l_c 2^(m_c - M'),  o' likewise.
+// Chunks are loaded kFoldBatch at a time, all loads of a batch in flight.
+constexpr int kFoldBatch = 8;
+__device__ __forceinline__ void fold_prefix(const DecodeKArgs& a, int s, int qh, int e, float& M,
+                                            float& L, float& o) {
+  const int nc = a.cas[s].y;
+  const int64_t row = static_cast<int64_t>(s) * a.num_heads + qh;
+  const int64_t cstride = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+  for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
+    float pm[kFoldBatch], pl[kFoldBatch], pv[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const int64_t r = (c0 + i < nc ? c0 + i : c0) * cstride + row;
+      pm[i] = a.pre_ml[r * 2];
+      pl[i] = a.pre_ml[r * 2 + 1];
+      pv[i] = a.pre_acc[r * kD + e];
+    }
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i)
+      if (c0 + i < nc) Mn = fmaxf(Mn, pm[i]);
+    const float f = __builtin_amdgcn_exp2f(M - Mn);
+    L *= f;
+    o *= f;
+    M = Mn;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      if (c0 + i < nc) {
+        const float wt = __builtin_amdgcn_exp2f(pm[i] - M);
+        L = fmaf(pl[i], wt, L);
+        o = fmaf(pv[i], wt, o);
+      }
+    }
+  }
+}
+
 // F8: the caches hold E4M3FN codes (K tile 2 KiB, V tile 2 KiB); they are
 // widened to bf16 in registers and the same arithmetic follows.
-template <int G, bool F8>
+// CAS: a cascade's private level (each sequence's keys after its shared
+// prefix; the prefix chunk states are folded in where a segment's output is
+// written).
+template <int G, bool F8, bool CAS>
 __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) {
   constexpr int kEl = F8 ? 1 : 2;                 // bytes per cache element
   constexpr int kTileBytes = kBlk * kD * kEl;
@@ -252,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int Hkv = a.num_kv_heads;
-  const int64_t U = total_units(a, lane);
+  const int64_t U = total_units<CAS>(a, lane);
   const Schedule sched = schedule_for(a, U);
 
   // per-wave softmax states of a piece, merged at its end
@@ -288,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   if (u0 >= u1) {
     if (tid == 0) a.desc[rg] = make_int4(-1, kRangeEmpty, 0, 0);
   } else {
-  Cursor cur = locate(a, u0, lane);
+  Cursor cur = locate<CAS>(a, u0, lane);
   if (tid == 0) {
     // the segment of this range's first piece: does this range end it after
     // it began in an earlier range?  Then the merge combines ranges ra..rg.
@@ -312,7 +367,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
     const int ctx_raw = a.context_lens[s];
     bool bad = ctx_raw < 1 || ctx_raw > a.max_context_len;
     const int ctx = clamp_ctx(ctx_raw, a.max_context_len);
-    const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks + b0 + wave;
+    const int kb0 = b0 + (CAS ? a.cas[s].x : 0);   // the piece's first block in the table
+    const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks + kb0 + wave;
 
     // this wave's block ids, 64 at a time: lane i of ids_c holds its block
     // cbase + i, of ids_n its block cbase + 64 + i
@@ -392,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
         sc = mfma_16x16x32_bf16(kf, qf[cc], sc);
       }
       // keys past the context (slots there may hold NaN) are excluded by select
-      const int t0 = (b0 + wave + kNW * i) * kBlk + j4 * 4;
+      const int t0 = (kb0 + wave + kNW * i) * kBlk + j4 * 4;
       float z[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) z[e] = t0 + e < ctx ? sc[e] : -INFINITY;
@@ -497,6 +553,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
       }
       if (whole) {                       // the whole segment: final output
         const int qh = g * G + h;
+        if constexpr (CAS) fold_prefix(a, s, qh, e, M, L, v);
         a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
             f32_to_bf16(pbad ? __builtin_nanf("") : v * a.out_scale / L);
       } else {                           // a share of the segment: partial state
@@ -515,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
     if (++cur.g == Hkv) {
       cur.g = 0;
       ++cur.s;
-      cur.n = nblocks_of(clamp_ctx(a.context_lens[cur.s], a.max_context_len));
+      cur.n = seg_blocks<CAS>(a, cur.s);
     }
   }
   }
@@ -537,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
 // ranges' empty flags, (m, l), the partial outputs) in flight together, and
 // the running sums are rescaled when the maximum moves.
 constexpr int kMergeBatch = 16;
-template <int G>
+template <int G, bool CAS>
 __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
   const int tid = threadIdx.x;
   const int njobs = a.claim[2];          // written by the stream kernel
@@ -581,8 +638,232 @@ __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
       }
     }
   }
+  if constexpr (CAS) fold_prefix(a, d.z, d.w * G + h, e, M, L, o);
   a.out[static_cast<int64_t>(d.z) * a.out_stride + static_cast<int64_t>(d.w * G + h) * kD + e] =
       f32_to_bf16(o * a.out_scale / L);
+  }
+}
+
+// ---- shared-prefix cascade: the prefix level ----
+//
+// Group p's members are seqs[indptr[p] .. indptr[p + 1]); its prefix is the
+// first lens[p] tokens (whole blocks) of each, held in the same physical
+// blocks, which are read through the first member's block table.  The
+// group's (member, query head) pairs of KV head g form cols = members x G
+// columns; column col is member col / G, query head g G + col % G.  The
+// prefix blocks are cut into chunks of chunk_blocks; task (p, g, chunk) x
+// four column tiles is one workgroup, wave w taking the 16 columns
+// 16 (4 xc + w) .. of the tile group xc.  Each wave attends its 16 columns to
+// the chunk's blocks with the decode's tile math (S^T = K Q^T, lazy online
+// softmax, O^T += V^T P^T); only the 16 columns now belong to 16 different
+// (sequence, head) pairs, so no MFMA column is padding once a group has 16
+// of them.  The chunk state (reference max, sum, partial output) goes to row
+// chunk (S H) + s H + qh of the prefix state arrays.
+//
+// A group is attended only when it is well formed: 0 < lens[p] <= the
+// host's max_prefix_len, whole blocks, first member in range with a key after
+// the prefix.  A member gets the cascade (cas[s] = (prefix blocks, chunks))
+// only when its group is attended and it has a key after the prefix;
+// every other sequence is decoded over its whole table.
+struct CascadeArgs {
+  const int32_t* indptr;   // [P + 1]
+  const int32_t* seqs;     // [members]
+  const int32_t* lens;     // [P] prefix tokens
+  int num_prefixes, num_members, max_prefix_len;
+  int chunk_blocks, max_chunks, col_wgs;
+};
+
+__device__ __forceinline__ int group_prefix_blocks(const DecodeKArgs& a, const CascadeArgs& ca,
+                                                   int p) {
+  const int L = ca.lens[p];
+  if (L <= 0 || L > ca.max_prefix_len || L % kBlk) return 0;
+  const int i0 = ca.indptr[p];
+  if (i0 < 0 || i0 >= ca.num_members || ca.indptr[p + 1] <= i0 ||
+      ca.indptr[p + 1] > ca.num_members)
+    return 0;
+  const int s0 = ca.seqs[i0];
+  if (s0 < 0 || s0 >= a.num_seqs) return 0;
+  const int PB = L / kBlk;
+  return PB < nblocks_of(clamp_ctx(a.context_lens[s0], a.max_context_len)) ? PB : 0;
+}
+
+// workgroup 0: zero the range and job counters and set cas[] for the
+// private level
+__device__ void cascade_prep(const DecodeKArgs& a, const CascadeArgs& ca) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    a.claim[0] = 0;
+    a.claim[2] = 0;
+  }
+  for (int s = tid; s < a.num_seqs; s += kThreads) a.cas[s] = make_int2(0, 0);
+  __syncthreads();
+  for (int i = tid; i < ca.num_members; i += kThreads) {
+    // the group of member i: the last p with indptr[p] <= i
+    int lo = 0, hi = ca.num_prefixes - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ca.indptr[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    if (ca.indptr[lo] > i || ca.indptr[lo + 1] <= i) continue;
+    const int PB = group_prefix_blocks(a, ca, lo);
+    const int s = ca.seqs[i];
+    if (PB == 0 || s < 0 || s >= a.num_seqs) continue;
+    if (PB >= nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len))) continue;
+    a.cas[s] = make_int2(PB, (PB + ca.chunk_blocks - 1) / ca.chunk_blocks);
+  }
+}
+
+template <int G, bool F8>
+__global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, CascadeArgs ca) {
+  if (blockIdx.x == 0) {
+    cascade_prep(a, ca);
+    return;
+  }
+  constexpr int kEl = F8 ? 1 : 2;
+  constexpr int kTileBytes = kBlk * kD * kEl;
+  constexpr int kKLoads = F8 ? 2 : 4;
+  using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const int task = blockIdx.x - 1;
+  const int xc = task % ca.col_wgs;
+  int y = task / ca.col_wgs;
+  const int chunk = y % ca.max_chunks;
+  y /= ca.max_chunks;
+  const int g = y % a.num_kv_heads;
+  const int p = y / a.num_kv_heads;
+  const int PB = group_prefix_blocks(a, ca, p);
+  const int i0 = ca.indptr[p];
+  const int cols = (ca.indptr[p + 1] - i0) * G;
+  const int col0 = (xc * kNW + wave) * 16;
+  const int bb = chunk * ca.chunk_blocks;
+  const int be = min(PB, bb + ca.chunk_blocks);
+  if (PB == 0 || col0 >= cols || bb >= be) return;    // uniform per wave
+  const int nb = be - bb;                              // <= 64 blocks
+
+  // this lane's column: (member sequence s, query head qh)
+  const int col = col0 + r16;
+  int s = col < cols ? ca.seqs[i0 + col / G] : -1;
+  if (s >= a.num_seqs) s = -1;
+  const int qh = g * G + col % G;
+  uint4 qf[4];
+  {
+    const uint16_t* qp = a.q + static_cast<int64_t>(s < 0 ? 0 : s) * a.q_stride +
+                         static_cast<int64_t>(qh) * kD;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int d = F8 ? (cc >> 1) * 64 + j4 * 16 + (cc & 1) * 8 : cc * 32 + j4 * 8;
+      qf[cc] = s >= 0 ? *reinterpret_cast<const uint4*>(qp + d) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // the chunk's block ids, lane i holding block bb + i
+  const int s0 = ca.seqs[i0];
+  const int ids = lane < nb ? a.block_tables[static_cast<int64_t>(s0) * a.max_blocks + bb + lane] : 0;
+  const int koff = r16 * kD * kEl + j4 * 16;
+  const int voff = (r16 * kBlk + j4 * 4) * kEl;
+  const float c = a.scale_log2;
+  bool bad = false;
+
+  auto issue = [&](int i, uint4 (&kb)[kKLoads], VWord (&vb)[8]) {
+    const bool live = i < nb;
+    int id = live ? __builtin_amdgcn_readlane(ids, i) : 0;
+    if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) {
+      bad = true;
+      id = 0;
+    }
+    const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
+                                                      static_cast<short>(0),
+                                                      live ? kTileBytes : 0, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
+                                                      static_cast<short>(0),
+                                                      live ? kTileBytes : 0, kBufferFlags);
+#pragma unroll
+    for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16(rk, koff + cc * 64);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if constexpr (F8)
+        vb[t] = ld_buf4(rv, voff + t * 16 * kBlk);
+      else
+        vb[t] = ld_buf8(rv, voff + t * 16 * kBlk * 2);
+    }
+  };
+
+  float ms = -INFINITY, l = 0.0f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  // every prefix key lies inside every member's context: no masking
+  auto block = [&](const uint4 (&kb)[kKLoads], const VWord (&vb)[8]) {
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      uint4 kf;
+      if constexpr (F8)
+        kf = fp8x8_to_bf16x8((cc & 1) ? make_uint2(kb[cc >> 1].z, kb[cc >> 1].w)
+                                      : make_uint2(kb[cc >> 1].x, kb[cc >> 1].y));
+      else
+        kf = kb[cc];
+      sc = mfma_16x16x32_bf16(kf, qf[cc], sc);
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float bms = bm * c;
+    const bool up = bms > ms + kLazy;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(ms - bms) : 1.0f;
+      ms = up ? bms : ms;
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    }
+    const float nm = -ms;
+    uint2 pp;
+    pp.x = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[0], c, nm)),
+                       __builtin_amdgcn_exp2f(fmaf(sc[1], c, nm)));
+    pp.y = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(sc[2], c, nm)),
+                       __builtin_amdgcn_exp2f(fmaf(sc[3], c, nm)));
+    l += (bf16_lo(pp.x) + bf16_hi(pp.x)) + (bf16_lo(pp.y) + bf16_hi(pp.y));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint2 vf;
+      if constexpr (F8)
+        vf = make_uint2(fp8x2_to_bf16x2<false>(vb[t]), fp8x2_to_bf16x2<true>(vb[t]));
+      else
+        vf = vb[t];
+      acc[t] = mfma_16x16x16_bf16(vf, pp, acc[t]);
+    }
+  };
+
+  // two tiles in flight: blocks i and i + 1
+  uint4 kb0[kKLoads], kb1[kKLoads];
+  VWord vb0[8], vb1[8];
+  issue(0, kb0, vb0);
+  for (int i = 0; i < nb; i += 2) {
+    issue(i + 1, kb1, vb1);
+    block(kb0, vb0);
+    issue(i + 2, kb0, vb0);
+    if (i + 1 < nb) block(kb1, vb1);
+  }
+
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (s >= 0) {
+    const int64_t row = static_cast<int64_t>(chunk) * a.num_seqs * a.num_heads +
+                        static_cast<int64_t>(s) * a.num_heads + qh;
+    float* pa = a.pre_acc + row * kD;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      *reinterpret_cast<float4*>(pa + t * 16 + j4 * 4) =
+          make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    if (j4 == 0) {
+      float* pm = a.pre_ml + row * 2;
+      pm[0] = ms;
+      pm[1] = bad ? __builtin_nanf("") : l;
+    }
   }
 }
 
@@ -629,16 +910,15 @@ static void launch_stream(const DecodeKArgs& k, const AttnArgs& a, hipStream_t s
   const int grid = k.num_ranges < kCUs ? k.num_ranges : kCUs;
   hipLaunchKernelGGL(decode_claim_reset_kernel, dim3(1), dim3(64), 0, stream, k.claim);
   if (a.cache_fp8)
-    hipLaunchKernelGGL((decode_stream_kernel<G, true>), dim3(grid), dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_stream_kernel<G, true, false>), dim3(grid), dim3(kThreads), 0, stream, k);
   else
-    hipLaunchKernelGGL((decode_stream_kernel<G, false>), dim3(grid), dim3(kThreads), 0, stream, k);
-  hipLaunchKernelGGL((decode_merge_kernel<G>), dim3(grid), dim3(G * kD), 0, stream, k);
+    hipLaunchKernelGGL((decode_stream_kernel<G, false, false>), dim3(grid), dim3(kThreads), 0, stream, k);
+  hipLaunchKernelGGL((decode_merge_kernel<G, false>), dim3(grid), dim3(G * kD), 0, stream, k);
 }
 
-hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t stream) {
-  if (!p.fast) return launch_attn_generic(a, stream);
-  const int G = a.num_heads / a.num_kv_heads;
+static DecodeKArgs make_kargs(const AttnArgs& a) {
   DecodeKArgs k{};
+  const int G = a.num_heads / a.num_kv_heads;
   k.q = static_cast<const uint16_t*>(a.q);
   k.q_stride = a.q_stride;
   k.k_cache = static_cast<const uint8_t*>(a.k_cache);
@@ -658,13 +938,20 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
   for (int t = 0; t < kTiers; ++t) k.num_ranges += k.tier_wgs[t];
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
-  k.claim = static_cast<int*>(a.workspace);
-  k.desc = reinterpret_cast<int4*>(static_cast<uint8_t*>(a.workspace) + kWsHeader);
-  k.jobs = reinterpret_cast<int*>(static_cast<uint8_t*>(a.workspace) + kWsHeader +
-                                   desc_bytes(k.num_ranges));
-  k.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(a.workspace) + kWsHeader +
-                                      desc_bytes(k.num_ranges) + jobs_bytes(k.num_ranges));
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  k.claim = reinterpret_cast<int*>(ws);
+  k.desc = reinterpret_cast<int4*>(ws + kWsHeader);
+  k.jobs = reinterpret_cast<int*>(ws + kWsHeader + desc_bytes(k.num_ranges));
+  k.ws_acc = reinterpret_cast<float*>(ws + kWsHeader + desc_bytes(k.num_ranges) +
+                                      jobs_bytes(k.num_ranges));
   k.ws_ml = k.ws_acc + static_cast<size_t>(2) * k.num_ranges * G * kD;
+  return k;
+}
+
+hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t stream) {
+  if (!p.fast) return launch_attn_generic(a, stream);
+  const int G = a.num_heads / a.num_kv_heads;
+  const DecodeKArgs k = make_kargs(a);
   switch (G) {
     case 1: launch_stream<1>(k, a, stream); break;
     case 2: launch_stream<2>(k, a, stream); break;
@@ -674,6 +961,81 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& p, hipStream_t str
     case 6: launch_stream<6>(k, a, stream); break;
     case 7: launch_stream<7>(k, a, stream); break;
     default: launch_stream<8>(k, a, stream); break;
+  }
+  return hipGetLastError();
+}
+
+// ---- cascade plan and launch ----
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+CascadePlan plan_cascade(int num_seqs, int max_context_len, int max_prefix_len, int num_members,
+                         int num_prefixes, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int dtype, int cache_fp8) {
+  CascadePlan c{};
+  c.dec = plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                      dtype, cache_fp8);
+  c.ws_bytes = c.dec.ws_bytes;
+  const int max_pb = max_prefix_len / kBlk;
+  c.active = c.dec.fast && max_pb > 0 && num_members > 0 && num_prefixes > 0;
+  if (!c.active) return c;
+  const int G = num_heads / num_kv_heads;
+  int cb = (max_pb + 15) / 16;            // about 16 chunks of 8..64 blocks
+  cb = cb < 8 ? 8 : (cb > 64 ? 64 : cb);
+  c.chunk_blocks = cb;
+  c.max_chunks = (max_pb + cb - 1) / cb;
+  c.col_wgs = static_cast<int>((static_cast<int64_t>(num_members) * G + 16 * kNW - 1) / (16 * kNW));
+  c.tasks = static_cast<int64_t>(c.col_wgs) * num_prefixes * num_kv_heads * c.max_chunks;
+  const size_t rows = static_cast<size_t>(c.max_chunks) * num_seqs * num_heads;
+  c.cas_off = round256(c.dec.ws_bytes);
+  c.pre_ml_off = c.cas_off + round256(static_cast<size_t>(num_seqs) * sizeof(int2));
+  c.pre_acc_off = c.pre_ml_off + round256(rows * 2 * sizeof(float));
+  c.ws_bytes = c.pre_acc_off + rows * kD * sizeof(float);
+  return c;
+}
+
+template <int G>
+static void launch_cascade_g(const DecodeKArgs& k, const CascadeArgs& ca, int64_t tasks,
+                             const AttnArgs& a, hipStream_t stream) {
+  const int grid = k.num_ranges < kCUs ? k.num_ranges : kCUs;
+  const dim3 pgrid(static_cast<unsigned>(1 + tasks));
+  if (a.cache_fp8) {
+    hipLaunchKernelGGL((decode_prefix_kernel<G, true>), pgrid, dim3(kThreads), 0, stream, k, ca);
+    hipLaunchKernelGGL((decode_stream_kernel<G, true, true>), dim3(grid), dim3(kThreads), 0, stream, k);
+  } else {
+    hipLaunchKernelGGL((decode_prefix_kernel<G, false>), pgrid, dim3(kThreads), 0, stream, k, ca);
+    hipLaunchKernelGGL((decode_stream_kernel<G, false, true>), dim3(grid), dim3(kThreads), 0, stream, k);
+  }
+  hipLaunchKernelGGL((decode_merge_kernel<G, true>), dim3(grid), dim3(G * kD), 0, stream, k);
+}
+
+hipError_t launch_decode_cascade(const AttnArgs& a, const CascadeMeta& m, const CascadePlan& p,
+                                 hipStream_t stream) {
+  if (!p.active) return launch_decode(a, p.dec, stream);
+  const int G = a.num_heads / a.num_kv_heads;
+  DecodeKArgs k = make_kargs(a);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  k.cas = reinterpret_cast<int2*>(ws + p.cas_off);
+  k.pre_ml = reinterpret_cast<float*>(ws + p.pre_ml_off);
+  k.pre_acc = reinterpret_cast<float*>(ws + p.pre_acc_off);
+  CascadeArgs ca{};
+  ca.indptr = m.indptr;
+  ca.seqs = m.seqs;
+  ca.lens = m.lens;
+  ca.num_prefixes = m.num_prefixes;
+  ca.num_members = m.num_members;
+  ca.max_prefix_len = m.max_prefix_len;
+  ca.chunk_blocks = p.chunk_blocks;
+  ca.max_chunks = p.max_chunks;
+  ca.col_wgs = p.col_wgs;
+  switch (G) {
+    case 1: launch_cascade_g<1>(k, ca, p.tasks, a, stream); break;
+    case 2: launch_cascade_g<2>(k, ca, p.tasks, a, stream); break;
+    case 3: launch_cascade_g<3>(k, ca, p.tasks, a, stream); break;
+    case 4: launch_cascade_g<4>(k, ca, p.tasks, a, stream); break;
+    case 5: launch_cascade_g<5>(k, ca, p.tasks, a, stream); break;
+    case 6: launch_cascade_g<6>(k, ca, p.tasks, a, stream); break;
+    case 7: launch_cascade_g<7>(k, ca, p.tasks, a, stream); break;
+    default: launch_cascade_g<8>(k, ca, p.tasks, a, stream); break;
   }
   return hipGetLastError();
 }

@@ -54,6 +54,28 @@ struct DecodePlan {
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
                        int head_dim, int block_size, int dtype, int cache_fp8);
 
+// shared-prefix cascade decode: the prefix groups (device arrays) and the
+// plan (the private level's decode plan, chunking of the prefix level,
+// workspace layout after the decode's own part)
+struct CascadeMeta {
+  const int32_t* indptr;   // [num_prefixes + 1]
+  const int32_t* seqs;     // [num_members]
+  const int32_t* lens;     // [num_prefixes], tokens
+  int num_prefixes, num_members, max_prefix_len;
+};
+struct CascadePlan {
+  DecodePlan dec;
+  bool active;             // else the plain decode runs (same result)
+  int chunk_blocks, max_chunks, col_wgs;
+  int64_t tasks;           // prefix-level workgroups (plus one for the set-up)
+  size_t cas_off, pre_ml_off, pre_acc_off, ws_bytes;
+};
+CascadePlan plan_cascade(int num_seqs, int max_context_len, int max_prefix_len, int num_members,
+                         int num_prefixes, int num_heads, int num_kv_heads, int head_dim,
+                         int block_size, int dtype, int cache_fp8);
+hipError_t launch_decode_cascade(const AttnArgs& a, const CascadeMeta& m, const CascadePlan& p,
+                                 hipStream_t stream);
+
 hipError_t launch_rope_table(double* tab, int max_position, int rotary_dim, double theta,
                              hipStream_t stream);
 hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream);

@@ -343,6 +343,28 @@ size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int n
                          dtype, 0).ws_bytes;
 }
 
+static qw::AttnArgs decode_args(const void* q, int64_t q_row_stride, const void* k_cache,
+                                const void* v_cache, int num_blocks, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                                int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                                int num_seqs, int max_context_len, int num_heads,
+                                int num_kv_heads, int head_dim, int block_size, float scale,
+                                int dtype, int cache_fp8, float k_scale, float v_scale) {
+  qw::AttnArgs a{};
+  a.q = q; a.q_stride = q_row_stride;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.num_blocks = num_blocks;
+  a.cu_seqlens = nullptr; a.context_lens = context_lens;
+  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq;
+  a.out = out; a.out_stride = out_row_stride;
+  a.num_seqs = num_seqs; a.num_tokens = num_seqs; a.max_query_len = 1;
+  a.max_context_len = max_context_len;
+  a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
+  a.block_size = block_size; a.scale = scale; a.dtype = dtype;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
+  return a;
+}
+
 static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
                        const void* v_cache, int num_blocks, const int32_t* block_tables,
                        int max_blocks_per_seq, const int32_t* context_lens, void* out,
@@ -373,18 +395,11 @@ static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
       return fail(QW_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
     if (!aligned16(workspace)) return fail(QW_ERR_ALIGN, "workspace is not 16-byte aligned");
   }
-  qw::AttnArgs a{};
-  a.q = q; a.q_stride = q_row_stride;
-  a.k_cache = k_cache; a.v_cache = v_cache; a.num_blocks = num_blocks;
-  a.cu_seqlens = nullptr; a.context_lens = context_lens;
-  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq;
-  a.out = out; a.out_stride = out_row_stride;
-  a.num_seqs = num_seqs; a.num_tokens = num_seqs; a.max_query_len = 1;
-  a.max_context_len = max_context_len;
-  a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
-  a.block_size = block_size; a.scale = scale; a.dtype = dtype;
-  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-  a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
+  const qw::AttnArgs a = decode_args(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                                     max_blocks_per_seq, context_lens, out, out_row_stride,
+                                     workspace, workspace_bytes, num_seqs, max_context_len,
+                                     num_heads, num_kv_heads, head_dim, block_size, scale, dtype,
+                                     cache_fp8, k_scale, v_scale);
   return launched(qw::launch_decode(a, plan, stream));
 }
 
@@ -412,6 +427,159 @@ int qwen2_attn_decode_paged_fp8(const void* q, int64_t q_row_stride, const void*
                      max_blocks_per_seq, context_lens, out, out_row_stride, workspace,
                      workspace_bytes, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
                      block_size, scale, dtype, 1, k_scale, v_scale, stream);
+}
+
+size_t qwen2_attn_decode_cascade_workspace_size(int num_seqs, int max_context_len,
+                                                int max_prefix_len, int num_prefixes,
+                                                int num_prefix_members, int num_heads,
+                                                int num_kv_heads, int head_dim, int block_size,
+                                                int dtype) {
+  if (num_seqs < 0 || max_context_len < 1 || max_prefix_len < 0 || num_prefixes < 0 ||
+      num_prefix_members < 0)
+    return static_cast<size_t>(-1);
+  if (check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype)) return static_cast<size_t>(-1);
+  return qw::plan_cascade(num_seqs, max_context_len, max_prefix_len, num_prefix_members,
+                          num_prefixes, num_heads, num_kv_heads, head_dim, block_size, dtype, 0)
+      .ws_bytes;
+}
+
+static int cascade_impl(const void* q, int64_t q_row_stride, const void* k_cache,
+                        const void* v_cache, int num_blocks, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens,
+                        const int32_t* prefix_indptr, const int32_t* prefix_seqs,
+                        const int32_t* prefix_lens, int num_prefixes, int num_prefix_members,
+                        int max_prefix_len, void* out, int64_t out_row_stride, void* workspace,
+                        size_t workspace_bytes, int num_seqs, int max_context_len, int num_heads,
+                        int num_kv_heads, int head_dim, int block_size, float scale, int dtype,
+                        int cache_fp8, float k_scale, float v_scale, hipStream_t stream) {
+  if (num_prefixes < 0 || num_prefix_members < 0 || max_prefix_len < 0)
+    return fail(QW_ERR_SHAPE, "negative prefix-group size (num_prefixes=%d members=%d max_prefix_len=%d)",
+                num_prefixes, num_prefix_members, max_prefix_len);
+  if (num_prefixes > 0 && (!prefix_indptr || !prefix_lens))
+    return fail(QW_ERR_NULL, "prefix_indptr/prefix_lens is NULL");
+  if (num_prefix_members > 0 && !prefix_seqs) return fail(QW_ERR_NULL, "prefix_seqs is NULL");
+  if (cache_fp8) {
+    const int st = check_fp8_scales(k_scale, v_scale);
+    if (st) return st;
+  }
+  if (num_seqs < 0) return fail(QW_ERR_SHAPE, "num_seqs=%d < 0", num_seqs);
+  if (num_seqs > 65535) return fail(QW_ERR_UNSUPPORTED, "num_seqs=%d > 65535", num_seqs);
+  if (num_seqs == 0) {
+    int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
+    return st ? st : ok();
+  }
+  int st = check_attn_common(q, q_row_stride, k_cache, v_cache, num_blocks, context_lens,
+                             block_tables, max_blocks_per_seq, out, out_row_stride, num_seqs,
+                             max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                             scale, dtype);
+  if (st) return st;
+  const qw::CascadePlan plan =
+      qw::plan_cascade(num_seqs, max_context_len, max_prefix_len, num_prefix_members,
+                       num_prefixes, num_heads, num_kv_heads, head_dim, block_size, dtype,
+                       cache_fp8);
+  if (plan.active && plan.tasks > 2147483646LL - 1)
+    return fail(QW_ERR_SHAPE, "prefix level needs %lld workgroups", static_cast<long long>(plan.tasks));
+  if (plan.ws_bytes > 0) {
+    if (!workspace) return fail(QW_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.ws_bytes);
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(QW_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
+    if (!aligned16(workspace)) return fail(QW_ERR_ALIGN, "workspace is not 16-byte aligned");
+  }
+  const qw::AttnArgs a = decode_args(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                                     max_blocks_per_seq, context_lens, out, out_row_stride,
+                                     workspace, workspace_bytes, num_seqs, max_context_len,
+                                     num_heads, num_kv_heads, head_dim, block_size, scale, dtype,
+                                     cache_fp8, k_scale, v_scale);
+  qw::CascadeMeta m{};
+  m.indptr = prefix_indptr;
+  m.seqs = prefix_seqs;
+  m.lens = prefix_lens;
+  m.num_prefixes = num_prefixes;
+  m.num_members = num_prefix_members;
+  m.max_prefix_len = max_prefix_len;
+  return launched(qw::launch_decode_cascade(a, m, plan, stream));
+}
+
+int qwen2_attn_decode_paged_cascade(const void* q, int64_t q_row_stride, const void* k_cache,
+                                    const void* v_cache, int num_blocks,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, const int32_t* prefix_indptr,
+                                    const int32_t* prefix_seqs, const int32_t* prefix_lens,
+                                    int num_prefixes, int num_prefix_members, int max_prefix_len,
+                                    void* out, int64_t out_row_stride, void* workspace,
+                                    size_t workspace_bytes, int num_seqs, int max_context_len,
+                                    int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                    float scale, int dtype, hipStream_t stream) {
+  return cascade_impl(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                      max_blocks_per_seq, context_lens, prefix_indptr, prefix_seqs, prefix_lens,
+                      num_prefixes, num_prefix_members, max_prefix_len, out, out_row_stride,
+                      workspace, workspace_bytes, num_seqs, max_context_len, num_heads,
+                      num_kv_heads, head_dim, block_size, scale, dtype, 0, 1.0f, 1.0f, stream);
+}
+
+int qwen2_attn_decode_paged_cascade_fp8(const void* q, int64_t q_row_stride, const void* k_cache,
+                                        const void* v_cache, int num_blocks,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens,
+                                        const int32_t* prefix_indptr, const int32_t* prefix_seqs,
+                                        const int32_t* prefix_lens, int num_prefixes,
+                                        int num_prefix_members, int max_prefix_len, void* out,
+                                        int64_t out_row_stride, void* workspace,
+                                        size_t workspace_bytes, int num_seqs,
+                                        int max_context_len, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, float scale, int dtype,
+                                        float k_scale, float v_scale, hipStream_t stream) {
+  return cascade_impl(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                      max_blocks_per_seq, context_lens, prefix_indptr, prefix_seqs, prefix_lens,
+                      num_prefixes, num_prefix_members, max_prefix_len, out, out_row_stride,
+                      workspace, workspace_bytes, num_seqs, max_context_len, num_heads,
+                      num_kv_heads, head_dim, block_size, scale, dtype, 1, k_scale, v_scale,
+                      stream);
+}
+
+int qwen2_check_prefix_groups_host(const int32_t* prefix_indptr, const int32_t* prefix_seqs,
+                                   const int32_t* prefix_lens, int num_prefixes,
+                                   int num_prefix_members, int max_prefix_len,
+                                   const int32_t* context_lens, const int32_t* block_tables,
+                                   int num_seqs, int max_blocks_per_seq, int block_size) {
+  if (num_prefixes < 0 || num_prefix_members < 0 || num_seqs < 0 || block_size < 1)
+    return fail(QW_ERR_SHAPE, "negative sizes");
+  if (num_prefixes == 0) return num_prefix_members == 0 ? ok()
+                                : fail(QW_ERR_METADATA, "members without a group");
+  if (!prefix_indptr || !prefix_lens || (num_prefix_members > 0 && !prefix_seqs) ||
+      (num_seqs > 0 && (!context_lens || !block_tables)))
+    return fail(QW_ERR_NULL, "NULL host array");
+  if (prefix_indptr[0] != 0 || prefix_indptr[num_prefixes] != num_prefix_members)
+    return fail(QW_ERR_METADATA, "prefix_indptr must run from 0 to %d", num_prefix_members);
+  std::vector<char> seen(static_cast<size_t>(num_seqs), 0);
+  for (int p = 0; p < num_prefixes; ++p) {
+    const int i0 = prefix_indptr[p], i1 = prefix_indptr[p + 1];
+    if (i1 < i0) return fail(QW_ERR_METADATA, "prefix_indptr decreases at group %d", p);
+    const int L = prefix_lens[p];
+    if (L <= 0 || L % block_size || L > max_prefix_len)
+      return fail(QW_ERR_METADATA, "group %d: prefix length %d is not a positive multiple of %d up to %d",
+                  p, L, block_size, max_prefix_len);
+    const int nb = L / block_size;
+    if (nb > max_blocks_per_seq)
+      return fail(QW_ERR_METADATA, "group %d: prefix of %d blocks > max_blocks_per_seq", p, nb);
+    for (int i = i0; i < i1; ++i) {
+      const int s = prefix_seqs[i];
+      if (s < 0 || s >= num_seqs)
+        return fail(QW_ERR_METADATA, "group %d: member %d outside [0, %d)", p, s, num_seqs);
+      if (seen[s]) return fail(QW_ERR_METADATA, "sequence %d is listed twice", s);
+      seen[s] = 1;
+      if (context_lens[s] <= L)
+        return fail(QW_ERR_METADATA, "group %d: member %d has context %d <= prefix %d", p, s,
+                    context_lens[s], L);
+      const int32_t* bt = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
+      const int32_t* b0 = block_tables + static_cast<int64_t>(prefix_seqs[i0]) * max_blocks_per_seq;
+      for (int b = 0; b < nb; ++b)
+        if (bt[b] != b0[b])
+          return fail(QW_ERR_METADATA, "group %d: member %d names block %d at %d, the group %d", p,
+                      s, bt[b], b, b0[b]);
+    }
+  }
+  return ok();
 }
 
 int qwen2_check_metadata_host(const int32_t* positions, const int32_t* slot_mapping, int num_tokens,

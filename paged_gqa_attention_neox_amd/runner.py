@@ -3,8 +3,9 @@
 Uploads a ``workloads.Batch`` to device memory (torch tensors) and calls
 ``qwen2_rope_cache_write`` over every token, then
 ``qwen2_attn_prefill_varlen`` over the prefill sequences and
-``qwen2_attn_decode_paged`` over the decode sequences, all on the current
-stream.  Only marshalling: the arithmetic happens in the HIP library.
+``qwen2_attn_decode_paged`` (or, with cascade=True and prefix groups,
+``qwen2_attn_decode_paged_cascade``) over the decode sequences, all on the
+current stream.  Only marshalling: the arithmetic happens in the HIP library.
 """
 from __future__ import annotations
 
@@ -58,7 +59,7 @@ def rope_table(head_dim: int, theta: float, max_position: int, device="cuda",
 class DeviceStep:
     """Device copies of one batch plus the calls of the step."""
 
-    def __init__(self, batch, device="cuda", k_cache=None, v_cache=None):
+    def __init__(self, batch, device="cuda", k_cache=None, v_cache=None, cascade=False):
         sh = batch.shape
         self.batch = batch
         self.sh = sh
@@ -95,8 +96,17 @@ class DeviceStep:
             ctx, bt = batch.decode_part()
             self.d_ctx, self.d_bt = i32(ctx), i32(bt)
             self.d_max_c = int(ctx.max())
-            ws = B.qwen2_attn_decode_workspace_size(batch.num_decode, self.d_max_c, H, Hkv, d,
-                                                    sh.block_size, self.tdtype)
+            self.cascade = cascade and batch.prefix_groups is not None
+            if self.cascade:
+                ind, seqs, lens = batch.prefix_groups
+                self.pg = (i32(ind), i32(seqs), i32(lens))
+                self.max_prefix = int(np.max(lens))
+                ws = B.qwen2_attn_decode_cascade_workspace_size(
+                    batch.num_decode, self.d_max_c, self.max_prefix, len(lens), len(seqs), H, Hkv,
+                    d, sh.block_size, self.tdtype)
+            else:
+                ws = B.qwen2_attn_decode_workspace_size(batch.num_decode, self.d_max_c, H, Hkv, d,
+                                                        sh.block_size, self.tdtype)
             self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=device) if ws else None
 
     # --- the three calls ---
@@ -130,6 +140,13 @@ class DeviceStep:
         if not self.batch.num_decode:
             return
         sh = self.sh
+        if self.cascade:
+            B.qwen2_attn_decode_paged_cascade(
+                self.q_out[self.Tp:], self.k_cache, self.v_cache, self.d_bt, self.d_ctx, *self.pg,
+                self.max_prefix, self.out[self.Tp:], self.workspace, self.d_max_c, sh.num_heads,
+                sh.num_kv_heads, sh.head_dim, sh.block_size, sh.scale,
+                sh.k_scale if self.fp8 else None, sh.v_scale if self.fp8 else None, stream)
+            return
         args = (self.q_out[self.Tp:], self.k_cache, self.v_cache, self.d_bt, self.d_ctx,
                 self.out[self.Tp:], self.workspace, self.d_max_c, sh.num_heads, sh.num_kv_heads,
                 sh.head_dim, sh.block_size, sh.scale)

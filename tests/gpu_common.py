@@ -27,8 +27,8 @@ def require_gpu():
     B.lib()
 
 
-def run_gpu(batch, k_cache=None, v_cache=None, repeat=1):
-    dev = runner.DeviceStep(batch, k_cache=k_cache, v_cache=v_cache)
+def run_gpu(batch, k_cache=None, v_cache=None, repeat=1, cascade=False):
+    dev = runner.DeviceStep(batch, k_cache=k_cache, v_cache=v_cache, cascade=cascade)
     for _ in range(repeat):
         dev.step()
     return dev.results(), dev

@@ -277,3 +277,94 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix (cascade) decode: argument checks, workspace, host contract
+def _cascade(lib, fp8=False, **kw):
+    a = dict(q=P, qs=28 * 128, kc=P2, vc=P3, nb=100, bt=P, mb=64, ctx=P, ind=P, seqs=P2, lens=P3,
+             np_=1, nm=3, maxp=512, out=P2, os=28 * 128, ws=P3, wsb=1 << 30, S=4, maxc=1024, H=28,
+             Hkv=4, d=128, B=16, scale=0.0884, dt=1)
+    a.update(kw)
+    args = [a["q"], a["qs"], a["kc"], a["vc"], a["nb"], a["bt"], a["mb"], a["ctx"], a["ind"],
+            a["seqs"], a["lens"], a["np_"], a["nm"], a["maxp"], a["out"], a["os"], a["ws"], a["wsb"],
+            a["S"], a["maxc"], a["H"], a["Hkv"], a["d"], a["B"], a["scale"], a["dt"]]
+    if fp8:
+        return lib.qwen2_attn_decode_paged_cascade_fp8(*args, a.get("ksc", 1.0), a.get("vsc", 1.0),
+                                                       None)
+    return lib.qwen2_attn_decode_paged_cascade(*args, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(np_=-1), QW_ERR_SHAPE),
+    (dict(nm=-2), QW_ERR_SHAPE),
+    (dict(maxp=-16), QW_ERR_SHAPE),
+    (dict(ind=0), QW_ERR_NULL),
+    (dict(lens=0), QW_ERR_NULL),
+    (dict(seqs=0), QW_ERR_NULL),
+    (dict(q=0), QW_ERR_NULL),
+    (dict(H=30), QW_ERR_SHAPE),
+    (dict(mb=8), QW_ERR_SHAPE),
+    (dict(ws=0), QW_ERR_WORKSPACE),
+    (dict(wsb=4096), QW_ERR_WORKSPACE),
+    (dict(ws=MIS), QW_ERR_ALIGN),
+    (dict(S=-1), QW_ERR_SHAPE),
+])
+def test_cascade_validation(lib, kw, status):
+    assert _cascade(lib, **kw) == status
+    assert lib.qwen2_last_error().decode()
+
+
+def test_cascade_validation_fp8_and_zero_work(lib):
+    assert _cascade(lib, fp8=True, ksc=0.0) == QW_ERR_SHAPE
+    assert _cascade(lib, fp8=True, vsc=float("inf")) == QW_ERR_SHAPE
+    assert _cascade(lib, S=0, q=0, out=0) == QW_OK
+    assert _cascade(lib, S=0, q=0, out=0, fp8=True) == QW_OK
+
+
+def test_cascade_workspace_size(lib):
+    bf16 = __import__("torch").bfloat16
+    plain = B.qwen2_attn_decode_workspace_size(96, 8192, 14, 2, 128, 16, bf16)
+    # no group, or a prefix shorter than a block: the plain decode's workspace
+    assert B.qwen2_attn_decode_cascade_workspace_size(96, 8192, 0, 0, 0, 14, 2, 128, 16, bf16) == plain
+    assert B.qwen2_attn_decode_cascade_workspace_size(96, 8192, 8, 1, 48, 14, 2, 128, 16, bf16) == plain
+    # a 1024-token prefix: 8 chunks of 8 blocks, one state row per (chunk, sequence, head)
+    n = B.qwen2_attn_decode_cascade_workspace_size(96, 8192, 1024, 1, 48, 14, 2, 128, 16, bf16)
+    assert n >= plain + 8 * 96 * 14 * 130 * 4
+    assert n <= plain + 8 * 96 * 14 * 130 * 4 + 96 * 8 + 4 * 256
+    # chunks stay about 16 for long prefixes, 8..64 blocks each
+    m = B.qwen2_attn_decode_cascade_workspace_size(64, 8192, 4096, 4, 64, 28, 4, 128, 16, bf16)
+    plain64 = B.qwen2_attn_decode_workspace_size(64, 8192, 28, 4, 128, 16, bf16)
+    assert m - plain64 >= 16 * 64 * 28 * 130 * 4
+    assert m - plain64 <= 16 * 64 * 28 * 130 * 4 + 64 * 8 + 4 * 256
+    assert lib.qwen2_attn_decode_cascade_workspace_size(8, 100, -1, 1, 1, 28, 4, 128, 16, 1) == \
+        ctypes.c_size_t(-1).value
+
+
+def test_cascade_host_checker_agrees_with_oracle_contract(lib):
+    """The C host checker and the oracle's check_prefix_groups accept the
+    workloads' groupings and refuse the same broken ones."""
+    import oracle.reference as R
+    for b in (W.mixed_tp2(), W.shared_prompt_decode(num_groups=2, members_per_group=4,
+                                                        prefix_len=512)):
+        ctx, bt = b.decode_part()
+        ind, seqs, lens = b.prefix_groups
+        B.qwen2_check_prefix_groups_host(ind, seqs, lens, int(lens.max()), ctx, bt, 16)
+        R.check_prefix_groups(bt, ctx, ind, seqs, lens, 16)
+    b = W.shared_prompt_decode(num_groups=2, members_per_group=4, prefix_len=512)
+    ctx, bt = b.decode_part()
+    ind, seqs, lens = b.prefix_groups
+    bt_bad = bt.copy()
+    bt_bad[5, 3] = bt_bad[5, 3] + 1 if bt_bad[5, 3] + 1 != bt_bad[4, 3] else bt_bad[5, 3] + 2
+    broken = [
+        (ind, seqs, lens, bt_bad),                                         # member 5 holds another block
+        (ind, np.array([0, 1, 2, 3, 4, 5, 6, 6], np.int32), lens, bt),     # listed twice
+        (ind, seqs, np.array([512, 520], np.int32), bt),                   # partial block
+        (ind, seqs, np.array([512, 4096], np.int32), bt),                  # prefix reaches the context
+        (np.array([0, 3, 8], np.int32), seqs, lens, bt),                   # member 3 in group 0's ids
+    ]
+    for ind_, seqs_, lens_, bt_ in broken:
+        with pytest.raises(B.QwenAttnError):
+            B.qwen2_check_prefix_groups_host(ind_, seqs_, lens_, 4096, ctx, bt_, 16)
+        with pytest.raises(ValueError):
+            R.check_prefix_groups(bt_, ctx, ind_, seqs_, lens_, 16)
