@@ -15,7 +15,8 @@ larger than the 256 MB last-level cache, so every step streams KV from HBM.
 
 Also reported on the same line: Qwen2-7B varlen causal prefill (8 sequences
 of 128..512 tokens) TFLOP/s, the mixed TP=2-share batch in tokens/s, the long
-decode over an FP8 E4M3FN cache, the Qwen3 q/k-norm cache write, plus the
+decode over an FP8 E4M3FN cache, the Qwen3 q/k-norm cache write, the
+shared-prefix (cascade) decode against the plain decode, plus the
 roofline of the decode call and the CPU oracle baseline.
 Prints one JSON line.
 """
@@ -180,6 +181,33 @@ def bench_mixed(steps, warmup):
                 decode_kv_bytes=b.decode_kv_bytes())
 
 
+def bench_cascade(steps, warmup):
+    """Shared-prefix (cascade) decode against the plain decode on the same
+    batches: the shared-system-prompt decode (4 groups x 16 sequences over one
+    4096-token prefix each) and the mixed TP=2 step (48 of its 96 decodes
+    share a 1024-token prefix)."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    out = {}
+    b = W.shared_prompt_decode()
+    plain = runner.DeviceStep(b)
+    plain_ms, _ = _time(plain.decode, steps, warmup)
+    casc = runner.DeviceStep(b, k_cache=plain.k_cache, v_cache=plain.v_cache, cascade=True)
+    casc_ms, _ = _time(casc.decode, steps, warmup)
+    out["shared_prompt"] = dict(plain_ms=plain_ms, cascade_ms=casc_ms,
+                                logical_bytes=b.decode_bytes(),
+                                unique_bytes=b.decode_cascade_bytes())
+    del plain, casc
+    m = W.mixed_tp2()
+    plain = runner.DeviceStep(m)
+    plain_ms, _ = _time(plain.step, steps, warmup)
+    casc = runner.DeviceStep(m, k_cache=plain.k_cache, v_cache=plain.v_cache, cascade=True)
+    casc_ms, _ = _time(casc.step, steps, warmup)
+    out["mixed"] = dict(plain_ms=plain_ms, cascade_ms=casc_ms, tokens=m.num_tokens)
+    return out
+
+
 def cpu_baseline(batch, budget_s=12.0):
     """The CPU oracle (as it stands) on a bounded sample of the same decode
     workload: the rope + cache write of all new tokens once (setup, not
@@ -274,6 +302,10 @@ def main():
         log(f"fp8 decode: step {res['fp8']['step_ms']:.3f} ms (decode {res['fp8']['decode_ms']:.3f})")
         res["qknorm"] = bench_qknorm(args.steps, args.warmup)
         log(f"q/k-norm rope + cache write: {res['qknorm']['ms']:.4f} ms")
+        res["cascade"] = bench_cascade(args.steps, args.warmup)
+        log(f"cascade: shared-prompt decode {res['cascade']['shared_prompt']['cascade_ms']:.3f} ms "
+            f"(plain {res['cascade']['shared_prompt']['plain_ms']:.3f}), mixed step "
+            f"{res['cascade']['mixed']['cascade_ms']:.3f} ms (plain {res['cascade']['mixed']['plain_ms']:.3f})")
         res["ctx131k"] = bench_decode_131k(args.steps, args.warmup)
         log(f"131k decode: step {res['ctx131k']['step_ms']:.3f} ms (decode {res['ctx131k']['decode_ms']:.3f})")
 
@@ -361,6 +393,22 @@ def main():
             "ms": round(qn["ms"], 4),
             "GB/s": round(qn["bytes"] / (qn["ms"] * 1e-3) / 1e9, 2),
             "plain_write_ms": round(res["prefill"]["rope_ms"], 4),
+        }
+    if "cascade" in res:
+        sp, mx = res["cascade"]["shared_prompt"], res["cascade"]["mixed"]
+        out["cascade_decode"] = {
+            "workload": "qwen2-7b decode, 4 groups x 16 sequences sharing a 4096-token prefix "
+                        "each, private suffixes U[256, 2048], seed 7",
+            "plain_decode_ms": round(sp["plain_ms"], 4),
+            "cascade_decode_ms": round(sp["cascade_ms"], 4),
+            "speedup": round(sp["plain_ms"] / sp["cascade_ms"], 3),
+            "logical_kv_GB/s": round(sp["logical_bytes"] / (sp["cascade_ms"] * 1e-3) / 1e9, 2),
+            "unique_bytes_GB/s": round(sp["unique_bytes"] / (sp["cascade_ms"] * 1e-3) / 1e9, 2),
+            "unique_bytes_hbm_frac": round(sp["unique_bytes"] / (sp["cascade_ms"] * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 4),
+            "mixed_step_plain_ms": round(mx["plain_ms"], 4),
+            "mixed_step_cascade_ms": round(mx["cascade_ms"], 4),
+            "mixed_tokens_per_s_cascade": round(mx["tokens"] / (mx["cascade_ms"] * 1e-3), 1),
         }
     if "ctx131k" in res:
         c = res["ctx131k"]
