@@ -589,14 +589,23 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
 // in slot 2 r_a if the segment is r_a's first, else 2 r_a + 1; every later
 // non-empty range's piece is its first (slot 2 r'); empty ranges have none.
 //   M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
-// Workgroup r, one thread per (head, dim).  The merge is bound by memory
-// latency, so pieces are taken 16 at a time with every load of a batch (the
-// ranges' empty flags, (m, l), the partial outputs) in flight together, and
-// the running sums are rescaled when the maximum moves.
+// One workgroup per job (a range whose first piece ends a shared segment),
+// G x 128 threads.  The merge is bound by memory latency: in the first phase
+// thread (quarter qr, head h, dims 4 e4 .. 4 e4 + 3) merges every fourth
+// piece (x = qr, qr + 4, ...), taking them kMergeBatch at a time with every
+// load of a batch (the ranges' empty flags, (m, l), 16 bytes of partial
+// output) in flight together, so a segment of up to 4 kMergeBatch pieces
+// costs one round of loads.  The four quarters' states meet in LDS and
+// thread (h, e) merges them in quarter order: the result depends only on the
+// logical sizes and is bitwise reproducible.
 constexpr int kMergeBatch = 16;
 template <int G, bool CAS>
 __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
+  __shared__ float4 q_o[4][G][kD / 4];
+  __shared__ float q_ml[4][G][2];
   const int tid = threadIdx.x;
+  const int qr = tid / (G * (kD / 4)), qh = (tid / (kD / 4)) % G, e4 = tid % (kD / 4);
+  const int h = tid / kD, e = tid % kD;
   const int njobs = a.claim[2];          // written by the stream kernel
   for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
   const int r = a.jobs[job];
@@ -604,20 +613,21 @@ __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
   const int ra = d.x;
   const bool ra_first = (d.y & kRangeFirst) != 0;
   const int np = r - ra + 1;
-  const int h = tid / kD, e = tid % kD;
-  float M = -INFINITY, L = 0.0f, o = 0.0f;
-  for (int x0 = 0; x0 < np; x0 += kMergeBatch) {
-    float pm[kMergeBatch], pl[kMergeBatch], v[kMergeBatch];
+  float M = -INFINITY, L = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int x0 = qr; x0 < np; x0 += 4 * kMergeBatch) {
+    float pm[kMergeBatch], pl[kMergeBatch];
+    float4 v[kMergeBatch];
     bool live[kMergeBatch];
 #pragma unroll
     for (int q = 0; q < kMergeBatch; ++q) {
-      const int x = x0 + q;
+      const int x = x0 + 4 * q;
       const int rx = ra + (x < np ? x : 0);
-      const int64_t sb = static_cast<int64_t>(2 * rx + (x == 0 && !ra_first ? 1 : 0)) * G + h;
+      const int64_t sb = static_cast<int64_t>(2 * rx + (x == 0 && !ra_first ? 1 : 0)) * G + qh;
       live[q] = x < np && (x == 0 || (a.desc[rx].y & kRangeEmpty) == 0);
       pm[q] = a.ws_ml[sb * 2];
       pl[q] = a.ws_ml[sb * 2 + 1];
-      v[q] = a.ws_acc[sb * kD + e];
+      v[q] = reinterpret_cast<const float4*>(a.ws_acc)[sb * (kD / 4) + e4];
     }
     float Mc = M;
 #pragma unroll
@@ -626,7 +636,7 @@ __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
     if (Mc > M) {                        // rescale the running sums (M = -inf: they are 0)
       const float f = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
       L *= f;
-      o *= f;
+      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
       M = Mc;
     }
 #pragma unroll
@@ -634,13 +644,39 @@ __global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
       if (live[q]) {
         const float wt = __builtin_amdgcn_exp2f(pm[q] - M);
         L = fmaf(pl[q], wt, L);
-        o = fmaf(v[q], wt, o);
+        o.x = fmaf(v[q].x, wt, o.x);
+        o.y = fmaf(v[q].y, wt, o.y);
+        o.z = fmaf(v[q].z, wt, o.z);
+        o.w = fmaf(v[q].w, wt, o.w);
       }
     }
   }
-  if constexpr (CAS) fold_prefix(a, d.z, d.w * G + h, e, M, L, o);
-  a.out[static_cast<int64_t>(d.z) * a.out_stride + static_cast<int64_t>(d.w * G + h) * kD + e] =
-      f32_to_bf16(o * a.out_scale / L);
+  q_o[qr][qh][e4] = o;
+  if (e4 == 0) {
+    q_ml[qr][qh][0] = M;
+    q_ml[qr][qh][1] = L;
+  }
+  __syncthreads();
+  {
+    // quarters in order; quarter 0 holds piece 0, so Mf is finite
+    float Mf = q_ml[0][h][0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) Mf = fmaxf(Mf, q_ml[k][h][0]);
+    float Lf = 0.0f, of = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float mk = q_ml[k][h][0];
+      if (mk != -INFINITY) {
+        const float wt = __builtin_amdgcn_exp2f(mk - Mf);
+        Lf = fmaf(q_ml[k][h][1], wt, Lf);
+        of = fmaf(reinterpret_cast<const float*>(&q_o[k][h][0])[e], wt, of);
+      }
+    }
+    if constexpr (CAS) fold_prefix(a, d.z, d.w * G + h, e, Mf, Lf, of);
+    a.out[static_cast<int64_t>(d.z) * a.out_stride + static_cast<int64_t>(d.w * G + h) * kD + e] =
+        f32_to_bf16(of * a.out_scale / Lf);
+  }
+  __syncthreads();                       // the LDS states are read before the next job
   }
 }
 
