@@ -175,8 +175,15 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
   constexpr int VCH = D / 8;      // v items per head (8 elements each)
   const int H = a.num_heads, Hkv = a.num_kv_heads, B = a.block_size;
   const int rot_items = (H + Hkv) * RCH;
-  const int per_tok = rot_items + Hkv * VCH;
-  const int64_t total = static_cast<int64_t>(a.num_tokens) * per_tok;
+  const int vch = Hkv * VCH;                      // v items per token
+  // Item space: the rotation items token by token, then (from a wave
+  // boundary) the v items in groups of 16 tokens with the token fastest, so
+  // that the 16 lanes storing one dims row of a V tile ([d][B]) hold 16
+  // consecutive tokens: with consecutive slots (a prefill's block) their
+  // 2-byte stores fill whole 32-byte rows instead of touching one row each.
+  const int64_t rot_total = static_cast<int64_t>(a.num_tokens) * rot_items;
+  const int64_t v_base = (rot_total + 63) / 64 * 64;
+  const int64_t total = v_base + (static_cast<int64_t>(a.num_tokens) + 15) / 16 * 16 * vch;
   const int64_t cache_slots = static_cast<int64_t>(a.num_blocks) * B;
 
   const T* q = static_cast<const T*>(a.q);            // may alias q_out (in place)
@@ -189,10 +196,41 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
   uint8_t* __restrict__ vc8 = static_cast<uint8_t*>(a.v_cache);
   const double ks = a.k_scale, vs = a.v_scale;
 
+  // 32-bit item arithmetic when the items fit (the usual case)
+  const bool narrow = total <= 0x7fffffff;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int t = static_cast<int>(idx / per_tok);
-    int w = static_cast<int>(idx - static_cast<int64_t>(t) * per_tok);
+    int t, w;                                     // w >= rot_items: v item w - rot_items
+    if (idx < rot_total) {
+      t = narrow ? static_cast<int>(static_cast<uint32_t>(idx) / static_cast<uint32_t>(rot_items))
+                 : static_cast<int>(idx / rot_items);
+      w = static_cast<int>(idx - static_cast<int64_t>(t) * rot_items);
+    } else {
+      if (idx < v_base) continue;
+      const int64_t vi = idx - v_base;
+      const int64_t rest = vi >> 4;
+      const int64_t th = narrow ? static_cast<int64_t>(static_cast<uint32_t>(rest) / static_cast<uint32_t>(vch))
+                                : rest / vch;
+      t = static_cast<int>(th * 16 + (vi & 15));
+      w = rot_items + static_cast<int>(rest - th * vch);
+      if (t >= a.num_tokens) continue;
+    }
+    // the item's input vectors are loaded first: their addresses do not
+    // depend on the position or slot, so these loads and the metadata loads
+    // are in flight together
+    Vec8<T> x1v, x2v;
+    if (w < rot_items) {
+      const int head = w / RCH;
+      const int i0 = (w - head * RCH) * 8;
+      const T* src = head < H ? q + static_cast<int64_t>(t) * a.q_stride + static_cast<int64_t>(head) * D
+                              : k + static_cast<int64_t>(t) * a.k_stride + static_cast<int64_t>(head - H) * D;
+      x1v.load(src + i0);
+      x2v.load(src + HALF + i0);
+    } else {
+      const int wv = w - rot_items;
+      const int gv = wv / VCH;
+      x1v.load(v + static_cast<int64_t>(t) * a.v_stride + static_cast<int64_t>(gv) * D + (wv - gv * VCH) * 8);
+    }
     const int pos = a.positions[t];
     const int slot = a.slots[t];
     const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
@@ -222,11 +260,6 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
         const int gk = head - H;
         dst = CF8 ? nullptr : kc + ((blk * Hkv + gk) * B + off) * D;
       }
-      const T* src = is_q ? q + static_cast<int64_t>(t) * a.q_stride + static_cast<int64_t>(head) * D
-                          : k + static_cast<int64_t>(t) * a.k_stride + static_cast<int64_t>(head - H) * D;
-      Vec8<T> x1v, x2v;
-      x1v.load(src + i0);
-      x2v.load(src + HALF + i0);
       double x1[8], x2[8], y1[8], y2[8];
       x1v.to_f64(x1);
       x2v.to_f64(x2);
@@ -289,8 +322,7 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       w -= rot_items;
       const int gv = w / VCH;
       const int e0 = (w - gv * VCH) * 8;
-      Vec8<T> x;
-      x.load(v + static_cast<int64_t>(t) * a.v_stride + static_cast<int64_t>(gv) * D + e0);
+      const Vec8<T>& x = x1v;
       if (CF8) {
         double xv[8];
         x.to_f64(xv);
@@ -311,8 +343,11 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
 
 hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream) {
   const int d = a.head_dim;
-  const int per_tok = (a.num_heads + a.num_kv_heads) * (d / 16) + a.num_kv_heads * (d / 8);
-  const int64_t total = static_cast<int64_t>(a.num_tokens) * per_tok;
+  // the kernel's item space: rotation items, then v items padded to whole
+  // waves and groups of 16 tokens
+  const int64_t rot_total = static_cast<int64_t>(a.num_tokens) * (a.num_heads + a.num_kv_heads) * (d / 16);
+  const int64_t total = (rot_total + 63) / 64 * 64 +
+                        (static_cast<int64_t>(a.num_tokens) + 15) / 16 * 16 * a.num_kv_heads * (d / 8);
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 1 << 20) blocks = 1 << 20;
