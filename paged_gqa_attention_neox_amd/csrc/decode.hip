@@ -71,7 +71,6 @@ constexpr int kTierPctHost[kTiers + 1] = {0, 75, 90, 100};
 constexpr int kTierWgs[kTiers] = {kCUs, kCUs, 2 * kCUs};
 __constant__ int kTierMin[kTiers] = {64, 32, 24};
 constexpr int kTierMinHost[kTiers] = {64, 32, 24};
-constexpr int kMaxRanges = 6 * kCUs;
 constexpr int kClaimAhead = 6;          // blocks of wave 0 left when the next range is claimed
 // LDS per workgroup: the merge buffer, sized so that a CU holds one
 // workgroup (four waves, one per SIMD)
