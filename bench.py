@@ -14,7 +14,8 @@ per-call figures come from graphs of K calls of that call alone.  The KV pool (~
 larger than the 256 MB last-level cache, so every step streams KV from HBM.
 
 Also reported on the same line: Qwen2-7B varlen causal prefill (8 sequences
-of 128..512 tokens) TFLOP/s, the mixed TP=2-share batch in tokens/s, the long
+of 128..512 tokens) TFLOP/s over a bf16 and over an FP8 cache, the mixed
+TP=2-share batch in tokens/s, the long
 decode over an FP8 E4M3FN cache, the Qwen3 q/k-norm cache write, the
 shared-prefix (cascade) decode against the plain decode, plus the
 roofline of the decode call and the CPU oracle baseline.
@@ -170,6 +171,19 @@ def bench_prefill(steps, warmup):
                 rope_bytes=b.rope_write_bytes())
 
 
+def bench_prefill_fp8(steps, warmup):
+    """The Qwen2-7B prefill over an FP8 (E4M3FN) cache: the same batch, the
+    cache written as codes by the FP8 rope + cache write."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    b = W.qwen2_prefill_fp8()
+    dev = runner.DeviceStep(b)
+    rope_ms, _ = _time(dev.rope_write, steps, warmup)
+    pf_ms, _ = _time(dev.prefill, steps, warmup)
+    return dict(tokens=b.num_tokens, flops=b.prefill_flops(), prefill_ms=pf_ms, rope_ms=rope_ms)
+
+
 def bench_mixed(steps, warmup):
     from paged_gqa_attention_neox_amd import runner
     from paged_gqa_attention_neox_amd import workloads as W
@@ -296,6 +310,8 @@ def main():
     if not args.only_decode:
         res["prefill"] = bench_prefill(args.steps, args.warmup)
         log(f"prefill: {res['prefill']['prefill_ms']:.3f} ms")
+        res["prefill_fp8"] = bench_prefill_fp8(args.steps, args.warmup)
+        log(f"fp8 prefill: {res['prefill_fp8']['prefill_ms']:.3f} ms")
         res["mixed"] = bench_mixed(args.steps, args.warmup)
         log(f"mixed: {res['mixed']['step_ms']:.3f} ms")
         res["fp8"] = bench_decode_fp8(args.steps, args.warmup)
@@ -362,6 +378,16 @@ def main():
             "rope_cache_write_ms": round(p["rope_ms"], 4),
             "rope_cache_write_GB/s": round(p["rope_bytes"] / (p["rope_ms"] * 1e-3) / 1e9, 2),
             "tokens_per_s": round(p["tokens"] / ((p["prefill_ms"] + p["rope_ms"]) * 1e-3), 1),
+        }
+    if "prefill_fp8" in res:
+        p = res["prefill_fp8"]
+        tf = p["flops"] / (p["prefill_ms"] * 1e-3) / 1e12
+        out["fp8_kv_prefill"] = {
+            "workload": "the same qwen2-7b varlen causal prefill over an FP8 E4M3FN KV cache "
+                        "(k_scale 0.0312, v_scale 0.0287), seed 3",
+            "prefill_ms": round(p["prefill_ms"], 4), "TFLOP/s": round(tf, 2),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "fp8_rope_cache_write_ms": round(p["rope_ms"], 4),
         }
     if "mixed" in res:
         m = res["mixed"]

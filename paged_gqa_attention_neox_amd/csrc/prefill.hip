@@ -45,7 +45,8 @@
 //   * key tiles past the causal limit of the query tile are skipped; the
 //     grid is issued longest tile level first, XCD- and shader-engine-aware
 //     (see the work-item mapping at the top of the kernel).
-// Other shapes, fp32 and FP8 caches use the generic kernel.
+// FP8 caches: the same kernel with the codes widened to bf16 on their way
+// into LDS (the F8 variant).  Other shapes and fp32 use the generic kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,7 +77,8 @@ struct PrefillKArgs {
   uint16_t* out; int64_t out_stride;
   int num_tokens, max_context_len, num_heads, num_kv_heads;
   int num_seqs, num_qtiles, pairs_per_xcd;        // pairs_per_xcd 0: plain order
-  float scale_log2;
+  float scale_log2;                               // scale * log2 e (* k_scale for an FP8 cache)
+  float out_scale;                                // 1, or v_scale for an FP8 cache
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -129,9 +131,20 @@ __device__ __forceinline__ int load_offset(int j, int lane) {
   return d * (kB * 2) + h * 16;
 }
 
+// two E4M3FN codes (bytes 2 HI, 2 HI + 1 of w) -> a bf16 pair, exactly
+// (every E4M3FN value is a bf16 value)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // KG key groups (1 or 2) of WPG waves each.  A wave owns 32 query columns:
 // one head x 32 rows (KG 1) or two heads x 16 rows (KG 2).
-template <int KG, int WPG>
+// F8: the caches hold E4M3FN codes.  Their tiles (half the bytes) are read
+// into registers, widened exactly to bf16 and written to the same LDS
+// layout, one step ahead of the arithmetic; k_scale is folded into the
+// score scale and v_scale into the output.
+template <int KG, int WPG, bool F8>
 __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   constexpr int NW = KG * WPG;                    // waves
   constexpr int HPW = KG == 1 ? 1 : 2;            // heads per wave
@@ -408,6 +421,112 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     if (KG * t + kg < nkt) finish(KG * t + kg, qk(cur), cur);
   };
 
+  if constexpr (F8) {
+    // Chunk i of a step (8 codes -> one 16-byte LDS slot), tile hf = i / 1024
+    // of the step, w = i % 1024:
+    //   w < 512:  key R = w / 16 of the tile, dims chunk c = w % 16: codes at
+    //             (R % 16) * 128 + 8 c of block R / 16's K tile ([B][d]),
+    //             K slot R * 16 + (c ^ perm23(R % 16));
+    //   w >= 512: v = w - 512, block b = v / 256, dims row d = (v % 256) / 2,
+    //             keys 8 h .. 8 h + 7 (h = v % 2): codes at d * 16 + 8 h of the
+    //             V tile ([d][B]), V^T slot 512 + b * 256 + d * 2 + (h ^ vswz(d)).
+    // V entries of keys >= ctx are written as zeros (slots there may hold
+    // anything, a zero probability times NaN would poison the row).
+    constexpr int kChunks = KG * 1024;
+    constexpr int NCH = (kChunks + NW * 64 - 1) / (NW * 64);
+    constexpr int kTile8 = kB * kD;                 // bytes of one head's FP8 K (or V) block tile
+    const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(a.k_cache);
+    const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(a.v_cache);
+    const int64_t head8 = static_cast<int64_t>(g) * kTile8;
+    const int64_t blk8 = static_cast<int64_t>(a.num_kv_heads) * kTile8;
+    auto gload = [&](int t, uint2 (&r)[NCH]) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = tid + i * NW * 64;
+        r[i] = make_uint2(0u, 0u);
+        if (ci < kChunks) {
+          const int hf = ci >> 10, w = ci & 1023;
+          int b, off;
+          const uint8_t* base;
+          if (w < 512) {
+            const int R = w >> 4;
+            b = R >> 4;
+            off = (R & 15) * kD + (w & 15) * 8;
+            base = kc8;
+          } else {
+            const int v = w - 512;
+            b = v >> 8;
+            off = ((v & 255) >> 1) * kB + (v & 1) * 8;
+            base = vc8;
+          }
+          const int blk = sids[2 * (KG * t + hf) + b];
+          r[i] = *reinterpret_cast<const uint2*>(base + blk * blk8 + head8 + off);
+        }
+      }
+    };
+    auto commit = [&](int t, const uint2 (&r)[NCH], uint8_t* dst) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = tid + i * NW * 64;
+        if (ci < kChunks) {
+          const int hf = ci >> 10, w = ci & 1023;
+          uint4 x = make_uint4(fp8x2_bf16x2<false>(r[i].x), fp8x2_bf16x2<true>(r[i].x),
+                               fp8x2_bf16x2<false>(r[i].y), fp8x2_bf16x2<true>(r[i].y));
+          int slot;
+          if (w < 512) {
+            const int R = w >> 4;
+            slot = R * 16 + ((w & 15) ^ perm23(R & 15));
+          } else {
+            const int v = w - 512;
+            const int b = v >> 8, d = (v & 255) >> 1, h = v & 1;
+            slot = 512 + b * 256 + d * 2 + (h ^ vswz(d));
+            const int key0 = t * KG * kBK + hf * kBK + b * kB + h * 8;
+            if (key0 + 8 > ctx) {
+              uint32_t* e = reinterpret_cast<uint32_t*>(&x);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int k0 = key0 + 2 * q;
+                uint32_t y = e[q];
+                if (k0 >= ctx) y &= 0xffff0000u;
+                if (k0 + 1 >= ctx) y &= 0x0000ffffu;
+                e[q] = y;
+              }
+            }
+          }
+          *reinterpret_cast<uint4*>(dst + hf * kTile + slot * 16) = x;
+        }
+      }
+    };
+    // registers: step s in ra (s even) or rb (s odd), two steps in flight;
+    // LDS: step s in st0 (s even) or st1 (s odd).  Step t: the arithmetic of
+    // step t, then step t + 1 widened into the other stage (every wave passed
+    // the barrier after step t - 1, so that stage is free), then step t + 3's
+    // loads into the registers step t + 1 freed; one barrier.
+    uint2 ra[NCH], rb[NCH];
+    gload(0, ra);
+    if (nst > 1) gload(1, rb);
+    commit(0, ra, st0);
+    if (nst > 2) gload(2, ra);
+    wait_lds();
+    barrier();
+    for (int t = 0; t < nst; t += 2) {
+      if (KG * t + kg < nkt) finish(KG * t + kg, qk(st0), st0);
+      if (t + 1 < nst) {
+        commit(t + 1, rb, st1);
+        if (t + 3 < nst) gload(t + 3, rb);
+      }
+      wait_lds();
+      barrier();
+      if (t + 1 >= nst) break;
+      if (KG * (t + 1) + kg < nkt) finish(KG * (t + 1) + kg, qk(st1), st1);
+      if (t + 2 < nst) {
+        commit(t + 2, ra, st0);
+        if (t + 4 < nst) gload(t + 4, ra);
+      }
+      wait_lds();
+      barrier();
+    }
+  } else {
   issue(0, st0);
   if (nst > 1) issue(1, st1);
   if (nst > 2) issue(2, st2);
@@ -419,6 +538,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     step(t + 2, st2, st1);
     if (t + 3 >= nst) break;
     step(t + 3, st3, st2);
+  }
   }
 
   __syncthreads();
@@ -464,7 +584,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // (column, dims chunk c) = column * 16 + (c ^ (column & 15))) so that each
   // store instruction writes four whole 256-byte output rows.
   const float lt = l + __shfl_xor(l, 32);
-  const float inv = bad ? __builtin_nanf("") : 1.0f / lt;
+  const float inv = bad ? __builtin_nanf("") : a.out_scale / lt;
   uint8_t* ot;                                    // this wave's 8 KiB in the (free) ring
   if constexpr (KG == 2) {
     ot = mg + 16 * 64 * 16 + 512;                 // after the merge data of the wave's stage
@@ -498,11 +618,14 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
 }
 
 template <int KG, int WPG>
-void launch_kg(const PrefillKArgs& k, hipStream_t stream) {
+void launch_kg(const PrefillKArgs& k, bool f8, hipStream_t stream) {
   const int64_t np = static_cast<int64_t>(k.num_kv_heads) * k.num_seqs;
   const int64_t slots = k.pairs_per_xcd > 0 ? int64_t{8} * k.pairs_per_xcd : np;
   const dim3 grid(static_cast<unsigned>(slots * k.num_qtiles));
-  hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG>), grid, dim3(KG * WPG * 64), 0, stream, k);
+  if (f8)
+    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, true>), grid, dim3(KG * WPG * 64), 0, stream, k);
+  else
+    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, false>), grid, dim3(KG * WPG * 64), 0, stream, k);
 }
 
 }  // namespace
@@ -528,7 +651,7 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
   const int KG = key_groups(a);
   const int ids = 2 * KG * ((a.max_context_len + KG * kBK - 1) / (KG * kBK));
-  const bool mfma = a.dtype == kBF16 && !a.cache_fp8 && a.head_dim == kD && a.block_size == kB &&
+  const bool mfma = a.dtype == kBF16 && a.head_dim == kD && a.block_size == kB &&
                     G >= 1 && G <= 8 && ids <= kMaxIds;
   if (!mfma) return launch_attn_generic(a, stream);
   PrefillKArgs k{};
@@ -552,24 +675,26 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   k.num_qtiles = (a.max_query_len + rows - 1) / rows;
   const int np = a.num_kv_heads * a.num_seqs;
   k.pairs_per_xcd = np >= 8 ? (np + 7) / 8 : 0;
-  k.scale_log2 = a.scale * kLog2e;
+  k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
+  k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
+  const bool f8 = a.cache_fp8 != 0;
   if (KG == 1) {
     switch (G) {
-      case 1: launch_kg<1, 1>(k, stream); break;
-      case 2: launch_kg<1, 2>(k, stream); break;
-      case 3: launch_kg<1, 3>(k, stream); break;
-      case 4: launch_kg<1, 4>(k, stream); break;
-      case 5: launch_kg<1, 5>(k, stream); break;
-      case 6: launch_kg<1, 6>(k, stream); break;
-      case 7: launch_kg<1, 7>(k, stream); break;
-      default: launch_kg<1, 8>(k, stream); break;
+      case 1: launch_kg<1, 1>(k, f8, stream); break;
+      case 2: launch_kg<1, 2>(k, f8, stream); break;
+      case 3: launch_kg<1, 3>(k, f8, stream); break;
+      case 4: launch_kg<1, 4>(k, f8, stream); break;
+      case 5: launch_kg<1, 5>(k, f8, stream); break;
+      case 6: launch_kg<1, 6>(k, f8, stream); break;
+      case 7: launch_kg<1, 7>(k, f8, stream); break;
+      default: launch_kg<1, 8>(k, f8, stream); break;
     }
   } else {
     switch ((G + 1) / 2) {
-      case 1: launch_kg<2, 1>(k, stream); break;
-      case 2: launch_kg<2, 2>(k, stream); break;
-      case 3: launch_kg<2, 3>(k, stream); break;
-      default: launch_kg<2, 4>(k, stream); break;
+      case 1: launch_kg<2, 1>(k, f8, stream); break;
+      case 2: launch_kg<2, 2>(k, f8, stream); break;
+      case 3: launch_kg<2, 3>(k, f8, stream); break;
+      default: launch_kg<2, 4>(k, f8, stream); break;
     }
   }
   return hipGetLastError();

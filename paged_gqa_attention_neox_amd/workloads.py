@@ -495,6 +495,18 @@ def qwen2_long_decode_fp8(seed: int = 4, num_seqs: int = 64, keep_logical: bool 
                   keep_logical=keep_logical)
 
 
+def qwen2_prefill_fp8(seed: int = 3, num_seqs: int = 8, keep_logical: bool = False) -> Batch:
+    """The Qwen2-7B varlen causal prefill with an FP8 (E4M3FN) KV cache: same
+    lengths, rows and draws as the bf16 workload, the cache written as codes
+    of value / scale (k_scale 0.0312, v_scale 0.0287)."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128, cache_dtype="fp8",
+                      k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+    rng = np.random.default_rng(seed)
+    n = rng.integers(128, 512, size=num_seqs, endpoint=True).astype(np.int32)
+    return _build("qwen2_7b_prefill_8x[128,512]_fp8kv", shape, seed, rng, n.copy(), n.copy(),
+                  num_seqs, np.zeros(num_seqs, bool), 0, 1.0, keep_logical=keep_logical)
+
+
 def mixed_tp2(seed: int = 5, keep_logical: bool = False) -> Batch:
     """Mixed chunked batch at the TP=2 share of Qwen2-7B, bf16: 14 q heads,
     2 KV heads, head_dim 128.  4 prefill chunks of 512 tokens (2 continue a

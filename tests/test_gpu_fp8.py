@@ -38,6 +38,8 @@ def fp8_check(b, label, seqs=None):
     say(f"{label}: out max abs {mx:.3e} mean abs {mean:.3e}")
 
 
+_LENS = [1, 17, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 160, 191, 200, 224, 250, 255,
+         256, 257, 300, 131]
 CASES = [
     # (name, H, Hkv, contexts, query lens, num_prefill)
     ("decode_partition_edges", 28, 4, [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 1600], [1] * 10, 0),
@@ -47,6 +49,15 @@ CASES = [
     ("decode_g8", 32, 4, [777, 1500], [1] * 2, 0),
     ("prefill_chunks", 14, 2, [100, 700, 48], [37, 300, 48], 3),
     ("mixed", 28, 4, [90, 300, 2000, 1, 513], [90, 44, 1, 1, 1], 2),
+    # MFMA prefill over FP8 tiles: the one-key-group layout (many rows, ragged
+    # tails, chunks after cached context) and the two-key-group layout (few
+    # long rows), over G 1, 2, 4, 7, 8
+    ("prefill_1group_g7", 28, 4, _LENS, _LENS, len(_LENS)),
+    ("prefill_1group_g7_chunks", 28, 4, [x + 40 for x in _LENS], _LENS, len(_LENS)),
+    ("prefill_1group_g8", 32, 4, _LENS, _LENS, len(_LENS)),
+    ("prefill_2group_g1", 4, 4, [300, 40], [300, 40], 2),
+    ("prefill_2group_g2", 16, 8, [500, 33], [200, 33], 2),
+    ("prefill_2group_g7_long", 28, 4, [1537, 700], [512, 100], 2),
 ]
 
 
@@ -94,3 +105,9 @@ def test_fp8_halves_decode_bytes_and_tracks_bf16():
     fb, f8 = ob.view(np.float32), o8.view(np.float32)
     assert np.all(np.isfinite(f8))
     assert np.abs(fb - f8).mean() < 0.05 * np.abs(fb).mean() + 1e-3
+
+
+def test_fp8_qwen2_prefill_full():
+    """The Qwen2-7B prefill batch (8 sequences of 128..512 tokens) over an FP8
+    cache, every output row against the oracle."""
+    fp8_check(W.qwen2_prefill_fp8(), "fp8_qwen2_prefill")
