@@ -108,6 +108,52 @@ def bench_decode(steps, warmup):
                 rope_bytes=b.rope_write_bytes())
 
 
+def _time_cold(fn, reps, flush):
+    """GPU ms of fn with the last-level cache flushed before each call: a
+    read of all of `flush` (larger than the 256 MB cache) is enqueued first,
+    then fn between HIP events on the launching stream; the read keeps the
+    GPU busy while the call is enqueued, so the events see no launch gap.
+    The flush reads rather than writes: a write fill leaves the cache full of
+    dirty lines whose write-back would then compete with fn's reads (on the
+    long decode that adds ~64 us that belong to the fill).  Returns the
+    median and the per-call list."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    fn()
+    for e0, e1 in ev:
+        flush.sum(dtype=torch.int64)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return t[len(t) // 2], t
+
+
+def bench_cold(reps):
+    """Decode with a cold last-level cache: the Qwen3-0.6B-shaped decode
+    (batch 32, contexts U[128, 2048]: 143 MB of KV, which a warm 256 MB cache
+    would hold) and the Qwen2-7B long decode (a cross-check of the
+    graph-timed headline)."""
+    import torch
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, mk in (("qwen3_decode", W.qwen3_decode), ("qwen2_long_decode", W.qwen2_long_decode)):
+        b = mk()
+        dev = runner.DeviceStep(b)
+        dev.rope_write()
+        med, _ = _time_cold(dev.decode, reps, flush)
+        out[name] = dict(decode_ms=med, alg_bytes=b.decode_bytes(), kv_bytes=b.decode_kv_bytes(),
+                         seqs=b.num_seqs)
+        del dev
+    del flush
+    return out
+
+
 def bench_decode_fp8(steps, warmup):
     """The long-context decode with an FP8 (E4M3FN) KV cache: half the KV bytes."""
     from paged_gqa_attention_neox_amd import runner
@@ -324,6 +370,9 @@ def main():
             f"{res['cascade']['mixed']['cascade_ms']:.3f} ms (plain {res['cascade']['mixed']['plain_ms']:.3f})")
         res["ctx131k"] = bench_decode_131k(args.steps, args.warmup)
         log(f"131k decode: step {res['ctx131k']['step_ms']:.3f} ms (decode {res['ctx131k']['decode_ms']:.3f})")
+        res["cold"] = bench_cold(max(5, args.steps))
+        log(f"cold-cache decode: qwen3 {res['cold']['qwen3_decode']['decode_ms']:.4f} ms, "
+            f"qwen2 long {res['cold']['qwen2_long_decode']['decode_ms']:.4f} ms")
 
     b = dec["batch"]
     value = dec["kv_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
@@ -447,6 +496,23 @@ def main():
             "decode_ms": round(c["decode_ms"], 4),
             "kv_read_GB/s": round(c["kv_bytes"] / (c["step_ms"] * 1e-3) / 1e9, 2),
             "hbm_frac": round(c["alg_bytes"] / (c["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    if "cold" in res:
+        q3, q2 = res["cold"]["qwen3_decode"], res["cold"]["qwen2_long_decode"]
+        gbs = lambda r: r["alg_bytes"] / (r["decode_ms"] * 1e-3) / 1e9
+        out["cold_cache_decode"] = {
+            "method": "each call timed alone between HIP events after a 512 MiB read that "
+                      "evicts the 256 MB last-level cache (a read leaves no dirty lines to "
+                      "write back); median of the calls",
+            "qwen3_0.6b_decode": {
+                "workload": "qwen3-0.6b-shaped decode: 16 q / 8 kv heads, head_dim 128, block 16, "
+                            "batch 32, contexts U[128, 2048], values N(0,1)*0.5, seed 2",
+                "kv_bytes": int(q3["kv_bytes"]), "decode_ms": round(q3["decode_ms"], 4),
+                "alg_GB/s": round(gbs(q3), 2), "hbm_frac": round(gbs(q3) / HBM_PEAK_GBS, 4),
+                "tokens_per_s": round(q3["seqs"] / (q3["decode_ms"] * 1e-3), 1)},
+            "qwen2_7b_long_decode": {
+                "decode_ms": round(q2["decode_ms"], 4), "alg_GB/s": round(gbs(q2), 2),
+                "hbm_frac": round(gbs(q2) / HBM_PEAK_GBS, 4)},
         }
     if not args.no_cpu:
         log("CPU oracle baseline")
