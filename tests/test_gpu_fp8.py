@@ -55,6 +55,13 @@ CASES = [
     ("prefill_1group_g7", 28, 4, _LENS, _LENS, len(_LENS)),
     ("prefill_1group_g7_chunks", 28, 4, [x + 40 for x in _LENS], _LENS, len(_LENS)),
     ("prefill_1group_g8", 32, 4, _LENS, _LENS, len(_LENS)),
+    ("prefill_1group_g3", 12, 4, _LENS, _LENS, len(_LENS)),
+    ("prefill_1group_g5", 20, 4, _LENS, _LENS, len(_LENS)),
+    ("prefill_1group_g6", 24, 4, _LENS, _LENS, len(_LENS)),
+    ("prefill_2group_g3", 12, 4, [700, 45], [300, 45], 2),
+    ("prefill_2group_g4", 16, 4, [900, 77], [333, 77], 2),
+    ("prefill_2group_g5", 20, 4, [640, 1], [640, 1], 2),
+    ("prefill_2group_g6", 24, 4, [1000, 200], [256, 200], 2),
     ("prefill_2group_g1", 4, 4, [300, 40], [300, 40], 2),
     ("prefill_2group_g2", 16, 8, [500, 33], [200, 33], 2),
     ("prefill_2group_g7_long", 28, 4, [1537, 700], [512, 100], 2),
