@@ -217,6 +217,19 @@ def bench_prefill(steps, warmup):
                 rope_bytes=b.rope_write_bytes())
 
 
+def bench_prefill_qwen3(steps, warmup):
+    """Qwen3-0.6B-shaped prefill (16 q / 8 KV heads: two query heads per KV
+    head), 8 sequences of 128..512 tokens."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    b = W.qwen3_prefill()
+    dev = runner.DeviceStep(b)
+    dev.rope_write()
+    pf_ms, _ = _time(dev.prefill, steps, warmup)
+    return dict(tokens=b.num_tokens, flops=b.prefill_flops(), prefill_ms=pf_ms)
+
+
 def bench_prefill_fp8(steps, warmup):
     """The Qwen2-7B prefill over an FP8 (E4M3FN) cache: the same batch, the
     cache written as codes by the FP8 rope + cache write."""
@@ -356,6 +369,8 @@ def main():
     if not args.only_decode:
         res["prefill"] = bench_prefill(args.steps, args.warmup)
         log(f"prefill: {res['prefill']['prefill_ms']:.3f} ms")
+        res["prefill_qwen3"] = bench_prefill_qwen3(args.steps, args.warmup)
+        log(f"qwen3 prefill: {res['prefill_qwen3']['prefill_ms']:.3f} ms")
         res["prefill_fp8"] = bench_prefill_fp8(args.steps, args.warmup)
         log(f"fp8 prefill: {res['prefill_fp8']['prefill_ms']:.3f} ms")
         res["mixed"] = bench_mixed(args.steps, args.warmup)
@@ -427,6 +442,16 @@ def main():
             "rope_cache_write_ms": round(p["rope_ms"], 4),
             "rope_cache_write_GB/s": round(p["rope_bytes"] / (p["rope_ms"] * 1e-3) / 1e9, 2),
             "tokens_per_s": round(p["tokens"] / ((p["prefill_ms"] + p["rope_ms"]) * 1e-3), 1),
+        }
+    if "prefill_qwen3" in res:
+        p = res["prefill_qwen3"]
+        tf = p["flops"] / (p["prefill_ms"] * 1e-3) / 1e12
+        out["qwen3_0.6b_prefill"] = {
+            "workload": "qwen3-0.6b-shaped varlen causal prefill: 8 seqs, lengths U[128,512], "
+                        "16 q / 8 kv heads, seed 8",
+            "tokens": p["tokens"], "causal_gflop": round(p["flops"] / 1e9, 3),
+            "prefill_ms": round(p["prefill_ms"], 4), "TFLOP/s": round(tf, 2),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
         }
     if "prefill_fp8" in res:
         p = res["prefill_fp8"]

@@ -253,8 +253,10 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * (kB * kD);
 
   // issue the loads of step t's keys into stage dst; a 32-key tile past the
-  // causal limit gets empty ranges (no traffic)
-  auto issue = [&](int t, uint8_t* dst) {
+  // causal limit gets empty ranges (no traffic).  Forced inline: with one or
+  // two waves a wave issues 16 loads per step, and the compiler would
+  // otherwise make this a real call inside the step loop.
+  auto issue = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
     int b0, b1, b2 = 0, b3 = 0;                   // block ids of the step
     if constexpr (KG == 2) {
       const int4 ids = *reinterpret_cast<const int4*>(&sids[4 * t]);
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // leaves the loads of steps t + 1 and t + 2 outstanding), refill the stage
   // of step t - 1 (every wave passed the barrier, so it finished with it)
   // with step t + 3, then scores, softmax and PV of this key group's tile.
-  auto step = [&](int t, uint8_t* cur, uint8_t* refill) {
+  auto step = [&](int t, uint8_t* cur, uint8_t* refill) __attribute__((always_inline)) {
     if (t + 2 < nst) wait_vm<2 * NI>();
     else if (t + 1 < nst) wait_vm<NI>();
     else wait_vm<0>();

@@ -462,6 +462,17 @@ def qwen2_prefill(seed: int = 3, num_seqs: int = 8, keep_logical: bool = False) 
                   np.zeros(num_seqs, bool), 0, 1.0, keep_logical=keep_logical)
 
 
+def qwen3_prefill(seed: int = 8, num_seqs: int = 8, keep_logical: bool = False) -> Batch:
+    """Qwen3-0.6B-shaped varlen causal prefill, bf16: 16 q heads, 8 KV heads
+    (group 2), head_dim 128; 8 packed sequences with lengths uniform in
+    [128, 512]; values N(0,1)*0.5 as in the Qwen3 decode workload."""
+    shape = AttnShape(num_heads=16, num_kv_heads=8, head_dim=128)
+    rng = np.random.default_rng(seed)
+    n = rng.integers(128, 512, size=num_seqs, endpoint=True).astype(np.int32)
+    return _build("qwen3_0.6b_prefill_8x[128,512]", shape, seed, rng, n.copy(), n.copy(), num_seqs,
+                  np.zeros(num_seqs, bool), 0, 0.5, keep_logical=keep_logical)
+
+
 def qwen2_long_decode(seed: int = 4, num_seqs: int = 64, keep_logical: bool = False) -> Batch:
     """Qwen2-7B-shaped long-context decode, bf16: 28 q heads, 4 KV heads,
     head_dim 128; batch 64; context lengths log-uniform in [2048, 32768]."""
