@@ -83,6 +83,14 @@ struct PrefillKArgs {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// max of x over lanes i and i ^ 32, in registers (v_permlane32_swap swaps
+// the two halves of its operands; whichever result holds the other half,
+// the max of x and both results is the pair's max)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
 // swap bits 2 and 3 of a 4-bit index (its own inverse)
 __device__ __forceinline__ int perm23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 // V^T slot swizzle bit of dims row d
@@ -176,6 +184,10 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // the sequence metadata: the table row needs only s
   const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
   const int bt_early = tid < a.max_blocks ? bt[tid] : 0;
+  // the first 64 block ids again, lane i of every wave holding block i: the
+  // first steps take their ids with v_readlane instead of an LDS round trip
+  const int lane_id = tid & 63;
+  int idv = lane_id < a.max_blocks ? bt[lane_id] : 0;
   const int r0 = a.cu_seqlens[s];
   const int n = a.cu_seqlens[s + 1] - r0;
   const int q0 = qt * kBQ;
@@ -237,6 +249,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     wait_lds();
     barrier();
     if (lbad) sbad = 1;
+    if (lane_id >= nblk || static_cast<unsigned>(idv) >= static_cast<unsigned>(a.num_blocks)) idv = 0;
   }
 
   // per-lane source offsets of this wave's loads (load j = wave + NW * i;
@@ -258,7 +271,14 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // otherwise make this a real call inside the step loop.
   auto issue = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
     int b0, b1, b2 = 0, b3 = 0;                   // block ids of the step
-    if constexpr (KG == 2) {
+    if (2 * KG * t + 2 * KG <= 64) {              // from the register (uniform branch)
+      b0 = __builtin_amdgcn_readlane(idv, 2 * KG * t);
+      b1 = __builtin_amdgcn_readlane(idv, 2 * KG * t + 1);
+      if constexpr (KG == 2) {
+        b2 = __builtin_amdgcn_readlane(idv, 4 * t + 2);
+        b3 = __builtin_amdgcn_readlane(idv, 4 * t + 3);
+      }
+    } else if constexpr (KG == 2) {
       const int4 ids = *reinterpret_cast<const int4*>(&sids[4 * t]);
       b0 = uniform(ids.x), b1 = uniform(ids.y), b2 = uniform(ids.z), b3 = uniform(ids.w);
     } else {
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     float mt = sc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+    mt = max_halves(mt) * c2;
     // each column decides from its own scores alone (a column's result must
     // not depend on its neighbours)
     const bool up = mt > m + kLazy;
