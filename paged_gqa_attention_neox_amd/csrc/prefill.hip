@@ -159,7 +159,14 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   constexpr int kBQ = 32 / HPW;                   // query rows per tile
   constexpr int kStage = KG * kTile;              // one step's keys (32 KG)
   constexpr int kLoads = KG * kTileLoads;         // loads per step
-  constexpr int NI = (kLoads + NW - 1) / NW;      // loads per wave per step
+  // With at least 4 KG waves, wave w < 4 KG issues the four 1 KiB loads of
+  // one whole (tile, K or V, cache block) group through one descriptor and
+  // the other waves issue none: every descriptor and LDS address is built
+  // once per step by one wave (the scalar unit is shared by the CU's waves,
+  // and 16 KG separately built loads kept it busy for hundreds of cycles
+  // per step).  Fewer waves take loads j = wave + NW i.
+  constexpr bool GROUPED = NW >= 4 * KG;
+  constexpr int NI = GROUPED ? 4 : (kLoads + NW - 1) / NW;   // loads per loading wave per step
   // work item of this workgroup: (KV head g, sequence s, query tile qt)
   const int np = a.num_kv_heads * a.num_seqs;     // (g, s) pairs
   int p, z;
@@ -252,15 +259,17 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     if (lane_id >= nblk || static_cast<unsigned>(idv) >= static_cast<unsigned>(a.num_blocks)) idv = 0;
   }
 
-  // per-lane source offsets of this wave's loads (load j = wave + NW * i;
-  // j / 16 is the 32-key tile of the step, j % 16 the load within it)
+  // per-lane source offsets of this wave's loads (grouped: load i of group
+  // wave is j = 4 (wave % 4) + i of tile wave / 4; otherwise load j = wave +
+  // NW i, j / 16 the 32-key tile of the step, j % 16 the load within it)
   // (kept in registers when there are few; recomputed per load otherwise)
+  const bool loader = !GROUPED || wave < 4 * KG;  // wave-uniform
   constexpr int NV = NI <= 8 ? NI : 1;
   int voff[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int j = wave + NW * i;
-    voff[i] = j < kLoads ? load_offset(j & 15, lane) : 0;
+    const int j = GROUPED ? 16 * (wave >> 2) + 4 * (wave & 3) + i : wave + NW * i;
+    voff[i] = loader && j < kLoads ? load_offset(j & 15, lane) : 0;
   }
   const int64_t head_off = static_cast<int64_t>(g) * (kB * kD);
   const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * (kB * kD);
@@ -284,6 +293,20 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     } else {
       const int2 ids = *reinterpret_cast<const int2*>(&sids[2 * t]);
       b0 = uniform(ids.x), b1 = uniform(ids.y);
+    }
+    if constexpr (GROUPED) {
+      if (!loader) return;
+      const int half = wave >> 2, jj0 = 4 * (wave & 3);   // this wave's group
+      const int bi = 2 * half + ((jj0 >> 2) & 1);
+      const int blk = bi == 0 ? b0 : bi == 1 ? b1 : bi == 2 ? b2 : b3;
+      const bool live = KG * t + half < nkt;
+      const uint16_t* base = (jj0 >= 8 ? a.v_cache : a.k_cache) + blk * blk_elems + head_off;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(base), static_cast<short>(0), live ? kBlockBytes : 0, 0x00020000);
+      uint8_t* d = dst + half * kTile + jj0 * 1024;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_lds16(rs, d + i * 1024, voff[i]);
+      return;
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -430,9 +453,15 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // of step t - 1 (every wave passed the barrier, so it finished with it)
   // with step t + 3, then scores, softmax and PV of this key group's tile.
   auto step = [&](int t, uint8_t* cur, uint8_t* refill) __attribute__((always_inline)) {
-    if (t + 2 < nst) wait_vm<2 * NI>();
-    else if (t + 1 < nst) wait_vm<NI>();
-    else wait_vm<0>();
+    if (!loader) {
+      // no loads of this wave's own in flight
+    } else if (t + 2 < nst) {
+      wait_vm<2 * NI>();
+    } else if (t + 1 < nst) {
+      wait_vm<NI>();
+    } else {
+      wait_vm<0>();
+    }
     barrier();
     if (t == sani_st) {
       sanitize(t, cur);
