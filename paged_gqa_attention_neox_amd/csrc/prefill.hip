@@ -578,17 +578,30 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
       barrier();
     }
   } else {
+  // Steps in pairs: one wait and one barrier for two steps (the pair's
+  // keys, loaded during the previous pair), then the next pair's loads into
+  // the two stages the previous pair used, then both steps' arithmetic with
+  // no barrier between them.
+  auto pair = [&](int t, uint8_t* c0, uint8_t* c1, uint8_t* r0, uint8_t* r1)
+      __attribute__((always_inline)) {
+    if (loader) wait_vm<0>();
+    barrier();
+    if (t == sani_st || t + 1 == sani_st) {
+      sanitize(sani_st, t == sani_st ? c0 : c1);
+      wait_lds();
+      barrier();
+    }
+    if (t + 2 < nst) issue(t + 2, r0);
+    if (t + 3 < nst) issue(t + 3, r1);
+    if (KG * t + kg < nkt) finish(KG * t + kg, qk(c0), c0);
+    if (t + 1 < nst && KG * (t + 1) + kg < nkt) finish(KG * (t + 1) + kg, qk(c1), c1);
+  };
   issue(0, st0);
   if (nst > 1) issue(1, st1);
-  if (nst > 2) issue(2, st2);
   for (int t = 0; t < nst; t += 4) {
-    step(t, st0, st3);
-    if (t + 1 >= nst) break;
-    step(t + 1, st1, st0);
+    pair(t, st0, st1, st2, st3);
     if (t + 2 >= nst) break;
-    step(t + 2, st2, st1);
-    if (t + 3 >= nst) break;
-    step(t + 3, st3, st2);
+    pair(t + 2, st2, st3, st0, st1);
   }
   }
 
