@@ -20,11 +20,17 @@
 //       are merged through LDS at the end, so a query tile's keys are
 //       covered in half the steps (short tiles, long contexts);
 //   * steps (16 or 32 KiB of K and V^T) go through a ring of four LDS stages
-//     with direct-to-LDS buffer loads (no register staging), three steps
-//     ahead.  Each wave issues the same number of 1 KiB loads per step
-//     (surplus ones have an empty range and land in a scratch line), so its
-//     outstanding-load count at every wait is a compile-time constant;
-//   * the block ids the workgroup needs are staged in LDS once, so no load
+//     with direct-to-LDS buffer loads (no register staging), processed in
+//     pairs: one load wait and one barrier per two steps, the next pair's
+//     loads in flight meanwhile.  With at least 4 KG waves each of the first
+//     4 KG waves issues the four 1 KiB loads of one (tile, K or V, block)
+//     group through one descriptor (the CU's scalar unit is shared: 16 KG
+//     separately built loads per step kept it busy); with fewer waves each
+//     wave issues the same number of loads (surplus ones have an empty range
+//     and land in a scratch line).  Either way a wave's outstanding-load
+//     count at every wait is a compile-time constant;
+//   * the block ids the workgroup needs are staged in LDS once (the first 64
+//     also in a register of every wave, read with v_readlane), so no load
 //     inside the loop depends on another load;
 //   * LDS layouts are XOR-swizzled at 16-byte granularity (the source address
 //     of each loaded chunk is chosen so that it lands in its swizzled slot):
