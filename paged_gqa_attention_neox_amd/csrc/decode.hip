@@ -84,14 +84,23 @@ constexpr float kLazy = 8.0f;           // log2-domain slack before the softmax 
 // gfx9-family buffer descriptor word 3 (raw 32-bit accesses, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
+// Buffer loads.  CP is the cache policy: 0 the default, kStream the
+// non-temporal hint (gfx950's NT bit): for tiles that a call reads exactly
+// once, so they do not displace what the caches hold (measured on the
+// long-context decode: 320 -> 297 us per call).  Tiles read again, by other
+// waves or by the next call, keep the default.
+constexpr int kStream = 2;
+template <int CP = 0>
 __device__ __forceinline__ uint4 ld_buf16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CP));
 }
+template <int CP = 0>
 __device__ __forceinline__ uint2 ld_buf8(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, CP));
 }
+template <int CP = 0>
 __device__ __forceinline__ uint32_t ld_buf4(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, CP);
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -414,13 +423,13 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
                                                         static_cast<short>(0),
                                                         live ? kTileBytes : 0, kBufferFlags);
 #pragma unroll
-      for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16(rk, koff + cc * 64);
+      for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16<kStream>(rk, koff + cc * 64);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         if constexpr (F8)
-          vb[t] = ld_buf4(rv, voff + t * 16 * kBlk);
+          vb[t] = ld_buf4<kStream>(rv, voff + t * 16 * kBlk);
         else
-          vb[t] = ld_buf8(rv, voff + t * 16 * kBlk * 2);
+          vb[t] = ld_buf8<kStream>(rv, voff + t * 16 * kBlk * 2);
       }
     };
 
