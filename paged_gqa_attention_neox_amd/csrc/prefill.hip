@@ -201,11 +201,15 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // first steps take their ids with v_readlane instead of an LDS round trip
   const int lane_id = tid & 63;
   int idv = lane_id < a.max_blocks ? bt[lane_id] : 0;
+  // the sequence's context length is fetched with its row range, not after
+  // it (one memory latency less before the first tile loads)
+  int ctx = a.context_lens[s];
   const int r0 = a.cu_seqlens[s];
-  const int n = a.cu_seqlens[s + 1] - r0;
+  const int r1 = a.cu_seqlens[s + 1];
+  asm volatile("" ::"s"(ctx), "s"(r0), "s"(r1));  // all three loaded here (none sunk past the exit)
+  const int n = r1 - r0;
   const int q0 = qt * kBQ;
   if (q0 >= n) return;
-  int ctx = a.context_lens[s];
   bool bad = ctx < n || ctx > a.max_context_len || r0 < 0 || r0 + n > a.num_tokens;
   if (bad) ctx = n;                               // keep every index in range; output is NaN
   if (r0 < 0 || r0 + n > a.num_tokens) return;    // rows not ours to write
