@@ -363,7 +363,13 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-  float m = -INFINITY, l = 0.0f;                  // running max (log2 units), sum
+  // running max (log2 units) and sum.  The max starts at the most negative
+  // finite float, not -inf: a column whose keys in a key group's first tile
+  // are all masked then gets probabilities exp2(-inf) = 0 there instead of
+  // exp2(-inf + inf) = NaN (with two key groups the second group's first
+  // tile can lie wholly past a row).  Its first visible tile raises the max
+  // and scales the (zero) state by exp2(-FLT_MAX - max) = 0 as -inf did.
+  float m = -__FLT_MAX__, l = 0.0f;
   const int qpos = pos0 + q0 + rq;
   const float c2 = a.scale_log2;
 
@@ -638,7 +644,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     const float m1 = ml[lane], l1 = ml[64 + lane];
     const float mm = fmaxf(m, m1);
     const float a0 = __builtin_amdgcn_exp2f(m - mm);
-    const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - mm);   // 0 when group 1 saw no key
     l = l * a0 + l1 * a1;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

@@ -173,6 +173,11 @@ TWO_GROUP = [
     ("prefill_2group_g2", 16, 8, [500, 33], [200, 33]),
     ("prefill_2group_g5", 20, 4, [640, 1], [640, 1]),
     ("prefill_2group_g7_long", 28, 4, [1537, 700], [512, 100]),
+    # a 20-token prefix: the first 16-row tile (positions 20..35) has two
+    # 32-key tiles, and the second key group's only tile (keys 32..63) lies
+    # wholly past its rows 20..31; those columns must come out of the merge
+    # with the first group's keys alone
+    ("prefill_2group_g7_short_prefix", 28, 4, [2000, 56], [40, 36]),
 ]
 
 
