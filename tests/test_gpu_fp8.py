@@ -65,6 +65,9 @@ CASES = [
     ("prefill_2group_g1", 4, 4, [300, 40], [300, 40], 2),
     ("prefill_2group_g2", 16, 8, [500, 33], [200, 33], 2),
     ("prefill_2group_g7_long", 28, 4, [1537, 700], [512, 100], 2),
+    ("prefill_2group_g8", 32, 4, [1200, 30], [64, 30], 2),
+    # the second key group's only tile wholly past some rows (20-token prefix)
+    ("prefill_2group_g7_short_prefix", 28, 4, [2000, 56], [40, 36], 2),
 ]
 
 

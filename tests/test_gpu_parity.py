@@ -123,6 +123,12 @@ SMALL = [
     ("prefill_g8_chunk", "bf16", 32, 4, 128, [1000, 40], [65, 40], 2),
     ("prefill_long_chunk", "bf16", 28, 4, 128, [2100], [100], 1),
     ("prefill_d64_generic", "bf16", 8, 2, 64, [50, 20], [50, 5], 2),
+    # a thousand decode rows of short contexts: many ranges, most holding
+    # several whole segments
+    ("decode_1000_short", "bf16", 28, 4, 128, [1 + (37 * i) % 300 for i in range(1000)],
+     [1] * 1000, 0),
+    # 160 tiny prefill sequences (1..40 tokens): 640 (sequence, KV head) pairs
+    ("prefill_160_tiny", "bf16", 28, 4, 128, list(range(1, 41)) * 4, list(range(1, 41)) * 4, 160),
 ]
 
 
@@ -178,6 +184,12 @@ TWO_GROUP = [
     # wholly past its rows 20..31; those columns must come out of the merge
     # with the first group's keys alone
     ("prefill_2group_g7_short_prefix", 28, 4, [2000, 56], [40, 36]),
+    # even groups over several waves (no padding column) and odd G = 3
+    ("prefill_2group_g3", 12, 4, [700, 45], [300, 45]),
+    ("prefill_2group_g4", 16, 4, [900, 77], [333, 77]),
+    ("prefill_2group_g6", 24, 4, [1000, 200], [256, 200]),
+    ("prefill_2group_g8", 32, 4, [1200, 30], [64, 30]),
+    ("prefill_2group_g8_chunks", 32, 4, [800, 100, 57], [400, 100, 57]),
 ]
 
 
