@@ -31,7 +31,10 @@
 //     count at every wait is a compile-time constant;
 //   * the block ids the workgroup needs are staged in LDS once (the first 64
 //     also in a register of every wave, read with v_readlane), so no load
-//     inside the loop depends on another load;
+//     inside the loop depends on another load.  Their LDS is sized per
+//     launch from the longest context beside the stages: up to ~120K-token
+//     contexts with two key groups, ~380K with one (which takes the longer
+//     ones);
 //   * LDS layouts are XOR-swizzled at 16-byte granularity (the source address
 //     of each loaded chunk is chosen so that it lands in its swizzled slot):
 //     every 16-lane group of an MFMA operand read hits 16 distinct bank groups;
@@ -68,7 +71,7 @@ constexpr int kBK = 32;              // keys per key group and step
 constexpr int kTile = 16384;         // bytes of one 32-key tile in LDS: K 8 KiB + V^T 8 KiB
 constexpr int kTileLoads = 16;       // 1 KiB direct-to-LDS loads per 32-key tile
 constexpr int kBlockBytes = kB * kD * 2;   // one head's K (or V) of one cache block
-constexpr int kMaxIds = 2048;        // block ids a workgroup stages (contexts up to 32K)
+constexpr int kLdsBytes = 160 * 1024;   // LDS of one CU (a workgroup's static + dynamic share)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;        // raise the running max only past this margin (log2 units)
 
@@ -234,7 +237,8 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   __shared__ __attribute__((aligned(1024))) uint8_t st3[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t trash[1024];
   __shared__ int sbad;
-  __shared__ __attribute__((aligned(16))) int sids[kMaxIds];   // block ids of super-tiles 0 .. nst-1
+  // block ids of steps 0 .. nst - 1, sized per launch for the longest context
+  extern __shared__ __attribute__((aligned(16))) int sids[];
 
   // Q^T operand: column = (head, row q0 + rq (clamped)), 8 dims per k-step
   bf16x8_t qb[kD / 16];
@@ -698,14 +702,16 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
 }
 
 template <int KG, int WPG>
-void launch_kg(const PrefillKArgs& k, bool f8, hipStream_t stream) {
+void launch_kg(const PrefillKArgs& k, bool f8, size_t ids_bytes, hipStream_t stream) {
   const int64_t np = static_cast<int64_t>(k.num_kv_heads) * k.num_seqs;
   const int64_t slots = k.pairs_per_xcd > 0 ? int64_t{8} * k.pairs_per_xcd : np;
   const dim3 grid(static_cast<unsigned>(slots * k.num_qtiles));
   if (f8)
-    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, true>), grid, dim3(KG * WPG * 64), 0, stream, k);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, true>), grid, dim3(KG * WPG * 64), ids_bytes,
+                       stream, k);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, false>), grid, dim3(KG * WPG * 64), 0, stream, k);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, false>), grid, dim3(KG * WPG * 64), ids_bytes,
+                       stream, k);
 }
 
 }  // namespace
@@ -727,12 +733,24 @@ int key_groups(const AttnArgs& a) {
   return t2 < t1 ? 2 : 1;
 }
 
+// LDS a workgroup of the layout holds besides the block ids (the four
+// stages, the scratch line and the flag; an upper bound)
+static int lds_static_bytes(int kg) { return 4 * kg * kTile + 2048; }
+// block ids a workgroup stages for contexts up to max_context_len
+static int staged_ids(int kg, int max_context_len) {
+  return 2 * kg * ((max_context_len + kg * kBK - 1) / (kg * kBK));
+}
+
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const int G = a.num_heads / a.num_kv_heads;
-  const int KG = key_groups(a);
-  const int ids = 2 * KG * ((a.max_context_len + KG * kBK - 1) / (KG * kBK));
+  int KG = key_groups(a);
+  // the block ids go to LDS beside the stages: past ~120K-token contexts
+  // the two-group layout has no room for them and the one-group layout
+  // (half the stage bytes) takes the call
+  if (KG == 2 && staged_ids(2, a.max_context_len) * 4 > kLdsBytes - lds_static_bytes(2)) KG = 1;
+  const int ids = staged_ids(KG, a.max_context_len);
   const bool mfma = a.dtype == kBF16 && a.head_dim == kD && a.block_size == kB &&
-                    G >= 1 && G <= 8 && ids <= kMaxIds;
+                    G >= 1 && G <= 8 && ids * 4 <= kLdsBytes - lds_static_bytes(KG);
   if (!mfma) return launch_attn_generic(a, stream);
   PrefillKArgs k{};
   k.q = static_cast<const uint16_t*>(a.q);
@@ -758,23 +776,24 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
   const bool f8 = a.cache_fp8 != 0;
+  const size_t ids_bytes = static_cast<size_t>(ids) * 4;
   if (KG == 1) {
     switch (G) {
-      case 1: launch_kg<1, 1>(k, f8, stream); break;
-      case 2: launch_kg<1, 2>(k, f8, stream); break;
-      case 3: launch_kg<1, 3>(k, f8, stream); break;
-      case 4: launch_kg<1, 4>(k, f8, stream); break;
-      case 5: launch_kg<1, 5>(k, f8, stream); break;
-      case 6: launch_kg<1, 6>(k, f8, stream); break;
-      case 7: launch_kg<1, 7>(k, f8, stream); break;
-      default: launch_kg<1, 8>(k, f8, stream); break;
+      case 1: launch_kg<1, 1>(k, f8, ids_bytes, stream); break;
+      case 2: launch_kg<1, 2>(k, f8, ids_bytes, stream); break;
+      case 3: launch_kg<1, 3>(k, f8, ids_bytes, stream); break;
+      case 4: launch_kg<1, 4>(k, f8, ids_bytes, stream); break;
+      case 5: launch_kg<1, 5>(k, f8, ids_bytes, stream); break;
+      case 6: launch_kg<1, 6>(k, f8, ids_bytes, stream); break;
+      case 7: launch_kg<1, 7>(k, f8, ids_bytes, stream); break;
+      default: launch_kg<1, 8>(k, f8, ids_bytes, stream); break;
     }
   } else {
     switch ((G + 1) / 2) {
-      case 1: launch_kg<2, 1>(k, f8, stream); break;
-      case 2: launch_kg<2, 2>(k, f8, stream); break;
-      case 3: launch_kg<2, 3>(k, f8, stream); break;
-      default: launch_kg<2, 4>(k, f8, stream); break;
+      case 1: launch_kg<2, 1>(k, f8, ids_bytes, stream); break;
+      case 2: launch_kg<2, 2>(k, f8, ids_bytes, stream); break;
+      case 3: launch_kg<2, 3>(k, f8, ids_bytes, stream); break;
+      default: launch_kg<2, 4>(k, f8, ids_bytes, stream); break;
     }
   }
   return hipGetLastError();

@@ -54,6 +54,11 @@ CASES = [
     ("decode_past_32k", 8, 2, [40000, 70001, 33000, 131072], [1] * 4, 0, (4.0, 32768)),
     ("prefill_chunk_past_32k", 8, 2, [36000, 40], [48, 40], 2, (4.0, 32768)),
     ("p2_setting_factor2_4096", 28, 4, [5000, 300, 8192], [64, 300, 1], 2, (2.0, 4096)),
+    # Qwen2-7B heads: a chunk after a 40K-token prefix (two key groups, 2500
+    # block ids staged), and one after a 130K-token prefix (8126 ids leave the
+    # two-group layout no LDS room: the one-group layout takes it)
+    ("prefill_chunk_40k_g7", 28, 4, [40000, 300], [64, 300], 2, (2.0, 32768)),
+    ("prefill_chunk_130k_g7", 28, 4, [130000, 64], [32, 64], 2, (4.0, 32768)),
 ]
 
 
