@@ -230,6 +230,21 @@ def bench_prefill_qwen3(steps, warmup):
     return dict(tokens=b.num_tokens, flops=b.prefill_flops(), prefill_ms=pf_ms)
 
 
+def bench_prefill_long_prefix(steps, warmup):
+    """Chunked prefill with long key loops: 8 chunks of 256 rows after
+    8192-token prefixes (Qwen2-7B heads).  Its work items are long, so it
+    shows the kernel's steady-state matrix-core rate, which the short items
+    of the headline prefill batch do not reach."""
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+
+    b = W.qwen2_prefill_long_prefix()
+    dev = runner.DeviceStep(b)
+    dev.rope_write()
+    pf_ms, _ = _time(dev.prefill, steps, warmup)
+    return dict(tokens=b.num_tokens, flops=b.prefill_flops(), prefill_ms=pf_ms)
+
+
 def bench_prefill_fp8(steps, warmup):
     """The Qwen2-7B prefill over an FP8 (E4M3FN) cache: the same batch, the
     cache written as codes by the FP8 rope + cache write."""
@@ -371,6 +386,8 @@ def main():
         log(f"prefill: {res['prefill']['prefill_ms']:.3f} ms")
         res["prefill_qwen3"] = bench_prefill_qwen3(args.steps, args.warmup)
         log(f"qwen3 prefill: {res['prefill_qwen3']['prefill_ms']:.3f} ms")
+        res["prefill_long"] = bench_prefill_long_prefix(args.steps, args.warmup)
+        log(f"long-prefix prefill: {res['prefill_long']['prefill_ms']:.3f} ms")
         res["prefill_fp8"] = bench_prefill_fp8(args.steps, args.warmup)
         log(f"fp8 prefill: {res['prefill_fp8']['prefill_ms']:.3f} ms")
         res["mixed"] = bench_mixed(args.steps, args.warmup)
@@ -449,6 +466,16 @@ def main():
         out["qwen3_0.6b_prefill"] = {
             "workload": "qwen3-0.6b-shaped varlen causal prefill: 8 seqs, lengths U[128,512], "
                         "16 q / 8 kv heads, seed 8",
+            "tokens": p["tokens"], "causal_gflop": round(p["flops"] / 1e9, 3),
+            "prefill_ms": round(p["prefill_ms"], 4), "TFLOP/s": round(tf, 2),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+        }
+    if "prefill_long" in res:
+        p = res["prefill_long"]
+        tf = p["flops"] / (p["prefill_ms"] * 1e-3) / 1e12
+        out["long_prefix_prefill"] = {
+            "workload": "qwen2-7b chunked prefill: 8 chunks of 256 rows after 8192-token "
+                        "prefixes, 28 q / 4 kv, seed 9",
             "tokens": p["tokens"], "causal_gflop": round(p["flops"] / 1e9, 3),
             "prefill_ms": round(p["prefill_ms"], 4), "TFLOP/s": round(tf, 2),
             "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),

@@ -462,6 +462,17 @@ def qwen2_prefill(seed: int = 3, num_seqs: int = 8, keep_logical: bool = False) 
                   np.zeros(num_seqs, bool), 0, 1.0, keep_logical=keep_logical)
 
 
+def qwen2_prefill_long_prefix(seed: int = 9, num_seqs: int = 8, keep_logical: bool = False) -> Batch:
+    """Qwen2-7B-shaped chunked prefill, bf16: 28 q heads, 4 KV heads, head_dim
+    128; 8 sequences, each a 256-row chunk after an 8192-token prefix already
+    in the cache (positions 8192..8447): long key loops per query tile."""
+    shape = AttnShape(num_heads=28, num_kv_heads=4, head_dim=128)
+    rng = np.random.default_rng(seed)
+    n = np.full(num_seqs, 256, np.int32)
+    return _build("qwen2_7b_prefill_8x256_after_8192", shape, seed, rng, n + 8192, n, num_seqs,
+                  np.zeros(num_seqs, bool), 0, 1.0, keep_logical=keep_logical)
+
+
 def qwen3_prefill(seed: int = 8, num_seqs: int = 8, keep_logical: bool = False) -> Batch:
     """Qwen3-0.6B-shaped varlen causal prefill, bf16: 16 q heads, 8 KV heads
     (group 2), head_dim 128; 8 packed sequences with lengths uniform in
@@ -641,6 +652,7 @@ WORKLOADS = {
     "tiny_f32": tiny_f32_steps,
     "qwen3_decode": qwen3_decode,
     "qwen2_prefill": qwen2_prefill,
+    "qwen2_prefill_long_prefix": qwen2_prefill_long_prefix,
     "qwen2_long_decode": qwen2_long_decode,
     "mixed_tp2": mixed_tp2,
     "qwen2_long_decode_fp8": qwen2_long_decode_fp8,

@@ -77,6 +77,12 @@ def test_qwen2_prefill_full():
     full_check(W.qwen2_prefill())
 
 
+def test_qwen2_prefill_long_prefix_sampled():
+    """The bench's long-key-loop prefill (8 chunks of 256 rows after 8192-token
+    prefixes), in its bench launch; the oracle attention on two chunks."""
+    full_check(W.qwen2_prefill_long_prefix(), seqs=[0, 7])
+
+
 @functools.lru_cache(maxsize=1)
 def _long_decode():
     return W.qwen2_long_decode()
