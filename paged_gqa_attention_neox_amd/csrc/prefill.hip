@@ -772,7 +772,13 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   const int rows = KG == 1 ? 32 : 16;
   k.num_qtiles = (a.max_query_len + rows - 1) / rows;
   const int np = a.num_kv_heads * a.num_seqs;
-  k.pairs_per_xcd = np >= 8 ? (np + 7) / 8 : 0;
+  // Pin each (KV head, sequence) pair to one XCD (its K/V stay in one L2)
+  // with 32-row tiles, and with 16-row tiles only while an XCD holds one
+  // pair: a long chunk then has up to twice as many tiles per pair, and
+  // pinned beside another pair they outnumber the XCD's 32 CUs and run in
+  // two rounds (a 512-row chunk beside two short ones: 53.7 us pinned, 31.9
+  // spread).  The plain order spreads a pair's tiles over all XCDs.
+  k.pairs_per_xcd = np >= 8 && (KG == 1 || np == 8) ? (np + 7) / 8 : 0;
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
   const bool f8 = a.cache_fp8 != 0;
