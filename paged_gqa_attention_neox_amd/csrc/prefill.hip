@@ -722,8 +722,14 @@ void launch_kg(const PrefillKArgs& k, bool f8, size_t ids_bytes, hipStream_t str
 // and ~5 us with two; a 32-key tile ~1.0 us (one group, 32 rows x G heads);
 // a 64-key step ~1.5 us (two groups, 16 rows x 2 ceil(G/2) heads).  Only
 // host-side maxima are known, so a row's keys are estimated from the longest
-// context and chunk: c - n / 2 on average, c at most.
+// context and chunk: c - n / 2 on average, c at most.  Two query heads per
+// KV head always take one group: the two-group workgroup would have two
+// waves issuing 16 loads each per step, and its 132 KB of stages leave one
+// workgroup per CU where the one-group layout fits two (measured one-group
+// wins: 55 against 64 us on a 512-row chunk at 1600 keys, 133 against 150 on
+// a 64-row chunk at 4000).
 int key_groups(const AttnArgs& a) {
+  if (a.num_heads == 2 * a.num_kv_heads) return 1;
   const double c = a.max_context_len, n = a.max_query_len;
   const double rows = static_cast<double>(a.num_kv_heads) * a.num_tokens;   // (row, KV head) pairs
   const double avg_keys = c - 0.5 * n;

@@ -63,7 +63,7 @@ CASES = [
     ("prefill_2group_g5", 20, 4, [640, 1], [640, 1], 2),
     ("prefill_2group_g6", 24, 4, [1000, 200], [256, 200], 2),
     ("prefill_2group_g1", 4, 4, [300, 40], [300, 40], 2),
-    ("prefill_2group_g2", 16, 8, [500, 33], [200, 33], 2),
+    ("prefill_g2_long", 16, 8, [500, 33], [200, 33], 2),
     ("prefill_2group_g7_long", 28, 4, [1537, 700], [512, 100], 2),
     ("prefill_2group_g8", 32, 4, [1200, 30], [64, 30], 2),
     # the second key group's only tile wholly past some rows (20-token prefix)

@@ -146,10 +146,12 @@ def test_small_cases(case):
     full_check(b, label=name)
 
 
-def _key_groups(ctx, ql, hkv):
+def _key_groups(ctx, ql, hkv, h):
     """The prefill launcher's layout choice (one or two key groups), restated
     from its cost estimate so that each case below is known to exercise the
-    layout it names."""
+    layout it names.  Two query heads per KV head always take one group."""
+    if h == 2 * hkv:
+        return 1
     c, n, rows = max(ctx), max(ql), hkv * sum(ql)
     avg = c - 0.5 * n
     t1 = max(4 + c / 32, rows / 32 * (4 + avg / 32) / 256)
@@ -167,13 +169,16 @@ ONE_GROUP = [
     ("prefill_1group_g2", 16, 8, _LENS[:20], _LENS[:20]),
     ("prefill_1group_g4", 16, 4, _LENS, _LENS),
     ("prefill_1group_g8", 32, 4, _LENS, _LENS),
+    # two query heads per KV head: one group even for few long rows
+    ("prefill_1group_g2_long", 16, 8, [500, 33], [200, 33]),
+    ("prefill_1group_g2_4000", 8, 4, [4000, 300], [64, 300]),
 ]
 
 
 @pytest.mark.parametrize("case", ONE_GROUP, ids=[c[0] for c in ONE_GROUP])
 def test_prefill_one_key_group(case):
     name, H, Hkv, ctx, ql = case
-    assert _key_groups(ctx, ql, Hkv) == 1, name
+    assert _key_groups(ctx, ql, Hkv, H) == 1, name
     b = W.small_case(170 + ONE_GROUP.index(case), "bf16", H, Hkv, 128, context_lens=ctx,
                      query_lens=ql, num_prefill=len(ql), keep_logical=False)
     full_check(b, label=name)
@@ -182,7 +187,6 @@ def test_prefill_one_key_group(case):
 TWO_GROUP = [
     # (name, H, Hkv, contexts, query lens): few long rows, the two-key-group layout
     ("prefill_2group_g1", 4, 4, [300, 40], [300, 40]),
-    ("prefill_2group_g2", 16, 8, [500, 33], [200, 33]),
     ("prefill_2group_g5", 20, 4, [640, 1], [640, 1]),
     ("prefill_2group_g7_long", 28, 4, [1537, 700], [512, 100]),
     # a 20-token prefix: the first 16-row tile (positions 20..35) has two
@@ -202,7 +206,7 @@ TWO_GROUP = [
 @pytest.mark.parametrize("case", TWO_GROUP, ids=[c[0] for c in TWO_GROUP])
 def test_prefill_two_key_groups(case):
     name, H, Hkv, ctx, ql = case
-    assert _key_groups(ctx, ql, Hkv) == 2, name
+    assert _key_groups(ctx, ql, Hkv, H) == 2, name
     b = W.small_case(190 + TWO_GROUP.index(case), "bf16", H, Hkv, 128, context_lens=ctx,
                      query_lens=ql, num_prefill=len(ql), keep_logical=False)
     full_check(b, label=name)
