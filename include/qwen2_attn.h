@@ -69,6 +69,10 @@
 extern "C" {
 #endif
 
+/* The entry points below are the library's only exported symbols (it is
+ * built with hidden default visibility). */
+#pragma GCC visibility push(default)
+
 typedef enum {
   QW_OK = 0,
   QW_ERR_NULL = 1,         /* a required pointer is NULL */
@@ -420,6 +424,8 @@ const char* qwen2_status_string(int status);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* qwen2_last_error(void);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -303,8 +303,11 @@ def gather_kv(k_cache, v_cache, block_table_row, context_len, block_size, dtype,
     blk = np.asarray(block_table_row)[j // B].astype(np.int64)
     off = j % B
     if cache_dtype == "fp8":
-        K = fp8_e4m3_decode(np.asarray(k_cache)[blk, :, off, :]) * float(k_scale)
-        V = fp8_e4m3_decode(np.asarray(v_cache)[blk, :, :, off]) * float(v_scale)
+        # the decoder applied to each of the 256 codes once, then looked up
+        # per element (the same values as decoding every element)
+        value = fp8_e4m3_decode(np.arange(256, dtype=np.uint8))
+        K = value[np.asarray(k_cache)[blk, :, off, :]] * float(k_scale)
+        V = value[np.asarray(v_cache)[blk, :, :, off]] * float(v_scale)
         return K, V
     K = to_f64(np.asarray(k_cache)[blk, :, off, :], dtype)
     V = to_f64(np.asarray(v_cache)[blk, :, :, off], dtype)

@@ -21,7 +21,8 @@ LIB = os.path.join(HERE, "libqwen2attn.so")
 SOURCES = ["qwen2_attn_api.cpp", "rope_cache.hip", "decode.hip", "prefill.hip", "attn_generic.hip"]
 ARCH = "gfx950"
 CFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
+    "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

@@ -2,6 +2,8 @@
 the CPU oracle, and compare element by element."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -11,8 +13,20 @@ import oracle.reference as R
 from paged_gqa_attention_neox_amd import binding as B
 from paged_gqa_attention_neox_amd import runner
 
-# tolerances the attention outputs must meet against the float64 oracle
+# tolerances the attention outputs must meet against the float64 oracle:
+# the stated absolute bars (max-abs, mean-abs) ...
 TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-5, 1e-6)}
+# ... and, per (row, head), the largest error over head_dim relative to the
+# RMS of that oracle output row.  The absolute bars lose their power where
+# outputs are small (a long context averages thousands of values: |o| ~ 0.01).
+# The relative bar follows from the arithmetic: the GPU rounds each
+# probability to bf16 before the PV product (independent relative errors of
+# at most 2^-9 with mean zero, which perturb an output element by ~2^-9/sqrt(3)
+# of the output's own scale) and rounds the output once (at most 2^-9 |o_e|,
+# and |o_e| is within ~4x the row RMS); fp32 score and sum arithmetic adds
+# ~2^-20.  Both together stay below 2^-6 of the row RMS; the bar is 2^-5.
+# fp32 storage rounds nothing but the output (2^-24), so 2^-16 is ample.
+REL_RMS = {"bf16": 2.0 ** -5, "f32": 2.0 ** -16}
 
 
 def say(msg: str) -> None:
@@ -92,7 +106,21 @@ def check_rotated(gpu, ora, dtype, what):
         assert np.all(d <= lim), f"{what}: a differing element is off by more than one ulp"
 
 
+def _log_parity(rec: dict) -> None:
+    """Append one record to the JSON-lines file named by QW_PARITY_LOG, if set
+    (the observed errors of every output comparison)."""
+    path = os.environ.get("QW_PARITY_LOG")
+    if not path:
+        return
+    rec["test"] = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    with open(path, "a") as f:
+        f.write(json.dumps(rec) + "\n")
+
+
 def check_out(gpu, ora64, dtype, rows=None, what="out"):
+    """Attention outputs [T][H][d] against the float64 oracle: the stated
+    max-abs / mean-abs bars over all elements, and the per-(row, head) bar
+    relative to the RMS of the oracle row.  Returns (max abs, mean abs)."""
     g = R.to_f64(gpu, dtype)
     o = ora64
     if rows is not None:
@@ -101,8 +129,17 @@ def check_out(gpu, ora64, dtype, rows=None, what="out"):
     assert np.all(np.isfinite(g)), f"{what}: GPU output has {int((~np.isfinite(g)).sum())} non-finite values"
     d = np.abs(g - o)
     mx, mean = TOL[dtype]
+    rms = np.sqrt((o * o).mean(axis=-1))
+    rel = d.max(axis=-1) / np.maximum(rms, 1e-30)
+    _log_parity({"what": what, "dtype": dtype, "elements": int(d.size), "max_abs": float(d.max()),
+                 "mean_abs": float(d.mean()), "max_rel_rms": float(rel.max()),
+                 "p99_rel_rms": float(np.quantile(rel, 0.99)),
+                 "min_row_rms": float(rms.min()), "bar_rel_rms": REL_RMS[dtype]})
     assert d.max() <= mx, f"{what}: max abs {d.max():.3e} > {mx} (at {np.unravel_index(d.argmax(), d.shape)})"
     assert d.mean() <= mean, f"{what}: mean abs {d.mean():.3e} > {mean}"
+    assert rel.max() <= REL_RMS[dtype], (
+        f"{what}: error {rel.max():.3e} x the row RMS > {REL_RMS[dtype]:.3e} "
+        f"(at row/head {np.unravel_index(rel.argmax(), rel.shape)})")
     return float(d.max()), float(d.mean())
 
 

@@ -27,6 +27,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from paged_gqa_attention_neox_amd import workloads as W
@@ -571,11 +572,9 @@ def pin_qk_norm_in_cache_write(R):
     assert np.allclose(np.sqrt((q2.astype(np.float64) ** 2).sum(-1)), want, rtol=1e-6)
 
 def pin_dynamic_ntk_closed_forms(R):
-    """Dynamic-NTK scaling: factor 1 changes nothing; the table spans factor x
-    original positions; the fastest frequency is unchanged and the slowest
-    one is divided by exactly factor * L / original - (factor - 1) =
-    factor^2 - factor + 1 (the d / (d - 2) exponent makes it exact); the
-    [P2] §7.1 setting (factor 2 over 4096) gives base 1e6 * 3^(128/126)."""
+    """Dynamic-NTK scaling, the parts fixed without any formula: factor 1
+    changes nothing, the table spans factor x original positions, the fastest
+    frequency (i = 0) stays 1 and every other one turns slower."""
     for d in (64, 128):
         base, L = R.rope_dynamic_ntk(1e6, d, 1.0, 32768)
         assert base == 1e6 and L == 32768
@@ -584,11 +583,31 @@ def pin_dynamic_ntk_closed_forms(R):
             assert L == int(s * L0)
             f0, f1 = R.rope_inv_freq(d, 1e6), R.rope_inv_freq(d, base)
             assert f1[0] == f0[0] == 1.0
-            np.testing.assert_allclose(f0[-1] / f1[-1], s * s - s + 1.0, rtol=1e-12)
             assert np.all(f1[1:] < f0[1:])
-    base, L = R.rope_dynamic_ntk(1e6, 128, 2.0, 4096)
-    assert L == 8192
-    np.testing.assert_allclose(base, 1e6 * 3.0 ** (128.0 / 126.0), rtol=1e-15)
+
+
+def pin_dynamic_ntk_matches_transformers(R):
+    """The scaled frequencies against an independent implementation of the
+    published dynamic-NTK rule: transformers' rope utilities
+    (``_compute_dynamic_ntk_parameters``) at a sequence length of factor x
+    original positions, the length the oracle's table spans.  The library
+    returns float32 frequencies, so they agree to float32 precision.  Settings:
+    the [P2] §7.1 one (factor 2 over 4096), factor 4 over Qwen2's native
+    32768, and factor 3 over 1000, at head_dim 64 and 128."""
+    tr = pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import _compute_dynamic_ntk_parameters
+    for d in (64, 128):
+        for s, L0 in ((2.0, 4096), (4.0, 32768), (3.0, 1000)):
+            cfg = tr.Qwen2Config(hidden_size=4 * d, num_attention_heads=4, num_key_value_heads=2,
+                                 max_position_embeddings=L0,
+                                 rope_parameters={"rope_type": "dynamic", "rope_theta": 1e6,
+                                                  "factor": s})
+            base, L = R.rope_dynamic_ntk(1e6, d, s, L0)
+            assert L == int(s * L0)
+            want, _ = _compute_dynamic_ntk_parameters(cfg, device="cpu", seq_len=L)
+            want = want.double().numpy()
+            assert want.shape == (d // 2,)
+            np.testing.assert_allclose(R.rope_inv_freq(d, base), want, rtol=1e-6, atol=0)
 
 
 # ---------------------------------------------------------------------------
@@ -684,7 +703,7 @@ def pin_cascade_contract(R):
 
 ALL_PINS = [
     pin_cascade_equals_plain_decode, pin_cascade_needles, pin_cascade_contract,
-    pin_dynamic_ntk_closed_forms,
+    pin_dynamic_ntk_closed_forms, pin_dynamic_ntk_matches_transformers,
     pin_rms_norm_matches_torch, pin_rms_norm_closed_forms, pin_qk_norm_in_cache_write,
     pin_fp8_decode_table, pin_fp8_matches_torch, pin_fp8_roundtrip_ties_saturation,
     pin_fp8_cache_write, pin_fp8_attention_reads_dequantized_cache,

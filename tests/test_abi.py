@@ -35,7 +35,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qwen2_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qwen[23]_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_three_path_calls():
@@ -55,8 +55,14 @@ def test_every_declared_symbol_is_exported(lib):
 def test_exported_dynamic_symbols_match_header(lib):
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (qwen2_\w+)", out))
+    exported = set(re.findall(r"\bT (qwen[23]_\w+)", out))
     assert exported == set(declared_functions())
+    # every exported symbol of the library is a declared entry point (no
+    # other external names leak out of the C ABI)
+    assert "qwen3_rope_cache_write" in exported and "qwen3_rope_cache_write_fp8" in exported
+    assert set(B.SIGNATURES) == exported
+    others = set(re.findall(r"\bT (\S+)", out)) - exported
+    assert not others, f"internal symbols exported: {sorted(others)[:5]}"
 
 
 def test_status_strings(lib):

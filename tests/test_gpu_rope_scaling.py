@@ -79,18 +79,15 @@ def test_scaled_rope_steps(case):
     say(f"rope scaling {name}: out max abs {mx:.3e} mean abs {mean:.3e}")
 
 
-def test_qwen2_131k_decode_sampled():
-    """Qwen2-7B decode at 65k-131k contexts with the factor-4 table; the oracle
-    attention on the shortest and longest sequences."""
+def test_qwen2_131k_decode_full():
+    """Qwen2-7B decode at 65k-131k contexts with the factor-4 table; every
+    sequence against the oracle."""
     b = W.qwen2_131k_decode()
-    order = np.argsort(b.context_lens)
-    seqs = sorted({int(order[0]), int(order[-1])})
     say("qwen2_131k_decode: GPU step")
     res, _ = run_gpu(b)
     say("qwen2_131k_decode: oracle")
-    ora = run_oracle(b, seqs=seqs)
+    ora = run_oracle(b)
     check_rotated(res["q_out"], ora["q_out"], "bf16", "q_out")
     check_caches(b, res, ora)
-    cu = b.cu_seqlens_q
-    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
-    check_out(res["out"], ora["out"], "bf16", rows=rows)
+    mx, mean = check_out(res["out"], ora["out"], "bf16")
+    say(f"qwen2_131k_decode: out max abs {mx:.3e} mean abs {mean:.3e}")

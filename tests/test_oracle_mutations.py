@@ -85,8 +85,8 @@ MUTATIONS = [
      "k_store = fp8_e4m3_encode(k_rot * float(k_scale))"),
     ("rope_cache_write", "v_store = fp8_e4m3_encode(x[:, H + Hkv:] / float(v_scale))",
      "v_store = fp8_e4m3_encode(x[:, H + Hkv:] / float(k_scale))"),
-    ("gather_kv", "V = fp8_e4m3_decode(np.asarray(v_cache)[blk, :, :, off]) * float(v_scale)",
-     "V = fp8_e4m3_decode(np.asarray(v_cache)[blk, :, :, off]) * float(k_scale)"),
+    ("gather_kv", "V = value[np.asarray(v_cache)[blk, :, :, off]] * float(v_scale)",
+     "V = value[np.asarray(v_cache)[blk, :, :, off]] * float(k_scale)"),
 ]
 
 
