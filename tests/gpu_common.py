@@ -19,14 +19,21 @@ TOL = {"bf16": (2e-2, 2e-3), "f32": (1e-5, 1e-6)}
 # ... and, per (row, head), the largest error over head_dim relative to the
 # RMS of that oracle output row.  The absolute bars lose their power where
 # outputs are small (a long context averages thousands of values: |o| ~ 0.01).
-# The relative bar follows from the arithmetic: the GPU rounds each
-# probability to bf16 before the PV product (independent relative errors of
-# at most 2^-9 with mean zero, which perturb an output element by ~2^-9/sqrt(3)
-# of the output's own scale) and rounds the output once (at most 2^-9 |o_e|,
-# and |o_e| is within ~4x the row RMS); fp32 score and sum arithmetic adds
-# ~2^-20.  Both together stay below 2^-6 of the row RMS; the bar is 2^-5.
-# fp32 storage rounds nothing but the output (2^-24), so 2^-16 is ample.
-REL_RMS = {"bf16": 2.0 ** -5, "f32": 2.0 ** -16}
+# The relative bar follows from the arithmetic.  The GPU rounds the output
+# once: at most half a bf16 step, 2^-8 of |o_e|, and |o_e| is rarely more
+# than ~4x the row RMS over 128 dims (2^-6 of the RMS).  It also rounds each
+# probability to bf16 before the PV product: relative errors of at most
+# 2^-8 with mean zero; over many keys they average out (~2^-8/sqrt(3) of
+# the row's own scale, a few times that at the largest of ~1e7 elements),
+# over a handful of keys (the first rows of a prefill) they do not, and
+# their effect reaches ~2^-8 of max |V_e| again.  The sum of both stays
+# below ~2^-5 (the largest ratio observed over the GPU suite is 0.030); the
+# bar is 2^-4, which still holds a long-context output to ~6e-4 where the
+# absolute bar allows 2e-2.  Two GPU results of the same rows (each rounded
+# once) differ by at most the same amount twice over the rounding step, and
+# are held to the same bar.  fp32 storage rounds nothing but the output
+# (2^-24) and the fp32 sums, so 2^-16 is ample.
+REL_RMS = {"bf16": 2.0 ** -4, "f32": 2.0 ** -16}
 
 
 def say(msg: str) -> None:
