@@ -24,7 +24,9 @@
  * Pointers: every array argument is a DEVICE pointer unless the comment says
  *   HOST.  The caller owns all memory; the library allocates nothing, keeps
  *   no pointer after returning and holds no global mutable state except a
- *   thread-local error string.  Entry points are thread-safe.
+ *   thread-local error string and the per-GPU scratch array of
+ *   qwen2_attn_decode_paged_noalloc.  Entry points are thread-safe (that one
+ *   with the restriction it states).
  * Streams: every call enqueues its kernels on `stream` (0 = the null stream)
  *   and returns without synchronising.
  * dtype: QW_BF16 (bfloat16 storage, fp32 arithmetic) or QW_F32.  q, k, v,
@@ -217,6 +219,34 @@ int qwen2_attn_decode_paged(const void* q, int64_t q_row_stride,
                             int num_seqs, int max_context_len, int num_heads,
                             int num_kv_heads, int head_dim, int block_size, float scale,
                             int dtype, hipStream_t stream);
+
+/*
+ * qwen2_attn_decode_paged_noalloc: qwen2_attn_decode_paged without a
+ * workspace argument, for callers that cannot allocate device memory at the
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, kernels and results as
+ * qwen2_attn_decode_paged (bitwise equal outputs); the workspace is a
+ * static device array of QWEN2_DECODE_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, resolved on the first call on each device (the
+ * calling thread's current device, which must be the stream's) and held
+ * until the process ends.  The call itself allocates nothing.  The kernels
+ * reset the array's counters at the start of every call, so stale contents
+ * from an earlier call never matter; but every call on one GPU shares that
+ * GPU's array, so calls that overlap in time on one GPU (different streams,
+ * or host threads) race and must not be issued.  A decode whose workspace
+ * (qwen2_attn_decode_workspace_size) would exceed the array returns
+ * QW_ERR_WORKSPACE without launching; every bf16 head_dim-128 decode with
+ * group <= 8 fits (at most 1024 ranges of partial states).
+ */
+#define QWEN2_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)9 << 20)
+int qwen2_attn_decode_paged_noalloc(const void* q, int64_t q_row_stride,
+                                    const void* k_cache, const void* v_cache, int num_blocks,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens,
+                                    void* out, int64_t out_row_stride,
+                                    int num_seqs, int max_context_len, int num_heads,
+                                    int num_kv_heads, int head_dim, int block_size, float scale,
+                                    int dtype, hipStream_t stream);
 
 /*
  * FP8 KV cache.  The three calls below are the ones above with a cache of

@@ -42,6 +42,8 @@ SIGNATURES = {
                                         _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _f, _p]),
     "qwen2_attn_prefill_varlen_fp8": (_i, [_p, _i64, _p, _p, _i, _p, _p, _p, _i, _p, _i64, _i,
                                            _i, _i, _i, _i, _i, _i, _i, _f, _i, _f, _f, _p]),
+    "qwen2_attn_decode_paged_noalloc": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _i64, _i, _i,
+                                             _i, _i, _i, _i, _f, _i, _p]),
     "qwen2_attn_decode_paged_fp8": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _i64, _p, _sz,
                                          _i, _i, _i, _i, _i, _i, _f, _i, _f, _f, _p]),
     "qwen3_rope_cache_write": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
@@ -232,6 +234,24 @@ def qwen2_attn_decode_paged(q, k_cache, v_cache, block_tables, context_lens, out
                                          _i32(context_lens), op, os_, wp, wb, q.shape[0],
                                          max_context_len, num_heads, num_kv_heads, head_dim,
                                          block_size, float(scale), _dtype(q), _stream(stream)))
+
+
+def qwen2_attn_decode_paged_noalloc(q, k_cache, v_cache, block_tables, context_lens, out,
+                                    max_context_len: int, num_heads: int, num_kv_heads: int,
+                                    head_dim: int, block_size: int, scale: float,
+                                    stream=None) -> None:
+    """As qwen2_attn_decode_paged, with the library's per-GPU static scratch
+    as the workspace (the call allocates nothing; overlapping calls on one
+    GPU race)."""
+    qp, qs = _rows(q, num_heads * head_dim)
+    op, os_ = _rows(out, num_heads * head_dim)
+    _check("qwen2_attn_decode_paged_noalloc",
+           lib().qwen2_attn_decode_paged_noalloc(qp, qs, k_cache.data_ptr(), v_cache.data_ptr(),
+                                                 k_cache.shape[0], _i32(block_tables),
+                                                 block_tables.shape[1], _i32(context_lens), op,
+                                                 os_, q.shape[0], max_context_len, num_heads,
+                                                 num_kv_heads, head_dim, block_size, float(scale),
+                                                 _dtype(q), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -365,13 +366,16 @@ static qw::AttnArgs decode_args(const void* q, int64_t q_row_stride, const void*
   return a;
 }
 
-static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
-                       const void* v_cache, int num_blocks, const int32_t* block_tables,
-                       int max_blocks_per_seq, const int32_t* context_lens, void* out,
-                       int64_t out_row_stride, void* workspace, size_t workspace_bytes,
-                       int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
-                       int head_dim, int block_size, float scale, int dtype, int cache_fp8,
-                       float k_scale, float v_scale, hipStream_t stream) {
+// Host validation of a decode call and its plan.  Returns the status; *empty
+// is set when there is nothing to launch (num_seqs == 0, arguments valid).
+static int decode_check(const void* q, int64_t q_row_stride, const void* k_cache,
+                        const void* v_cache, int num_blocks, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                        int64_t out_row_stride, int num_seqs, int max_context_len, int num_heads,
+                        int num_kv_heads, int head_dim, int block_size, float scale, int dtype,
+                        int cache_fp8, float k_scale, float v_scale, qw::DecodePlan* plan,
+                        bool* empty) {
+  *empty = false;
   if (cache_fp8) {
     const int st = check_fp8_scales(k_scale, v_scale);
     if (st) return st;
@@ -380,15 +384,34 @@ static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
   if (num_seqs > 65535) return fail(QW_ERR_UNSUPPORTED, "num_seqs=%d > 65535", num_seqs);
   if (num_seqs == 0) {
     int st = check_heads(num_heads, num_kv_heads, head_dim, block_size, dtype);
-    return st ? st : ok();
+    *empty = st == QW_OK;
+    return st;
   }
   int st = check_attn_common(q, q_row_stride, k_cache, v_cache, num_blocks, context_lens,
                              block_tables, max_blocks_per_seq, out, out_row_stride, num_seqs,
                              max_context_len, num_heads, num_kv_heads, head_dim, block_size,
                              scale, dtype);
   if (st) return st;
-  const qw::DecodePlan plan = qw::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads,
-                                              head_dim, block_size, dtype, cache_fp8);
+  *plan = qw::plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
+                          block_size, dtype, cache_fp8);
+  return QW_OK;
+}
+
+static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
+                       const void* v_cache, int num_blocks, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens, void* out,
+                       int64_t out_row_stride, void* workspace, size_t workspace_bytes,
+                       int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
+                       int head_dim, int block_size, float scale, int dtype, int cache_fp8,
+                       float k_scale, float v_scale, hipStream_t stream) {
+  qw::DecodePlan plan{};
+  bool empty = false;
+  const int st = decode_check(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                              max_blocks_per_seq, context_lens, out, out_row_stride, num_seqs,
+                              max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                              scale, dtype, cache_fp8, k_scale, v_scale, &plan, &empty);
+  if (st) return st;
+  if (empty) return ok();
   if (plan.ws_bytes > 0) {
     if (!workspace) return fail(QW_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.ws_bytes);
     if (workspace_bytes < plan.ws_bytes)
@@ -427,6 +450,73 @@ int qwen2_attn_decode_paged_fp8(const void* q, int64_t q_row_stride, const void*
                      max_blocks_per_seq, context_lens, out, out_row_stride, workspace,
                      workspace_bytes, num_seqs, max_context_len, num_heads, num_kv_heads, head_dim,
                      block_size, scale, dtype, 1, k_scale, v_scale, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Decode workspace of qwen2_attn_decode_paged_noalloc: one static array per
+// GPU (each device holds its own copy at its own address).  In host code the
+// name `scratch` is only a stand-in for the symbol, never a device address:
+// kernels get the address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __align__(256) uint8_t scratch[QWEN2_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address (resolved on the first call there)
+int current_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QW_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(QW_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QW_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwen2_attn_decode_paged_noalloc(const void* q, int64_t q_row_stride, const void* k_cache,
+                                    const void* v_cache, int num_blocks,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, void* out,
+                                    int64_t out_row_stride, int num_seqs, int max_context_len,
+                                    int num_heads, int num_kv_heads, int head_dim, int block_size,
+                                    float scale, int dtype, hipStream_t stream) {
+  // validation, and the workspace this decode needs must fit the array:
+  // both before the symbol lookup, so a refused call touches no device state
+  qw::DecodePlan plan{};
+  bool empty = false;
+  const int vst = decode_check(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, context_lens, out, out_row_stride, num_seqs,
+                               max_context_len, num_heads, num_kv_heads, head_dim, block_size,
+                               scale, dtype, 0, 1.0f, 1.0f, &plan, &empty);
+  if (vst) return vst;
+  if (empty) return ok();
+  if (plan.ws_bytes > QWEN2_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(QW_ERR_WORKSPACE, "decode needs %zu bytes of workspace > the %zu-byte scratch",
+                plan.ws_bytes, static_cast<size_t>(QWEN2_DECODE_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  const int st = current_scratch(&ws);
+  if (st) return st;
+  return decode_impl(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, out, out_row_stride, ws,
+                     QWEN2_DECODE_NOALLOC_SCRATCH_BYTES, num_seqs, max_context_len, num_heads,
+                     num_kv_heads, head_dim, block_size, scale, dtype, 0, 1.0f, 1.0f, stream);
 }
 
 size_t qwen2_attn_decode_cascade_workspace_size(int num_seqs, int max_context_len,

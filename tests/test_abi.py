@@ -374,3 +374,45 @@ def test_cascade_host_checker_agrees_with_oracle_contract(lib):
             B.qwen2_check_prefix_groups_host(ind_, seqs_, lens_, 4096, ctx, bt_, 16)
         with pytest.raises(ValueError):
             R.check_prefix_groups(bt_, ctx, ind_, seqs_, lens_, 16)
+
+
+# ---------------------------------------------------------------------------
+# qwen2_attn_decode_paged_noalloc: validation happens before the per-device
+# scratch lookup, so every refused call below touches no device state
+NOALLOC_SCRATCH = 9 << 20
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=P, qs=28 * 128, kc=P2, vc=P3, nb=100, bt=P, mb=64, ctx=P, out=P2, os=28 * 128,
+             S=4, maxc=1024, H=28, Hkv=4, d=128, B=16, scale=0.0884, dt=1)
+    a.update(kw)
+    return lib.qwen2_attn_decode_paged_noalloc(a["q"], a["qs"], a["kc"], a["vc"], a["nb"], a["bt"],
+                                               a["mb"], a["ctx"], a["out"], a["os"], a["S"],
+                                               a["maxc"], a["H"], a["Hkv"], a["d"], a["B"],
+                                               a["scale"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), QW_ERR_NULL),
+    (dict(out=0), QW_ERR_NULL),
+    (dict(bt=0), QW_ERR_NULL),
+    (dict(H=30), QW_ERR_SHAPE),
+    (dict(B=32), QW_ERR_UNSUPPORTED),
+    (dict(q=MIS), QW_ERR_ALIGN),
+    (dict(mb=8), QW_ERR_SHAPE),
+    (dict(S=-1), QW_ERR_SHAPE),
+])
+def test_decode_noalloc_validation(lib, kw, status):
+    assert _decode_noalloc(lib, **kw) == status
+    assert lib.qwen2_last_error().decode()
+
+
+def test_decode_noalloc_zero_work_and_scratch_bound(lib):
+    assert _decode_noalloc(lib, S=0, q=0, out=0) == QW_OK
+    # the largest decode plans (most ranges, group 8) fit the static scratch
+    bf16 = __import__("torch").bfloat16
+    for S, c, H, Hkv in ((65535, 131072, 32, 4), (64, 32768, 28, 4), (1, 1, 8, 1)):
+        n = B.qwen2_attn_decode_workspace_size(S, c, H, Hkv, 128, 16, bf16)
+        assert 0 < n <= NOALLOC_SCRATCH, (S, c, H, Hkv, n)
+    text = open(HEADER).read()
+    assert "#define QWEN2_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)9 << 20)" in text
