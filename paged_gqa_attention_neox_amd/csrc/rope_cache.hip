@@ -52,15 +52,37 @@ hipError_t launch_rope_table(double* tab, int max_position, int rotary_dim, doub
   return hipGetLastError();
 }
 
-// float64 -> storage with ONE rounding (round to nearest even).
-// bf16: round to odd into fp32 first (truncate, then set the last bit when
-// inexact), then fp32 -> bf16 to nearest even: with 16 extra bits kept, the
-// result is the correctly rounded bf16 of the float64 value.
-__device__ __forceinline__ uint16_t f64_to_bf16(double y) {
-  float t = __double2float_rz(y);
-  uint32_t u = __float_as_uint(t);
-  if (static_cast<double>(t) != y) u |= 1u;
-  return f32_to_bf16(__uint_as_float(u));
+// float64 -> bf16 with ONE rounding (round to nearest even).
+// t = the float32 nearest to y.  Every bf16 value and every midpoint between
+// two neighbouring bf16 values is a float32, and rounding is monotonic, so t
+// never lies past a bf16 midpoint that y does not reach: rounding t to bf16
+// gives the correctly rounded bf16 of y unless t sits exactly on a midpoint
+// (its low 16 bits are 0x8000) that y is not on.  Then t is moved one float32
+// step toward y, off the midpoint to y's side, and rounds the way y does.
+// That case is rare (a float32 tie after an inexact first rounding), so it
+// is handled under one branch for all N values, which a wave takes only when
+// some lane needs it.
+__device__ __forceinline__ float off_tie(float t, double y) {
+  const uint32_t u = __float_as_uint(t);
+  if ((u & 0xffffu) != 0x8000u || static_cast<double>(t) == y) return t;
+  // |y| above |t|: one step away from zero (bit pattern + 1), else toward it
+  return __uint_as_float(u + ((fabs(y) > fabs(static_cast<double>(t))) ? 1u : 0xffffffffu));
+}
+template <int N>
+__device__ __forceinline__ void f64_to_bf16_pairs(const double (&y)[N], uint32_t (&w)[N / 2]) {
+  float t[N];
+  bool tie = false;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    t[j] = static_cast<float>(y[j]);
+    tie |= (__float_as_uint(t[j]) & 0xffffu) == 0x8000u;
+  }
+  if (__builtin_expect(tie, 0)) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) t[j] = off_tie(t[j], y[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) w[j] = pack_bf16x2(t[2 * j], t[2 * j + 1]);
 }
 
 // float64 -> E4M3FN code with ONE rounding (nearest even), saturated at
@@ -111,13 +133,20 @@ template <> struct Vec8<uint16_t> {   // bf16
     for (int j = 0; j < 8; ++j) f[j] = t[j];
   }
   __device__ __forceinline__ void from_f64(const double (&f)[8]) {
-    uint16_t b[8];
+    uint32_t r[4];
+    f64_to_bf16_pairs<8>(f, r);
+    w = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+  // two vectors rounded together (one rare-case branch for both)
+  static __device__ __forceinline__ void from_f64_2(const double (&f1)[8], const double (&f2)[8],
+                                                    Vec8& o1, Vec8& o2) {
+    double f[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = f64_to_bf16(f[j]);
-    w.x = b[0] | (static_cast<uint32_t>(b[1]) << 16);
-    w.y = b[2] | (static_cast<uint32_t>(b[3]) << 16);
-    w.z = b[4] | (static_cast<uint32_t>(b[5]) << 16);
-    w.w = b[6] | (static_cast<uint32_t>(b[7]) << 16);
+    for (int j = 0; j < 8; ++j) { f[j] = f1[j]; f[8 + j] = f2[j]; }
+    uint32_t r[8];
+    f64_to_bf16_pairs<16>(f, r);
+    o1.w = make_uint4(r[0], r[1], r[2], r[3]);
+    o2.w = make_uint4(r[4], r[5], r[6], r[7]);
   }
   static __device__ __forceinline__ uint16_t nan() { return 0x7fc0; }
 };
@@ -155,6 +184,11 @@ template <> struct Vec8<float> {
     for (int j = 0; j < 8; ++j) t[j] = static_cast<float>(f[j]);   // one rounding, nearest even
     from_f32(t);
   }
+  static __device__ __forceinline__ void from_f64_2(const double (&f1)[8], const double (&f2)[8],
+                                                    Vec8& o1, Vec8& o2) {
+    o1.from_f64(f1);
+    o2.from_f64(f2);
+  }
   static __device__ __forceinline__ float nan() { return __builtin_nanf(""); }
 };
 
@@ -173,7 +207,8 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
   constexpr int HALF = D / 2;
   constexpr int RCH = HALF / 8;   // rotation items per head (8 pairs each)
   constexpr int VCH = D / 8;      // v items per head (8 elements each)
-  const int H = a.num_heads, Hkv = a.num_kv_heads, B = a.block_size;
+  constexpr int B = 16;           // tokens per cache block (validated on the host)
+  const int H = a.num_heads, Hkv = a.num_kv_heads;
   const int rot_items = (H + Hkv) * RCH;
   const int vch = Hkv * VCH;                      // v items per token
   // Item space: the rotation items token by token, then (from a wave
@@ -313,8 +348,7 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
         continue;
       }
       Vec8<T> o1, o2;
-      o1.from_f64(y1);
-      o2.from_f64(y2);
+      Vec8<T>::from_f64_2(y1, y2, o1, o2);
       o1.store(dst + i0);
       o2.store(dst + HALF + i0);
     } else {

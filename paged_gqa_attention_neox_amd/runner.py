@@ -160,6 +160,25 @@ class DeviceStep:
         self.prefill(stream)
         self.decode(stream)
 
+    def step_overlapped(self):
+        """The step with the prefill and the decode on two streams: both read
+        only what the cache write produced, so after it the prefill runs on a
+        side stream (default priority) while the decode runs on the current
+        one, and the current stream then waits for the side stream.  A graph
+        captured around this call records the same fork and join."""
+        if not (self.batch.num_prefill and self.batch.num_decode):
+            return self.step()
+        cur = torch.cuda.current_stream()
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream()
+        side = self._side
+        self.rope_write()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            self.prefill()
+        self.decode()
+        cur.wait_stream(side)
+
     def results(self):
         """Host copies: q_out, k_cache, v_cache, out (storage arrays)."""
         torch.cuda.synchronize()

@@ -44,3 +44,38 @@ def test_graph_replays_match_eager_bitwise():
         got = dev.results()
         for key in ("q_out", "k_cache", "v_cache", "out"):
             assert np.array_equal(got[key].view(np.uint16), ref[key].view(np.uint16)), (rep, key)
+
+
+def test_overlapped_step_matches_serial_bitwise():
+    """The mixed step with prefill and decode on two streams (forked after the
+    cache write, joined after both) gives the serial step's results bit for
+    bit, eagerly and as a captured graph replayed several times."""
+    require_gpu()
+    b = W.mixed_tp2()
+    say("overlap: serial step")
+    ser = runner.DeviceStep(b)
+    ser.step()
+    ref = ser.results()
+    dev = runner.DeviceStep(b)
+    say("overlap: eager overlapped step")
+    dev.step_overlapped()
+    got = dev.results()
+    for key in ("q_out", "k_cache", "v_cache", "out"):
+        assert np.array_equal(got[key].view(np.uint16), ref[key].view(np.uint16)), key
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.step_overlapped()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.step_overlapped()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say(f"overlap: graph replay {rep}")
+        dev.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        got = dev.results()
+        assert np.array_equal(got["out"].view(np.uint16), ref["out"].view(np.uint16)), rep
