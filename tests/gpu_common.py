@@ -150,6 +150,19 @@ def check_out(gpu, ora64, dtype, rows=None, what="out"):
     return float(d.max()), float(d.mean())
 
 
+def key_groups(ctx, ql, hkv, h):
+    """The prefill launcher's layout choice (one or two key groups), restated
+    from its cost estimate so that each case that names a layout is known to
+    exercise it.  Two query heads per KV head always take one group."""
+    if h == 2 * hkv:
+        return 1
+    c, n, rows = max(ctx), max(ql), hkv * sum(ql)
+    avg = c - 0.5 * n
+    t1 = max(4 + c / 32, rows / 32 * (4 + avg / 32) / 256)
+    t2 = max(5 + 1.5 * c / 64, rows / 16 * (5 + 1.5 * avg / 64) / 256)
+    return 2 if t2 < t1 else 1
+
+
 def written_mask(batch):
     """Boolean per (block, offset): slots this step writes."""
     B_ = batch.shape.block_size

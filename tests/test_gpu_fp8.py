@@ -11,7 +11,8 @@ import pytest
 
 from paged_gqa_attention_neox_amd import runner
 from paged_gqa_attention_neox_amd import workloads as W
-from gpu_common import check_caches, check_out, check_rotated, require_gpu, run_gpu, run_oracle, say
+from gpu_common import (check_caches, check_out, check_rotated, key_groups, require_gpu, run_gpu,
+                        run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +52,8 @@ CASES = [
     ("mixed", 28, 4, [90, 300, 2000, 1, 513], [90, 44, 1, 1, 1], 2),
     # MFMA prefill over FP8 tiles: the one-key-group layout (many rows, ragged
     # tails, chunks after cached context) and the two-key-group layout (few
-    # long rows), over G 1, 2, 4, 7, 8
+    # long rows), over G 1, 3-8; two query heads per KV head (G = 2) always
+    # take the one-group layout
     ("prefill_1group_g7", 28, 4, _LENS, _LENS, len(_LENS)),
     ("prefill_1group_g7_chunks", 28, 4, [x + 40 for x in _LENS], _LENS, len(_LENS)),
     ("prefill_1group_g8", 32, 4, _LENS, _LENS, len(_LENS)),
@@ -74,6 +76,10 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_fp8_small_cases(case):
     name, H, Hkv, ctx, ql, npf = case
+    if "1group" in name:
+        assert key_groups(ctx, ql, Hkv, H) == 1, name
+    if "2group" in name:
+        assert key_groups(ctx, ql, Hkv, H) == 2, name
     b = W.small_case(401 + CASES.index(case), "bf16", H, Hkv, 128, context_lens=ctx,
                      query_lens=ql, num_prefill=npf, keep_logical=False, cache_dtype="fp8",
                      k_scale=KS, v_scale=VS)

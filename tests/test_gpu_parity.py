@@ -13,8 +13,8 @@ import torch
 import oracle.reference as R
 from paged_gqa_attention_neox_amd import runner
 from paged_gqa_attention_neox_amd import workloads as W
-from gpu_common import (bits, check_caches, check_out, check_rotated, require_gpu, run_gpu,
-                        run_oracle, say)
+from gpu_common import (bits, check_caches, check_out, check_rotated, key_groups, require_gpu,
+                        run_gpu, run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,19 +137,6 @@ def test_small_cases(case):
     full_check(b, label=name)
 
 
-def _key_groups(ctx, ql, hkv, h):
-    """The prefill launcher's layout choice (one or two key groups), restated
-    from its cost estimate so that each case below is known to exercise the
-    layout it names.  Two query heads per KV head always take one group."""
-    if h == 2 * hkv:
-        return 1
-    c, n, rows = max(ctx), max(ql), hkv * sum(ql)
-    avg = c - 0.5 * n
-    t1 = max(4 + c / 32, rows / 32 * (4 + avg / 32) / 256)
-    t2 = max(5 + 1.5 * c / 64, rows / 16 * (5 + 1.5 * avg / 64) / 256)
-    return 2 if t2 < t1 else 1
-
-
 # many sequences: the one-key-group layout (32-row tiles, one wave per head)
 _LENS = [1, 17, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 160, 191, 200, 224, 250, 255,
          256, 257, 300, 131]
@@ -158,7 +145,10 @@ ONE_GROUP = [
     ("prefill_1group_g7_chunks", 28, 4, [x + 40 for x in _LENS], _LENS),
     ("prefill_1group_g1", 8, 8, _LENS[:20], _LENS[:20]),
     ("prefill_1group_g2", 16, 8, _LENS[:20], _LENS[:20]),
+    ("prefill_1group_g3", 12, 4, _LENS, _LENS),
     ("prefill_1group_g4", 16, 4, _LENS, _LENS),
+    ("prefill_1group_g5", 20, 4, _LENS, _LENS),
+    ("prefill_1group_g6", 24, 4, _LENS, _LENS),
     ("prefill_1group_g8", 32, 4, _LENS, _LENS),
     # two query heads per KV head: one group even for few long rows
     ("prefill_1group_g2_long", 16, 8, [500, 33], [200, 33]),
@@ -169,7 +159,7 @@ ONE_GROUP = [
 @pytest.mark.parametrize("case", ONE_GROUP, ids=[c[0] for c in ONE_GROUP])
 def test_prefill_one_key_group(case):
     name, H, Hkv, ctx, ql = case
-    assert _key_groups(ctx, ql, Hkv, H) == 1, name
+    assert key_groups(ctx, ql, Hkv, H) == 1, name
     b = W.small_case(170 + ONE_GROUP.index(case), "bf16", H, Hkv, 128, context_lens=ctx,
                      query_lens=ql, num_prefill=len(ql), keep_logical=False)
     full_check(b, label=name)
@@ -197,7 +187,7 @@ TWO_GROUP = [
 @pytest.mark.parametrize("case", TWO_GROUP, ids=[c[0] for c in TWO_GROUP])
 def test_prefill_two_key_groups(case):
     name, H, Hkv, ctx, ql = case
-    assert _key_groups(ctx, ql, Hkv, H) == 2, name
+    assert key_groups(ctx, ql, Hkv, H) == 2, name
     b = W.small_case(190 + TWO_GROUP.index(case), "bf16", H, Hkv, 128, context_lens=ctx,
                      query_lens=ql, num_prefill=len(ql), keep_logical=False)
     full_check(b, label=name)
