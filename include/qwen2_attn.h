@@ -383,6 +383,23 @@ int qwen3_rope_cache_write_fp8(const void* q, int64_t q_row_stride,
  * num_prefixes > 0 and QW_ERR_SHAPE for negative counts or a prefix-level
  * grid beyond 2^31 - 2 workgroups.
  */
+/*
+ * Whether the shared-prefix (cascade) decode is expected to beat the plain
+ * decode for a batch with these prefix groups: 1 when the prefix KV bytes it
+ * saves, (num_prefix_members - num_prefixes) * max_prefix_len * num_kv_heads
+ * * 2 * head_dim * element bytes (1 with cache_fp8, else 2), reach 96 MiB,
+ * else 0.  The cascade pays one more launch and a prefix pass before the
+ * private keys; on this GPU it lost ~3 us with 49 MB saved (48 members of a
+ * 1024-token prefix over 2 KV heads) and gained ~38 us with 503 MB saved
+ * (4 groups of 16 over 4096 tokens and 4 KV heads), a break-even near
+ * 80 MB.  Callers that leave the choice to the library call the cascade
+ * entry point only when this returns 1 (the results agree either way).
+ * Pure host function; returns 0 for negative or zero counts.
+ */
+int qwen2_attn_decode_cascade_worthwhile(int num_prefixes, int num_prefix_members,
+                                         int max_prefix_len, int num_kv_heads, int head_dim,
+                                         int cache_fp8);
+
 size_t qwen2_attn_decode_cascade_workspace_size(int num_seqs, int max_context_len,
                                                 int max_prefix_len, int num_prefixes,
                                                 int num_prefix_members, int num_heads,

@@ -51,6 +51,7 @@ SIGNATURES = {
     "qwen3_rope_cache_write_fp8": (_i, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i,
                                         _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _d, _f, _f,
                                         _p]),
+    "qwen2_attn_decode_cascade_worthwhile": (_i, [_i, _i, _i, _i, _i, _i]),
     "qwen2_attn_decode_cascade_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "qwen2_attn_decode_paged_cascade": (_i, [_p, _i64, _p, _p, _i, _p, _i, _p, _p, _p, _p, _i, _i,
                                              _i, _p, _i64, _p, _sz, _i, _i, _i, _i, _i, _i, _f,
@@ -382,6 +383,15 @@ def qwen2_check_metadata_host(positions, slot_mapping, cu_seqlens_q, context_len
 
 # ---------------------------------------------------------------------------
 # shared-prefix (cascade) decode
+def qwen2_attn_decode_cascade_worthwhile(num_prefixes: int, num_prefix_members: int,
+                                         max_prefix_len: int, num_kv_heads: int, head_dim: int,
+                                         cache_fp8: bool = False) -> bool:
+    """The library's estimate of whether the cascade decode beats the plain one."""
+    return bool(lib().qwen2_attn_decode_cascade_worthwhile(num_prefixes, num_prefix_members,
+                                                           max_prefix_len, num_kv_heads, head_dim,
+                                                           int(bool(cache_fp8))))
+
+
 def qwen2_attn_decode_cascade_workspace_size(num_seqs: int, max_context_len: int,
                                              max_prefix_len: int, num_prefixes: int,
                                              num_prefix_members: int, num_heads: int,

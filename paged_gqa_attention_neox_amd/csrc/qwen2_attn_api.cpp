@@ -519,6 +519,17 @@ int qwen2_attn_decode_paged_noalloc(const void* q, int64_t q_row_stride, const v
                      num_kv_heads, head_dim, block_size, scale, dtype, 0, 1.0f, 1.0f, stream);
 }
 
+int qwen2_attn_decode_cascade_worthwhile(int num_prefixes, int num_prefix_members,
+                                         int max_prefix_len, int num_kv_heads, int head_dim,
+                                         int cache_fp8) {
+  if (num_prefixes <= 0 || num_prefix_members <= num_prefixes || max_prefix_len <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0)
+    return 0;
+  const double saved = static_cast<double>(num_prefix_members - num_prefixes) * max_prefix_len *
+                       num_kv_heads * 2.0 * head_dim * (cache_fp8 ? 1.0 : 2.0);
+  return saved >= 96.0 * 1024.0 * 1024.0 ? 1 : 0;
+}
+
 size_t qwen2_attn_decode_cascade_workspace_size(int num_seqs, int max_context_len,
                                                 int max_prefix_len, int num_prefixes,
                                                 int num_prefix_members, int num_heads,

@@ -60,6 +60,9 @@ class DeviceStep:
     """Device copies of one batch plus the calls of the step."""
 
     def __init__(self, batch, device="cuda", k_cache=None, v_cache=None, cascade=False):
+        """cascade: False (plain decode), True (the cascade entry point whenever
+        the batch has prefix groups) or "auto" (the cascade where the library
+        expects it to pay, qwen2_attn_decode_cascade_worthwhile)."""
         sh = batch.shape
         self.batch = batch
         self.sh = sh
@@ -97,6 +100,11 @@ class DeviceStep:
             self.d_ctx, self.d_bt = i32(ctx), i32(bt)
             self.d_max_c = int(ctx.max())
             self.cascade = cascade and batch.prefix_groups is not None
+            if self.cascade == "auto":
+                # the library's estimate decides between the two evaluation orders
+                ind, seqs, lens = batch.prefix_groups
+                self.cascade = B.qwen2_attn_decode_cascade_worthwhile(
+                    len(lens), len(seqs), int(np.max(lens)) if len(lens) else 0, Hkv, d, self.fp8)
             if self.cascade:
                 ind, seqs, lens = batch.prefix_groups
                 self.pg = (i32(ind), i32(seqs), i32(lens))

@@ -416,3 +416,23 @@ def test_decode_noalloc_zero_work_and_scratch_bound(lib):
         assert 0 < n <= NOALLOC_SCRATCH, (S, c, H, Hkv, n)
     text = open(HEADER).read()
     assert "#define QWEN2_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)9 << 20)" in text
+
+
+def test_cascade_worthwhile_rule(lib):
+    """The library's estimate of when the cascade pays: saved prefix KV bytes
+    of at least 96 MiB (host-only function)."""
+    f = lib.qwen2_attn_decode_cascade_worthwhile
+    mixed = W.mixed_tp2()
+    ind, seqs, lens = mixed.prefix_groups
+    # the TP=2 mixed batch: 48 members of one 1024-token prefix over 2 KV heads (~49 MB)
+    assert f(len(lens), len(seqs), int(max(lens)), 2, 128, 0) == 0
+    # 4 groups of 16 sequences over 4096-token prefixes, 4 KV heads (~503 MB)
+    assert f(4, 64, 4096, 4, 128, 0) == 1
+    assert f(4, 64, 4096, 4, 128, 1) == 1                  # FP8: half the bytes, still above
+    # the threshold itself: 96 MiB exactly
+    n = 96 * 1024 * 1024 // (2 * 128 * 2)                  # tokens x heads x members saved
+    assert f(1, 1 + n // 1024, 1024, 1, 128, 0) == 1
+    assert f(1, n // 1024, 1024, 1, 128, 0) == 0
+    for bad in ((0, 5, 1024, 2, 128, 0), (2, 2, 1024, 2, 128, 0), (1, 5, 0, 2, 128, 0),
+                (-1, 5, 1024, 2, 128, 0), (1, 5, 1024, 0, 128, 0)):
+        assert f(*bad) == 0
