@@ -299,7 +299,10 @@ def bench_cascade(steps, warmup):
     plain_ms, _ = _time(plain.step, steps, warmup)
     casc = runner.DeviceStep(m, k_cache=plain.k_cache, v_cache=plain.v_cache, cascade=True)
     casc_ms, _ = _time(casc.step, steps, warmup)
-    out["mixed"] = dict(plain_ms=plain_ms, cascade_ms=casc_ms, tokens=m.num_tokens)
+    auto = runner.DeviceStep(m, k_cache=plain.k_cache, v_cache=plain.v_cache, cascade="auto")
+    auto_ms, _ = _time(auto.step, steps, warmup)
+    out["mixed"] = dict(plain_ms=plain_ms, cascade_ms=casc_ms, auto_ms=auto_ms,
+                        auto_uses_cascade=bool(auto.cascade), tokens=m.num_tokens)
     return out
 
 
@@ -417,6 +420,34 @@ def decode_traffic():
     return int(rec["traffic_bytes_per_launch"]) if rec.get("sources_sha256") == h.hexdigest() else None
 
 
+# --profile targets: (workload builder, the DeviceStep call repeated)
+PROFILE_CALLS = {
+    "prefill": ("qwen2_prefill", "prefill"),
+    "prefill_fp8": ("qwen2_prefill_fp8", "prefill"),
+    "rope_write": ("qwen2_prefill", "rope_write"),
+    "decode": ("qwen2_long_decode", "decode"),
+    "decode_fp8": ("qwen2_long_decode_fp8", "decode"),
+    "decode_qwen3": ("qwen3_decode", "decode"),
+    "mixed_overlapped": ("mixed_tp2", "step_overlapped"),
+}
+
+
+def profile_call(name, reps):
+    """Upload one workload, write its cache once, then run one of its calls
+    `reps` times eagerly: a short program whose kernels a profiler counts."""
+    import torch
+    from paged_gqa_attention_neox_amd import runner
+    from paged_gqa_attention_neox_amd import workloads as W
+    wl, call = PROFILE_CALLS[name]
+    dev = runner.DeviceStep(getattr(W, wl)())
+    dev.rope_write()
+    fn = getattr(dev, call)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    log(f"profile {name}: {reps} calls of {call} on {wl}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,6 +455,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-decode", action="store_true", help="time the decode workload only")
+    ap.add_argument("--profile", choices=sorted(PROFILE_CALLS),
+                    help="only run one workload's call --steps times, eagerly (no graphs, no "
+                         "timing): the target of rocprofv3 counter passes")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="only time the CPU oracle baseline (no GPU use) and print its record")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -444,6 +478,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.lib()
+    if args.profile:
+        profile_call(args.profile, args.steps)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")     # 1 GiB
         dst = torch.empty_like(src)
@@ -623,6 +660,8 @@ def main():
                                            / HBM_PEAK_GBS, 4),
             "mixed_step_plain_ms": round(mx["plain_ms"], 4),
             "mixed_step_cascade_ms": round(mx["cascade_ms"], 4),
+            "mixed_step_library_choice_ms": round(mx["auto_ms"], 4),
+            "mixed_step_library_chooses_cascade": mx["auto_uses_cascade"],
             "mixed_tokens_per_s_cascade": round(mx["tokens"] / (mx["cascade_ms"] * 1e-3), 1),
         }
     if "ctx131k" in res:

@@ -195,21 +195,32 @@ template <> struct Vec8<float> {
 // ---------------------------------------------------------------------------
 // fused rotate + scatter
 // ---------------------------------------------------------------------------
+// A rotation item is one 8-pair chunk (pairs i0 .. i0 + 7) of RH heads of
+// one token: the chunk's cos/sin (128 bytes of the table row) is read once
+// for the RH heads, and the RH heads' input loads are in flight together.
+// RH = 2 for batches of at least 512 tokens (more bytes in flight per wave;
+// measured on the 2463-token prefill batch: 13.9 us with one head per item,
+// 12.0 with two, 12.1 with four); RH = 1 for smaller batches (more items to
+// spread: 64 tokens 3.8 against 4.0 us), for FP8 caches, whose encoding
+// needs the registers (17.0 against 18.2 us), and with the q/k norm (its
+// float64 norm per head: 17.0 against 18.7 us on the prefill batch).
+
 // CF8: the caches hold E4M3FN codes of (rotated) k / k_scale and v / v_scale.
 // QKN: Qwen3 q/k norm before the rotation ("nano-vllm: Qwen3 骨架", §5 the
 // q_norm / k_norm RMSNorm modules of the attention; §3.2 rms_norm_eps): each
 // q and k head becomes x / sqrt(mean(x^2) + eps) * w in float64.  The RCH
-// items of a head sit in RCH consecutive lanes aligned to RCH (the item index
-// is idx, and per-token and per-head item counts are multiples of RCH), so
-// the head's sum of squares needs log2(RCH) lane exchanges.
-template <typename T, int D, bool CF8, bool QKN>
+// chunk items of a head group sit in RCH consecutive lanes aligned to RCH
+// (per-token item counts are multiples of RCH), so a head's sum of squares
+// needs log2(RCH) lane exchanges.
+template <typename T, int D, bool CF8, bool QKN, int kRH>
 __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) {
   constexpr int HALF = D / 2;
-  constexpr int RCH = HALF / 8;   // rotation items per head (8 pairs each)
+  constexpr int RCH = HALF / 8;   // chunks of 8 pairs per head
   constexpr int VCH = D / 8;      // v items per head (8 elements each)
   constexpr int B = 16;           // tokens per cache block (validated on the host)
   const int H = a.num_heads, Hkv = a.num_kv_heads;
-  const int rot_items = (H + Hkv) * RCH;
+  const int NH = H + Hkv;                         // rotated heads per token
+  const int rot_items = (NH + kRH - 1) / kRH * RCH;
   const int vch = Hkv * VCH;                      // v items per token
   // Item space: the rotation items token by token, then (from a wave
   // boundary) the v items in groups of 16 tokens with the token fastest, so
@@ -235,128 +246,136 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
   const bool narrow = total <= 0x7fffffff;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    int t, w;                                     // w >= rot_items: v item w - rot_items
     if (idx < rot_total) {
-      t = narrow ? static_cast<int>(static_cast<uint32_t>(idx) / static_cast<uint32_t>(rot_items))
-                 : static_cast<int>(idx / rot_items);
-      w = static_cast<int>(idx - static_cast<int64_t>(t) * rot_items);
+      // ---- rotation item: chunk i0 of heads hg * kRH .. hg * kRH + kRH - 1 ----
+      const int t = narrow ? static_cast<int>(static_cast<uint32_t>(idx) / static_cast<uint32_t>(rot_items))
+                           : static_cast<int>(idx / rot_items);
+      const int w = static_cast<int>(idx - static_cast<int64_t>(t) * rot_items);
+      const int hg = w / RCH;
+      const int i0 = (w - hg * RCH) * 8;
+      // the input vectors are loaded first: their addresses do not depend on
+      // the position or slot, so these loads and the metadata loads are in
+      // flight together
+      Vec8<T> x1v[kRH], x2v[kRH];
+#pragma unroll
+      for (int r = 0; r < kRH; ++r) {
+        const int head = hg * kRH + r;
+        if (head < NH) {
+          const T* src = head < H ? q + static_cast<int64_t>(t) * a.q_stride + static_cast<int64_t>(head) * D
+                                  : k + static_cast<int64_t>(t) * a.k_stride + static_cast<int64_t>(head - H) * D;
+          x1v[r].load(src + i0);
+          x2v[r].load(src + HALF + i0);
+        }
+      }
+      const int pos = a.positions[t];
+      const int slot = a.slots[t];
+      const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
+      const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
+      const int64_t blk = slot_ok ? slot / B : 0;
+      const int off = slot_ok ? slot % B : 0;
+      double cv[8], sv[8];
+      if (pos_ok) {
+        const double* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const double2 c2 = *reinterpret_cast<const double2*>(cs + i0 + j);
+          const double2 s2 = *reinterpret_cast<const double2*>(cs + HALF + i0 + j);
+          cv[j] = c2.x; cv[j + 1] = c2.y;
+          sv[j] = s2.x; sv[j + 1] = s2.y;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRH; ++r) {
+        const int head = hg * kRH + r;            // uniform across the RCH lanes of a head group
+        if (head >= NH) break;
+        const bool is_q = head < H;
+        if (!is_q && !(pos_ok && slot_ok)) continue;
+        T* dst;
+        if (is_q) {
+          dst = q_out + static_cast<int64_t>(t) * a.q_out_stride + static_cast<int64_t>(head) * D;
+          if (!pos_ok) {
+            Vec8<T> nanv;
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[j] = __builtin_nanf("");
+            nanv.from_f32(f);
+            nanv.store(dst + i0);
+            nanv.store(dst + HALF + i0);
+            continue;
+          }
+        } else {
+          const int gk = head - H;
+          dst = CF8 ? nullptr : kc + ((blk * Hkv + gk) * B + off) * D;
+        }
+        double x1[8], x2[8], y1[8], y2[8];
+        x1v[r].to_f64(x1);
+        x2v[r].to_f64(x2);
+        if constexpr (QKN) {
+          double ss = 0.0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ss = fma(x1[j], x1[j], fma(x2[j], x2[j], ss));
+#pragma unroll
+          for (int o = 1; o < RCH; o <<= 1) ss += __shfl_xor(ss, o);
+          const double rms = sqrt(ss / D + a.rms_eps);
+          const T* wp = static_cast<const T*>(is_q ? a.q_norm_w : a.k_norm_w);
+          Vec8<T> w1v, w2v;
+          w1v.load(wp + i0);
+          w2v.load(wp + HALF + i0);
+          double w1[8], w2[8];
+          w1v.to_f64(w1);
+          w2v.to_f64(w2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            x1[j] = x1[j] / rms * w1[j];
+            x2[j] = x2[j] / rms * w2[j];
+          }
+        }
+        // float64 rotation: the inputs are exact, each output is rounded once
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          y1[j] = fma(x1[j], cv[j], -(x2[j] * sv[j]));
+          y2[j] = fma(x2[j], cv[j], x1[j] * sv[j]);
+        }
+        if (CF8 && !is_q) {
+          // the code of the rotation divided by the scale: a correctly
+          // rounded float64 quotient, then one rounding to the code
+          double z1[8], z2[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            z1[j] = y1[j] / ks;
+            z2[j] = y2[j] / ks;
+          }
+          uint8_t* d8 = kc8 + ((blk * Hkv + (head - H)) * B + off) * D;
+          *reinterpret_cast<uint2*>(d8 + i0) = f64x8_to_fp8(z1);
+          *reinterpret_cast<uint2*>(d8 + HALF + i0) = f64x8_to_fp8(z2);
+          continue;
+        }
+        Vec8<T> o1, o2;
+        Vec8<T>::from_f64_2(y1, y2, o1, o2);
+        o1.store(dst + i0);
+        o2.store(dst + HALF + i0);
+      }
     } else {
+      // ---- v item: 8 elements of one v head of one token ----
       if (idx < v_base) continue;
       const int64_t vi = idx - v_base;
       const int64_t rest = vi >> 4;
       const int64_t th = narrow ? static_cast<int64_t>(static_cast<uint32_t>(rest) / static_cast<uint32_t>(vch))
                                 : rest / vch;
-      t = static_cast<int>(th * 16 + (vi & 15));
-      w = rot_items + static_cast<int>(rest - th * vch);
+      const int t = static_cast<int>(th * 16 + (vi & 15));
+      const int wv = static_cast<int>(rest - th * vch);
       if (t >= a.num_tokens) continue;
-    }
-    // the item's input vectors are loaded first: their addresses do not
-    // depend on the position or slot, so these loads and the metadata loads
-    // are in flight together
-    Vec8<T> x1v, x2v;
-    if (w < rot_items) {
-      const int head = w / RCH;
-      const int i0 = (w - head * RCH) * 8;
-      const T* src = head < H ? q + static_cast<int64_t>(t) * a.q_stride + static_cast<int64_t>(head) * D
-                              : k + static_cast<int64_t>(t) * a.k_stride + static_cast<int64_t>(head - H) * D;
-      x1v.load(src + i0);
-      x2v.load(src + HALF + i0);
-    } else {
-      const int wv = w - rot_items;
       const int gv = wv / VCH;
-      x1v.load(v + static_cast<int64_t>(t) * a.v_stride + static_cast<int64_t>(gv) * D + (wv - gv * VCH) * 8);
-    }
-    const int pos = a.positions[t];
-    const int slot = a.slots[t];
-    const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
-    const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
-    const int64_t blk = slot_ok ? slot / B : 0;
-    const int off = slot_ok ? slot % B : 0;
-
-    if (w < rot_items) {
-      const int head = w / RCH;
-      const int i0 = (w - head * RCH) * 8;
-      const bool is_q = head < H;
-      if (!is_q && !(pos_ok && slot_ok)) continue;
-      T* dst;
-      if (is_q) {
-        dst = q_out + static_cast<int64_t>(t) * a.q_out_stride + static_cast<int64_t>(head) * D;
-        if (!pos_ok) {
-          Vec8<T> nanv;
-          float f[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) f[j] = __builtin_nanf("");
-          nanv.from_f32(f);
-          nanv.store(dst + i0);
-          nanv.store(dst + HALF + i0);
-          continue;
-        }
-      } else {
-        const int gk = head - H;
-        dst = CF8 ? nullptr : kc + ((blk * Hkv + gk) * B + off) * D;
-      }
-      double x1[8], x2[8], y1[8], y2[8];
-      x1v.to_f64(x1);
-      x2v.to_f64(x2);
-      if constexpr (QKN) {
-        double ss = 0.0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fma(x1[j], x1[j], fma(x2[j], x2[j], ss));
-#pragma unroll
-        for (int o = 1; o < RCH; o <<= 1) ss += __shfl_xor(ss, o);
-        const double rms = sqrt(ss / D + a.rms_eps);
-        const T* wp = static_cast<const T*>(is_q ? a.q_norm_w : a.k_norm_w);
-        Vec8<T> w1v, w2v;
-        w1v.load(wp + i0);
-        w2v.load(wp + HALF + i0);
-        double w1[8], w2[8];
-        w1v.to_f64(w1);
-        w2v.to_f64(w2);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x1[j] = x1[j] / rms * w1[j];
-          x2[j] = x2[j] / rms * w2[j];
-        }
-      }
-      const double* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
-      double cv[8], sv[8];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const double2 c2 = *reinterpret_cast<const double2*>(cs + i0 + j);
-        const double2 s2 = *reinterpret_cast<const double2*>(cs + HALF + i0 + j);
-        cv[j] = c2.x; cv[j + 1] = c2.y;
-        sv[j] = s2.x; sv[j + 1] = s2.y;
-      }
-      // float64 rotation: the inputs are exact, each output is rounded once
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        y1[j] = fma(x1[j], cv[j], -(x2[j] * sv[j]));
-        y2[j] = fma(x2[j], cv[j], x1[j] * sv[j]);
-      }
-      if (CF8 && !is_q) {
-        // the code of the rotation divided by the scale: a correctly rounded
-        // float64 quotient, then one rounding to the code
-        double z1[8], z2[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          z1[j] = y1[j] / ks;
-          z2[j] = y2[j] / ks;
-        }
-        uint8_t* d8 = kc8 + ((blk * Hkv + (head - H)) * B + off) * D;
-        *reinterpret_cast<uint2*>(d8 + i0) = f64x8_to_fp8(z1);
-        *reinterpret_cast<uint2*>(d8 + HALF + i0) = f64x8_to_fp8(z2);
-        continue;
-      }
-      Vec8<T> o1, o2;
-      Vec8<T>::from_f64_2(y1, y2, o1, o2);
-      o1.store(dst + i0);
-      o2.store(dst + HALF + i0);
-    } else {
+      const int e0 = (wv - gv * VCH) * 8;
+      Vec8<T> x;
+      x.load(v + static_cast<int64_t>(t) * a.v_stride + static_cast<int64_t>(gv) * D + e0);
+      const int pos = a.positions[t];
+      const int slot = a.slots[t];
+      const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
+      const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
       if (!(pos_ok && slot_ok)) continue;
-      w -= rot_items;
-      const int gv = w / VCH;
-      const int e0 = (w - gv * VCH) * 8;
-      const Vec8<T>& x = x1v;
+      const int64_t blk = slot / B;
+      const int off = slot % B;
       if (CF8) {
         double xv[8];
         x.to_f64(xv);
@@ -379,15 +398,22 @@ hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream) {
   const int d = a.head_dim;
   // the kernel's item space: rotation items, then v items padded to whole
   // waves and groups of 16 tokens
-  const int64_t rot_total = static_cast<int64_t>(a.num_tokens) * (a.num_heads + a.num_kv_heads) * (d / 16);
+  const int RH = a.cache_fp8 || a.q_norm_w || a.num_tokens < 512 ? 1 : 2;   // heads per item
+  const int64_t rot_total = static_cast<int64_t>(a.num_tokens) *
+                            ((a.num_heads + a.num_kv_heads + RH - 1) / RH) * (d / 16);
   const int64_t total = (rot_total + 63) / 64 * 64 +
                         (static_cast<int64_t>(a.num_tokens) + 15) / 16 * 16 * a.num_kv_heads * (d / 8);
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 1 << 20) blocks = 1 << 20;
   const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
-#define QW_ROPE_LAUNCH(T, D, F8, N) \
-  hipLaunchKernelGGL((rope_cache_write_kernel<T, D, F8, N>), grid, block, 0, stream, a)
+#define QW_ROPE_LAUNCH(T, D, F8, N)                                                          \
+  do {                                                                                       \
+    if (RH == 2)                                                                             \
+      hipLaunchKernelGGL((rope_cache_write_kernel<T, D, F8, N, 2>), grid, block, 0, stream, a); \
+    else                                                                                     \
+      hipLaunchKernelGGL((rope_cache_write_kernel<T, D, F8, N, 1>), grid, block, 0, stream, a); \
+  } while (0)
 #define QW_ROPE_D(T, F8, N) \
   do { if (d == 128) QW_ROPE_LAUNCH(T, 128, F8, N); else QW_ROPE_LAUNCH(T, 64, F8, N); } while (0)
 #define QW_ROPE_N(T, F8) \

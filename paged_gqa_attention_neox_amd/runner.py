@@ -56,6 +56,21 @@ def rope_table(head_dim: int, theta: float, max_position: int, device="cuda",
     return t
 
 
+def use_cascade(batch, cascade) -> bool:
+    """Whether the decode of `batch` goes through the cascade entry point:
+    never without prefix groups; always for cascade=True; for "auto", when
+    the library expects it to pay (qwen2_attn_decode_cascade_worthwhile)."""
+    if not cascade or batch.prefix_groups is None:
+        return False
+    if cascade != "auto":
+        return True
+    sh = batch.shape
+    ind, seqs, lens = batch.prefix_groups
+    return B.qwen2_attn_decode_cascade_worthwhile(
+        len(lens), len(seqs), int(np.max(lens)) if len(lens) else 0, sh.num_kv_heads,
+        sh.head_dim, sh.cache_storage == "fp8")
+
+
 class DeviceStep:
     """Device copies of one batch plus the calls of the step."""
 
@@ -99,12 +114,7 @@ class DeviceStep:
             ctx, bt = batch.decode_part()
             self.d_ctx, self.d_bt = i32(ctx), i32(bt)
             self.d_max_c = int(ctx.max())
-            self.cascade = cascade and batch.prefix_groups is not None
-            if self.cascade == "auto":
-                # the library's estimate decides between the two evaluation orders
-                ind, seqs, lens = batch.prefix_groups
-                self.cascade = B.qwen2_attn_decode_cascade_worthwhile(
-                    len(lens), len(seqs), int(np.max(lens)) if len(lens) else 0, Hkv, d, self.fp8)
+            self.cascade = use_cascade(batch, cascade)
             if self.cascade:
                 ind, seqs, lens = batch.prefix_groups
                 self.pg = (i32(ind), i32(seqs), i32(lens))

@@ -79,3 +79,26 @@ def test_poison_and_nan_tails():
     # the ids in use are distinct across sequences (no sharing in this workload)
     used = np.concatenate([b.block_tables[s, :nblk[s]] for s in range(b.num_seqs)])
     assert len(np.unique(used)) == len(used)
+
+
+def test_runner_cascade_auto_follows_the_library_rule(monkeypatch):
+    """cascade="auto" asks qwen2_attn_decode_cascade_worthwhile with the
+    batch's groups (host side only: the query is replaced here)."""
+    from paged_gqa_attention_neox_amd import binding as B
+    from paged_gqa_attention_neox_amd import runner
+    seen = []
+
+    def fake(n_pre, n_mem, max_len, hkv, d, fp8):
+        seen.append((n_pre, n_mem, max_len, hkv, d, fp8))
+        return len(seen) > 1
+
+    monkeypatch.setattr(B, "qwen2_attn_decode_cascade_worthwhile", fake)
+    b = W.mixed_tp2()
+    ind, seqs, lens = b.prefix_groups
+    assert runner.use_cascade(b, "auto") is False
+    assert seen == [(len(lens), len(seqs), int(max(lens)), 2, 128, False)]
+    assert runner.use_cascade(b, "auto") is True
+    assert runner.use_cascade(b, True) is True and runner.use_cascade(b, False) is False
+    assert len(seen) == 2
+    plain = W.qwen2_prefill()
+    assert runner.use_cascade(plain, "auto") is False and runner.use_cascade(plain, True) is False
