@@ -65,9 +65,16 @@ constexpr int kTiers = 3;
 // the schedule: tier t takes units [U pct[t] / 100, U pct[t + 1] / 100) in
 // equal ranges of at least kTierMin[t] units, at most kTierWgs[t] of them
 // (the host sizes the workspace for the bound it knows; the kernels count
-// the ranges for the actual U)
+// the ranges for the actual U).  Batches of at least kOneTierUnits units
+// (128 blocks per CU) take one tier: equal ranges, one per workgroup, the
+// two later tiers empty.  There the shrinking tiers cost more in pieces and
+// merges than their balancing wins (measured: the long decode 295 -> 284 us,
+// the mixed step's 96 decodes 91 -> 86 us); smaller batches keep them (a
+// cascade's 64 short suffixes: 99 against 122 us with one tier).
 __constant__ int kTierPct[kTiers + 1] = {0, 75, 90, 100};
+__constant__ int kOneTierPct[kTiers + 1] = {0, 100, 100, 100};
 constexpr int kTierPctHost[kTiers + 1] = {0, 75, 90, 100};
+constexpr int64_t kOneTierUnits = 128 * 256;
 constexpr int kTierWgs[kTiers] = {kCUs, kCUs, 2 * kCUs};
 __constant__ int kTierMin[kTiers] = {64, 32, 24};
 constexpr int kTierMinHost[kTiers] = {64, 32, 24};
@@ -102,6 +109,22 @@ template <int CP = 0>
 __device__ __forceinline__ uint32_t ld_buf4(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, CP);
 }
+
+// 16 bytes per lane from buffer rs at byte offset voff into LDS at lds + 16 * lane
+// (gfx950 direct-to-LDS buffer load; lds is wave-uniform)
+__device__ __forceinline__ void ld_buf_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(N), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// workgroup barrier without __syncthreads' fences (those would wait for
+// every direct-to-LDS load in flight); callers wait for what must be done
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -224,16 +247,20 @@ __device__ Cursor locate(const DecodeKArgs& a, int64_t u, int lane) {
   return c;   // not reached for u < U
 }
 
-// The ranges per tier for the batch's U units.
+// The ranges per tier for the batch's U units.  With one tier R is at most
+// kCUs + 2, below the host's three-tier bound for any U >= kOneTierUnits.
 struct Schedule {
   int n[kTiers];
+  int pct[kTiers + 1];
   int R;
 };
 __device__ Schedule schedule_for(const DecodeKArgs& a, int64_t U) {
   Schedule sc;
   sc.R = 0;
+  const int* pct = U >= kOneTierUnits ? kOneTierPct : kTierPct;
+  for (int t = 0; t <= kTiers; ++t) sc.pct[t] = pct[t];
   for (int t = 0; t < kTiers; ++t) {
-    const int64_t share = U * kTierPct[t + 1] / 100 - U * kTierPct[t] / 100;
+    const int64_t share = U * sc.pct[t + 1] / 100 - U * sc.pct[t] / 100;
     const int64_t n = (share + kTierMin[t] - 1) / kTierMin[t];
     sc.n[t] = static_cast<int>(n < 1 ? 1 : (n > a.tier_wgs[t] ? a.tier_wgs[t] : n));
     sc.R += sc.n[t];
@@ -245,7 +272,7 @@ __device__ int64_t range_begin(const Schedule& sc, int64_t r, int64_t U) {
   int64_t first = 0;
   for (int t = 0; t < kTiers; ++t) {
     const int n = sc.n[t];
-    const int64_t b0 = U * kTierPct[t] / 100, b1 = U * kTierPct[t + 1] / 100;
+    const int64_t b0 = U * sc.pct[t] / 100, b1 = U * sc.pct[t + 1] / 100;
     if (r < first + n) return b0 + (r - first) * (b1 - b0) / n;
     first += n;
   }
@@ -257,7 +284,7 @@ __device__ int64_t range_of(const Schedule& sc, int64_t u, int64_t U) {
   int64_t first = 0;
   for (int t = 0; t < kTiers; ++t) {
     const int n = sc.n[t];
-    const int64_t b0 = U * kTierPct[t] / 100, b1 = U * kTierPct[t + 1] / 100;
+    const int64_t b0 = U * sc.pct[t] / 100, b1 = U * sc.pct[t + 1] / 100;
     if (u < b1) return first + ((u - b0 + 1) * n - 1) / (b1 - b0);
     first += n;
   }
@@ -783,8 +810,14 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
   const int col0 = (xc * kNW + wave) * 16;
   const int bb = chunk * ca.chunk_blocks;
   const int be = min(PB, bb + ca.chunk_blocks);
-  if (PB == 0 || col0 >= cols || bb >= be) return;    // uniform per wave
+  if (PB == 0 || bb >= be || xc * kNW * 16 >= cols) return;   // uniform per workgroup
   const int nb = be - bb;                              // <= 64 blocks
+  // a wave whose 16 columns all lie past the group's pairs computes nothing
+  // (with bf16 tiles it still loads its share of the workgroup's tiles)
+  const bool wave_live = col0 < cols;                  // wave-uniform
+  if constexpr (F8) {
+    if (!wave_live) return;
+  }
 
   // this lane's column: (member sequence s, query head qh)
   const int col = col0 + r16;
@@ -804,54 +837,20 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
   // the chunk's block ids, lane i holding block bb + i
   const int s0 = ca.seqs[i0];
   const int ids = lane < nb ? a.block_tables[static_cast<int64_t>(s0) * a.max_blocks + bb + lane] : 0;
-  const int koff = r16 * kD * kEl + j4 * 16;
-  const int voff = (r16 * kBlk + j4 * 4) * kEl;
   const float c = a.scale_log2;
   bool bad = false;
-
-  auto issue = [&](int i, uint4 (&kb)[kKLoads], VWord (&vb)[8]) {
-    const bool live = i < nb;
-    int id = live ? __builtin_amdgcn_readlane(ids, i) : 0;
-    if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) {
-      bad = true;
-      id = 0;
-    }
-    const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes;
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
-                                                      static_cast<short>(0),
-                                                      live ? kTileBytes : 0, kBufferFlags);
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
-                                                      static_cast<short>(0),
-                                                      live ? kTileBytes : 0, kBufferFlags);
-#pragma unroll
-    for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16(rk, koff + cc * 64);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if constexpr (F8)
-        vb[t] = ld_buf4(rv, voff + t * 16 * kBlk);
-      else
-        vb[t] = ld_buf8(rv, voff + t * 16 * kBlk * 2);
-    }
-  };
 
   float ms = -INFINITY, l = 0.0f;
   f32x4_t acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  // every prefix key lies inside every member's context: no masking
-  auto block = [&](const uint4 (&kb)[kKLoads], const VWord (&vb)[8]) {
+  // every prefix key lies inside every member's context: no masking.
+  // kf(cc): the K operand of dims chunk cc; vf(t): the V operand of dims 16 t ..
+  auto block = [&](auto&& kf, auto&& vf) __attribute__((always_inline)) {
     f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      uint4 kf;
-      if constexpr (F8)
-        kf = fp8x8_to_bf16x8((cc & 1) ? make_uint2(kb[cc >> 1].z, kb[cc >> 1].w)
-                                      : make_uint2(kb[cc >> 1].x, kb[cc >> 1].y));
-      else
-        kf = kb[cc];
-      sc = mfma_16x16x32_bf16(kf, qf[cc], sc);
-    }
+    for (int cc = 0; cc < 4; ++cc) sc = mfma_16x16x32_bf16(kf(cc), qf[cc], sc);
     float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -872,25 +871,116 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
                        __builtin_amdgcn_exp2f(fmaf(sc[3], c, nm)));
     l += (bf16_lo(pp.x) + bf16_hi(pp.x)) + (bf16_lo(pp.y) + bf16_hi(pp.y));
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint2 vf;
-      if constexpr (F8)
-        vf = make_uint2(fp8x2_to_bf16x2<false>(vb[t]), fp8x2_to_bf16x2<true>(vb[t]));
-      else
-        vf = vb[t];
-      acc[t] = mfma_16x16x16_bf16(vf, pp, acc[t]);
-    }
+    for (int t = 0; t < 8; ++t) acc[t] = mfma_16x16x16_bf16(vf(t), pp, acc[t]);
   };
 
-  // two tiles in flight: blocks i and i + 1
-  uint4 kb0[kKLoads], kb1[kKLoads];
-  VWord vb0[8], vb1[8];
-  issue(0, kb0, vb0);
-  for (int i = 0; i < nb; i += 2) {
-    issue(i + 1, kb1, vb1);
-    block(kb0, vb0);
-    issue(i + 2, kb0, vb0);
-    if (i + 1 < nb) block(kb1, vb1);
+  if constexpr (F8) {
+    // FP8 tiles: each wave reads its tiles into registers (codes widened to
+    // bf16 there), two blocks in flight
+    const int koff = r16 * kD * kEl + j4 * 16;
+    const int voff = (r16 * kBlk + j4 * 4) * kEl;
+    auto issue = [&](int i, uint4 (&kb)[kKLoads], VWord (&vb)[8]) {
+      const bool live = i < nb;
+      int id = live ? __builtin_amdgcn_readlane(ids, i) : 0;
+      if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) {
+        bad = true;
+        id = 0;
+      }
+      const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes;
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
+                                                        static_cast<short>(0),
+                                                        live ? kTileBytes : 0, kBufferFlags);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
+                                                        static_cast<short>(0),
+                                                        live ? kTileBytes : 0, kBufferFlags);
+#pragma unroll
+      for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16(rk, koff + cc * 64);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) vb[t] = ld_buf4(rv, voff + t * 16 * kBlk);
+    };
+    auto run = [&](const uint4 (&kb)[kKLoads], const VWord (&vb)[8]) {
+      block([&](int cc) {
+              return fp8x8_to_bf16x8((cc & 1) ? make_uint2(kb[cc >> 1].z, kb[cc >> 1].w)
+                                              : make_uint2(kb[cc >> 1].x, kb[cc >> 1].y));
+            },
+            [&](int t) {
+              return make_uint2(fp8x2_to_bf16x2<false>(vb[t]), fp8x2_to_bf16x2<true>(vb[t]));
+            });
+    };
+    uint4 kb0[kKLoads], kb1[kKLoads];
+    VWord vb0[8], vb1[8];
+    issue(0, kb0, vb0);
+    for (int i = 0; i < nb; i += 2) {
+      issue(i + 1, kb1, vb1);
+      run(kb0, vb0);
+      issue(i + 2, kb0, vb0);
+      if (i + 1 < nb) run(kb1, vb1);
+    }
+  } else {
+    // bf16 tiles go through an LDS ring of kPS blocks shared by the
+    // workgroup's four waves (the four column tiles of the same blocks):
+    // each block is read from L2/HBM once per workgroup, and kPS - 1 blocks
+    // are in flight.  Stage layout (8 KiB): K tile [16 keys][256 B] with the
+    // 16-byte chunks of key r at positions chunk ^ r; V tile [128 dims][32 B]
+    // with the 16-byte halves of dim d at half ^ ((d >> 3) & 1).  Direct-to-
+    // LDS loads (lane i's 16 bytes land at base + 16 i) fetch, per lane, the
+    // source chunk that its slot holds.  Wave w issues K load w (keys 4w ..
+    // 4w + 3) and V load w (dims 32 w .. 32 w + 31) of every block.
+    constexpr int kPS = 8;
+    constexpr int kStageBytes = 2 * kTileBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kPS * kStageBytes];
+    const int kr = 4 * wave + (lane >> 4), kp = lane & 15;        // K slot of this lane's load
+    const int ksrc = kr * (kD * 2) + ((kp ^ kr) & 15) * 16;
+    const int vd = 32 * wave + (lane >> 1), vq = lane & 1;        // V slot of this lane's load
+    const int vsrc = vd * (kBlk * 2) + ((vq ^ (vd >> 3)) & 1) * 16;
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      const bool live = i < nb;
+      int id = live ? __builtin_amdgcn_readlane(ids, i) : 0;
+      if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) {
+        bad = true;
+        id = 0;
+      }
+      const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes;
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
+                                                        static_cast<short>(0),
+                                                        live ? kTileBytes : 0, kBufferFlags);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
+                                                        static_cast<short>(0),
+                                                        live ? kTileBytes : 0, kBufferFlags);
+      uint8_t* st = ring + (i % kPS) * kStageBytes;
+      ld_buf_lds16(rk, st + wave * 1024, ksrc);
+      ld_buf_lds16(rv, st + kTileBytes + wave * 1024, vsrc);
+    };
+    // MFMA operands from a stage: K of key r16, 16-byte chunk 4 cc + j4;
+    // V of dim 16 t + r16, keys 4 j4 .. 4 j4 + 3 (8 bytes)
+    auto run = [&](int i) __attribute__((always_inline)) {
+      const uint8_t* st = ring + (i % kPS) * kStageBytes;
+      block([&](int cc) {
+              return *reinterpret_cast<const uint4*>(st + r16 * (kD * 2) +
+                                                     (((4 * cc + j4) ^ r16) & 15) * 16);
+            },
+            [&](int t) {
+              const int d = 16 * t + r16;
+              return *reinterpret_cast<const uint2*>(
+                  st + kTileBytes + d * (kBlk * 2) + (((j4 >> 1) ^ (d >> 3)) & 1) * 16 +
+                  (j4 & 1) * 8);
+            });
+    };
+    // Block i: wait for this wave's loads of block i (2 loads per block;
+    // those of the kPS - 2 later blocks may stay in flight), barrier (every
+    // wave's loads of block i landed, and every wave is done with block
+    // i - 1), refill that stage with block i + kPS - 1 (loads past the
+    // chunk's end have empty ranges: zeros, no traffic), then the block.
+#pragma unroll
+    for (int i = 0; i < kPS - 1; ++i) issue(i);
+    for (int i = 0; i < nb; ++i) {
+      wait_vmcnt<2 * (kPS - 2)>();
+      lds_barrier();
+      issue(i + kPS - 1);
+      if (wave_live) run(i);
+    }
+    wait_vmcnt<0>();
+    if (!wave_live) return;
   }
 
   l += __shfl_xor(l, 16);
