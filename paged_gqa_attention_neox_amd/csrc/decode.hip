@@ -804,13 +804,17 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
   y /= ca.max_chunks;
   const int g = y % a.num_kv_heads;
   const int p = y / a.num_kv_heads;
-  const int PB = group_prefix_blocks(a, ca, p);
+  // the host sizes the column workgroups for all members in one group, so
+  // most of them find no column of their group: they leave after one round
+  // of loads (the group's member range), before its length and table
   const int i0 = ca.indptr[p];
   const int cols = (ca.indptr[p + 1] - i0) * G;
+  if (xc * kNW * 16 >= cols) return;                   // uniform per workgroup
+  const int PB = group_prefix_blocks(a, ca, p);
   const int col0 = (xc * kNW + wave) * 16;
   const int bb = chunk * ca.chunk_blocks;
   const int be = min(PB, bb + ca.chunk_blocks);
-  if (PB == 0 || bb >= be || xc * kNW * 16 >= cols) return;   // uniform per workgroup
+  if (PB == 0 || bb >= be) return;                     // uniform per workgroup
   const int nb = be - bb;                              // <= 64 blocks
   // a wave whose 16 columns all lie past the group's pairs computes nothing
   // (with bf16 tiles it still loads its share of the workgroup's tiles)

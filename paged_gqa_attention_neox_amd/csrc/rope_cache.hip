@@ -201,9 +201,9 @@ template <> struct Vec8<float> {
 // RH = 2 for batches of at least 512 tokens (more bytes in flight per wave;
 // measured on the 2463-token prefill batch: 13.9 us with one head per item,
 // 12.0 with two, 12.1 with four); RH = 1 for smaller batches (more items to
-// spread: 64 tokens 3.8 against 4.0 us), for FP8 caches, whose encoding
-// needs the registers (17.0 against 18.2 us), and with the q/k norm (its
-// float64 norm per head: 17.0 against 18.7 us on the prefill batch).
+// spread: 64 tokens 3.8 against 4.0 us) and for FP8 caches, whose encoding
+// needs the registers (17.0 against 18.2 us).  With the q/k norm the
+// prefill batch takes 16.0 us with two heads, 16.4 with one.
 
 // CF8: the caches hold E4M3FN codes of (rotated) k / k_scale and v / v_scale.
 // QKN: Qwen3 q/k norm before the rotation ("nano-vllm: Qwen3 骨架", §5 the
@@ -316,7 +316,11 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
           for (int j = 0; j < 8; ++j) ss = fma(x1[j], x1[j], fma(x2[j], x2[j], ss));
 #pragma unroll
           for (int o = 1; o < RCH; o <<= 1) ss += __shfl_xor(ss, o);
-          const double rms = sqrt(ss / D + a.rms_eps);
+          // x / rms as x * (1 / rms): one float64 division per head instead
+          // of one per element (the product differs from the quotient by at
+          // most an ulp or two of float64, far below the single rounding to
+          // the storage type)
+          const double inv_rms = 1.0 / sqrt(ss / D + a.rms_eps);
           const T* wp = static_cast<const T*>(is_q ? a.q_norm_w : a.k_norm_w);
           Vec8<T> w1v, w2v;
           w1v.load(wp + i0);
@@ -326,8 +330,8 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
           w2v.to_f64(w2);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            x1[j] = x1[j] / rms * w1[j];
-            x2[j] = x2[j] / rms * w2[j];
+            x1[j] = x1[j] * inv_rms * w1[j];
+            x2[j] = x2[j] * inv_rms * w2[j];
           }
         }
         // float64 rotation: the inputs are exact, each output is rounded once
@@ -398,7 +402,7 @@ hipError_t launch_rope_cache_write(const RopeWriteArgs& a, hipStream_t stream) {
   const int d = a.head_dim;
   // the kernel's item space: rotation items, then v items padded to whole
   // waves and groups of 16 tokens
-  const int RH = a.cache_fp8 || a.q_norm_w || a.num_tokens < 512 ? 1 : 2;   // heads per item
+  const int RH = a.cache_fp8 || a.num_tokens < 512 ? 1 : 2;   // heads per rotation item
   const int64_t rot_total = static_cast<int64_t>(a.num_tokens) *
                             ((a.num_heads + a.num_kv_heads + RH - 1) / RH) * (d / 16);
   const int64_t total = (rot_total + 63) / 64 * 64 +
