@@ -126,6 +126,11 @@ SMALL = [
      [1] * 1000, 0),
     # 160 tiny prefill sequences (1..40 tokens): 640 (sequence, KV head) pairs
     ("prefill_160_tiny", "bf16", 28, 4, 128, list(range(1, 41)) * 4, list(range(1, 41)) * 4, 160),
+    # the decode schedule's switch at 32768 units ((sequence, KV head, block)
+    # triples): exactly 32768 takes one tier of equal ranges, one unit less
+    # the three shrinking tiers
+    ("decode_one_tier_at_threshold", "bf16", 28, 4, 128, [16384] * 8, [1] * 8, 0),
+    ("decode_three_tiers_below_threshold", "bf16", 28, 4, 128, [16384] * 7 + [16368], [1] * 8, 0),
 ]
 
 
