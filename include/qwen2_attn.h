@@ -41,8 +41,11 @@
  *   A token at logical position p of sequence s lives in physical block
  *   block_tables[s][p / block_size] at offset p % block_size; its slot is
  *   block * block_size + offset.
- * Supported shapes: head_dim 64 or 128, block_size 16, num_heads a multiple
- *   of num_kv_heads, group num_heads/num_kv_heads <= 16.
+ * Supported shapes: head_dim 64 or 128, block_size 16, 32 or 64 tokens,
+ *   num_heads a multiple of num_kv_heads, group num_heads/num_kv_heads <= 16.
+ *   ("Qwen2大模型架构解析与vLLM优化实践", §5.2 configures 64-token cache
+ *   blocks; "vLLM 部署 Qwen", §5.1 names a 16-token default raised to 32.
+ *   The matrix-core kernels read every size as 16-token blocks.)
  * Errors: host-side validation runs before any launch.  A failing call
  *   returns a nonzero qw_status, launches nothing and records a message for
  *   qwen2_last_error().  Zero-size work returns QW_OK without a launch.
@@ -374,7 +377,7 @@ int qwen3_rope_cache_write_fp8(const void* q, int64_t q_row_stride,
  *
  * num_prefixes, num_prefix_members, max_prefix_len: HOST ints (>= 0).  With
  * no group, no member or max_prefix_len < block_size, and for shapes other
- * than bf16 / head_dim 128 / block 16 / G <= 8, the call is the plain
+ * than bf16 / head_dim 128 / G <= 8, the call is the plain
  * decode.  Workspace: qwen2_attn_decode_cascade_workspace_size(...) bytes,
  * scratch as for the plain decode (it holds, besides the decode's part, the
  * prefix chunk states: about 16 chunks x num_seqs x num_heads x 520 bytes).

@@ -1,4 +1,5 @@
-// Paged single-token GQA decode for bf16, head_dim 128, block 16.  The cache
+// Paged single-token GQA decode for bf16, head_dim 128, cache blocks of 16,
+// 32 or 64 tokens (streamed as 16-token blocks).  The cache
 // may hold bf16 or FP8 E4M3FN codes ("Qwen2大模型架构解析与vLLM优化实践",
 // §4.1-4.2 FP8 KV-cache quantization with cache scales, §6.3 E4M3FN): FP8
 // tiles are half the bytes and are widened to bf16 in registers (exact),
@@ -334,10 +335,16 @@ __device__ __forceinline__ void fold_prefix(const DecodeKArgs& a, int s, int qh,
 // CAS: a cascade's private level (each sequence's keys after its shared
 // prefix; the prefix chunk states are folded in where a segment's output is
 // written).
-template <int G, bool F8, bool CAS>
+// BS: cache blocks of 16 << BS tokens.  The work units stay 16-token blocks:
+// unit b of a sequence is sub-block b % 2^BS of its table entry b >> BS,
+// whose K rows are contiguous and whose V rows are 16-key runs of the
+// longer dims rows of the [d][16 << BS] tile.
+template <int G, bool F8, bool CAS, int BS>
 __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) {
   constexpr int kEl = F8 ? 1 : 2;                 // bytes per cache element
-  constexpr int kTileBytes = kBlk * kD * kEl;
+  constexpr int kTileBytes = kBlk * kD * kEl;     // one 16-token (sub-)tile of K or V
+  constexpr int kBS = kBlk << BS;                 // tokens per cache block
+  constexpr int kVRange = (127 * kBS + kBlk) * kEl;   // V bytes from a sub-tile's start
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   // V: dim 16 t + r16, keys 4 j4 .. 4 j4 + 3 (bf16: 8 bytes; FP8: 4 bytes).
   constexpr int kKLoads = F8 ? 2 : 4;
   const int koff = r16 * kD * kEl + j4 * 16;
-  const int voff = (r16 * kBlk + j4 * 4) * kEl;
+  const int voff = (r16 * kBS + j4 * 4) * kEl;
   using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
   const float c = a.scale_log2;
 
@@ -402,14 +409,16 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
     const int ctx_raw = a.context_lens[s];
     bool bad = ctx_raw < 1 || ctx_raw > a.max_context_len;
     const int ctx = clamp_ctx(ctx_raw, a.max_context_len);
-    const int kb0 = b0 + (CAS ? a.cas[s].x : 0);   // the piece's first block in the table
-    const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks + kb0 + wave;
+    const int kb0 = b0 + (CAS ? a.cas[s].x : 0);   // the piece's first 16-token block
+    const int vb0 = kb0 + wave;                      // this wave's first 16-token block
+    const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
 
     // this wave's block ids, 64 at a time: lane i of ids_c holds its block
-    // cbase + i, of ids_n its block cbase + 64 + i
+    // cbase + i, of ids_n its block cbase + 64 + i (table entries; with
+    // longer cache blocks consecutive 16-token blocks share an entry)
     int cbase = 0;
-    int ids_c = lane < nbw ? bt[kNW * lane] : 0;
-    int ids_n = 64 + lane < nbw ? bt[kNW * (64 + lane)] : 0;
+    int ids_c = lane < nbw ? bt[(vb0 + kNW * lane) >> BS] : 0;
+    int ids_n = 64 + lane < nbw ? bt[(vb0 + kNW * (64 + lane)) >> BS] : 0;
 
     // q as the B operand in the dim order of the K pieces: chunk cc (32
     // dims) of lane (j4, head r16) holds dims 32 cc + 8 j4 .. (bf16 cache) or
@@ -442,21 +451,22 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
           id = 0;
         }
       }
-      const int64_t tile = (static_cast<int64_t>(id) * Hkv + g) * kTileBytes;
-      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
-                                                        static_cast<short>(0),
-                                                        live ? kTileBytes : 0, kBufferFlags);
-      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
-                                                        static_cast<short>(0),
-                                                        live ? kTileBytes : 0, kBufferFlags);
+      const int sub = (vb0 + kNW * i) & ((1 << BS) - 1);   // 16-token sub-block of the entry
+      const int64_t tile = (static_cast<int64_t>(id) * Hkv + g) * (kTileBytes << BS);
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.k_cache + tile + sub * kTileBytes), static_cast<short>(0),
+          live ? kTileBytes : 0, kBufferFlags);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.v_cache + tile + sub * kBlk * kEl), static_cast<short>(0),
+          live ? kVRange : 0, kBufferFlags);
 #pragma unroll
       for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16<kStream>(rk, koff + cc * 64);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         if constexpr (F8)
-          vb[t] = ld_buf4<kStream>(rv, voff + t * 16 * kBlk);
+          vb[t] = ld_buf4<kStream>(rv, voff + t * 16 * kBS);
         else
-          vb[t] = ld_buf8<kStream>(rv, voff + t * 16 * kBlk * 2);
+          vb[t] = ld_buf8<kStream>(rv, voff + t * 16 * kBS * 2);
       }
     };
 
@@ -546,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
           if (i + j == cbase + 64 && i + j < nbw) {   // next 64 ids; the window covers the prefetch
             cbase += 64;
             ids_c = ids_n;
-            ids_n = cbase + 64 + lane < nbw ? bt[kNW * (cbase + 64 + lane)] : 0;
+            ids_n = cbase + 64 + lane < nbw ? bt[(vb0 + kNW * (cbase + 64 + lane)) >> BS] : 0;
           }
           issue(i + j + kNBuf - 1, kb[(j + kNBuf - 1) % kNBuf], vb[(j + kNBuf - 1) % kNBuf]);
           if (i + j < nbw) block(i + j, kb[j], vb[j]);
@@ -744,10 +754,12 @@ struct CascadeArgs {
   int chunk_blocks, max_chunks, col_wgs;
 };
 
+// the group's prefix in 16-token blocks (0: the group is not attended)
+template <int BS>
 __device__ __forceinline__ int group_prefix_blocks(const DecodeKArgs& a, const CascadeArgs& ca,
                                                    int p) {
   const int L = ca.lens[p];
-  if (L <= 0 || L > ca.max_prefix_len || L % kBlk) return 0;
+  if (L <= 0 || L > ca.max_prefix_len || L % (kBlk << BS)) return 0;
   const int i0 = ca.indptr[p];
   if (i0 < 0 || i0 >= ca.num_members || ca.indptr[p + 1] <= i0 ||
       ca.indptr[p + 1] > ca.num_members)
@@ -760,6 +772,7 @@ __device__ __forceinline__ int group_prefix_blocks(const DecodeKArgs& a, const C
 
 // workgroup 0: zero the range and job counters and set cas[] for the
 // private level
+template <int BS>
 __device__ void cascade_prep(const DecodeKArgs& a, const CascadeArgs& ca) {
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -776,7 +789,7 @@ __device__ void cascade_prep(const DecodeKArgs& a, const CascadeArgs& ca) {
       if (ca.indptr[mid] <= i) lo = mid; else hi = mid - 1;
     }
     if (ca.indptr[lo] > i || ca.indptr[lo + 1] <= i) continue;
-    const int PB = group_prefix_blocks(a, ca, lo);
+    const int PB = group_prefix_blocks<BS>(a, ca, lo);
     const int s = ca.seqs[i];
     if (PB == 0 || s < 0 || s >= a.num_seqs) continue;
     if (PB >= nblocks_of(clamp_ctx(a.context_lens[s], a.max_context_len))) continue;
@@ -784,14 +797,16 @@ __device__ void cascade_prep(const DecodeKArgs& a, const CascadeArgs& ca) {
   }
 }
 
-template <int G, bool F8>
+template <int G, bool F8, int BS>
 __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, CascadeArgs ca) {
   if (blockIdx.x == 0) {
-    cascade_prep(a, ca);
+    cascade_prep<BS>(a, ca);
     return;
   }
   constexpr int kEl = F8 ? 1 : 2;
-  constexpr int kTileBytes = kBlk * kD * kEl;
+  constexpr int kTileBytes = kBlk * kD * kEl;     // one 16-token (sub-)tile of K or V
+  constexpr int kBS = kBlk << BS;                 // tokens per cache block
+  constexpr int kVRange = (127 * kBS + kBlk) * kEl;   // V bytes from a sub-tile's start
   constexpr int kKLoads = F8 ? 2 : 4;
   using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
   const int lane = threadIdx.x & 63;
@@ -810,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
   const int i0 = ca.indptr[p];
   const int cols = (ca.indptr[p + 1] - i0) * G;
   if (xc * kNW * 16 >= cols) return;                   // uniform per workgroup
-  const int PB = group_prefix_blocks(a, ca, p);
+  const int PB = group_prefix_blocks<BS>(a, ca, p);
   const int col0 = (xc * kNW + wave) * 16;
   const int bb = chunk * ca.chunk_blocks;
   const int be = min(PB, bb + ca.chunk_blocks);
@@ -838,9 +853,10 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
       qf[cc] = s >= 0 ? *reinterpret_cast<const uint4*>(qp + d) : make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  // the chunk's block ids, lane i holding block bb + i
+  // the chunk's block ids, lane i holding (the table entry of) 16-token block bb + i
   const int s0 = ca.seqs[i0];
-  const int ids = lane < nb ? a.block_tables[static_cast<int64_t>(s0) * a.max_blocks + bb + lane] : 0;
+  const int ids =
+      lane < nb ? a.block_tables[static_cast<int64_t>(s0) * a.max_blocks + ((bb + lane) >> BS)] : 0;
   const float c = a.scale_log2;
   bool bad = false;
 
@@ -882,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
     // FP8 tiles: each wave reads its tiles into registers (codes widened to
     // bf16 there), two blocks in flight
     const int koff = r16 * kD * kEl + j4 * 16;
-    const int voff = (r16 * kBlk + j4 * 4) * kEl;
+    const int voff = (r16 * kBS + j4 * 4) * kEl;
     auto issue = [&](int i, uint4 (&kb)[kKLoads], VWord (&vb)[8]) {
       const bool live = i < nb;
       int id = live ? __builtin_amdgcn_readlane(ids, i) : 0;
@@ -890,17 +906,18 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
         bad = true;
         id = 0;
       }
-      const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes;
-      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
-                                                        static_cast<short>(0),
-                                                        live ? kTileBytes : 0, kBufferFlags);
-      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
-                                                        static_cast<short>(0),
-                                                        live ? kTileBytes : 0, kBufferFlags);
+      const int sub = (bb + i) & ((1 << BS) - 1);
+      const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * (kTileBytes << BS);
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.k_cache + tile + sub * kTileBytes), static_cast<short>(0),
+          live ? kTileBytes : 0, kBufferFlags);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.v_cache + tile + sub * kBlk * kEl), static_cast<short>(0),
+          live ? kVRange : 0, kBufferFlags);
 #pragma unroll
       for (int cc = 0; cc < kKLoads; ++cc) kb[cc] = ld_buf16(rk, koff + cc * 64);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) vb[t] = ld_buf4(rv, voff + t * 16 * kBlk);
+      for (int t = 0; t < 8; ++t) vb[t] = ld_buf4(rv, voff + t * 16 * kBS);
     };
     auto run = [&](const uint4 (&kb)[kKLoads], const VWord (&vb)[8]) {
       block([&](int cc) {
@@ -936,7 +953,7 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
     const int kr = 4 * wave + (lane >> 4), kp = lane & 15;        // K slot of this lane's load
     const int ksrc = kr * (kD * 2) + ((kp ^ kr) & 15) * 16;
     const int vd = 32 * wave + (lane >> 1), vq = lane & 1;        // V slot of this lane's load
-    const int vsrc = vd * (kBlk * 2) + ((vq ^ (vd >> 3)) & 1) * 16;
+    const int vsrc = vd * (kBS * 2) + ((vq ^ (vd >> 3)) & 1) * 16;
     auto issue = [&](int i) __attribute__((always_inline)) {
       const bool live = i < nb;
       int id = live ? __builtin_amdgcn_readlane(ids, i) : 0;
@@ -944,13 +961,14 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
         bad = true;
         id = 0;
       }
-      const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kTileBytes;
-      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_cache + tile),
-                                                        static_cast<short>(0),
-                                                        live ? kTileBytes : 0, kBufferFlags);
-      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_cache + tile),
-                                                        static_cast<short>(0),
-                                                        live ? kTileBytes : 0, kBufferFlags);
+      const int sub = (bb + i) & ((1 << BS) - 1);
+      const int64_t tile = (static_cast<int64_t>(id) * a.num_kv_heads + g) * (kTileBytes << BS);
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.k_cache + tile + sub * kTileBytes), static_cast<short>(0),
+          live ? kTileBytes : 0, kBufferFlags);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.v_cache + tile + sub * kBlk * 2), static_cast<short>(0),
+          live ? kVRange : 0, kBufferFlags);
       uint8_t* st = ring + (i % kPS) * kStageBytes;
       ld_buf_lds16(rk, st + wave * 1024, ksrc);
       ld_buf_lds16(rv, st + kTileBytes + wave * 1024, vsrc);
@@ -1032,7 +1050,9 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   (void)cache_fp8;                    // both cache formats have the stream kernel
   DecodePlan p{};
   const int G = num_heads / num_kv_heads;
-  p.fast = dtype == kBF16 && head_dim == kD && block_size == kBlk && G >= 1 && G <= kMaxG;
+  p.fast = dtype == kBF16 && head_dim == kD &&
+           (block_size == kBlk || block_size == 2 * kBlk || block_size == 4 * kBlk) && G >= 1 &&
+           G <= kMaxG;
   if (!p.fast) return p;
   int wgs[kTiers];
   decode_schedule(num_seqs, max_context_len, num_kv_heads, wgs);
@@ -1043,14 +1063,28 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   return p;
 }
 
+// log2 of the cache block size in 16-token blocks (16, 32, 64 tokens; validated on the host)
+static int block_shift(int block_size) { return block_size == 4 * kBlk ? 2 : block_size == 2 * kBlk ? 1 : 0; }
+
+template <int G, int BS>
+static void launch_stream_bs(const DecodeKArgs& k, const AttnArgs& a, int grid, hipStream_t stream) {
+  if (a.cache_fp8)
+    hipLaunchKernelGGL((decode_stream_kernel<G, true, false, BS>), dim3(grid), dim3(kThreads), 0,
+                       stream, k);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<G, false, false, BS>), dim3(grid), dim3(kThreads), 0,
+                       stream, k);
+}
+
 template <int G>
 static void launch_stream(const DecodeKArgs& k, const AttnArgs& a, hipStream_t stream) {
   const int grid = k.num_ranges < kCUs ? k.num_ranges : kCUs;
   hipLaunchKernelGGL(decode_claim_reset_kernel, dim3(1), dim3(64), 0, stream, k.claim);
-  if (a.cache_fp8)
-    hipLaunchKernelGGL((decode_stream_kernel<G, true, false>), dim3(grid), dim3(kThreads), 0, stream, k);
-  else
-    hipLaunchKernelGGL((decode_stream_kernel<G, false, false>), dim3(grid), dim3(kThreads), 0, stream, k);
+  switch (block_shift(a.block_size)) {
+    case 0: launch_stream_bs<G, 0>(k, a, grid, stream); break;
+    case 1: launch_stream_bs<G, 1>(k, a, grid, stream); break;
+    default: launch_stream_bs<G, 2>(k, a, grid, stream); break;
+  }
   hipLaunchKernelGGL((decode_merge_kernel<G, false>), dim3(grid), dim3(G * kD), 0, stream, k);
 }
 
@@ -1113,8 +1147,10 @@ CascadePlan plan_cascade(int num_seqs, int max_context_len, int max_prefix_len, 
   c.dec = plan_decode(num_seqs, max_context_len, num_heads, num_kv_heads, head_dim, block_size,
                       dtype, cache_fp8);
   c.ws_bytes = c.dec.ws_bytes;
-  const int max_pb = max_prefix_len / kBlk;
-  c.active = c.dec.fast && max_pb > 0 && num_members > 0 && num_prefixes > 0;
+  if (!c.dec.fast) return c;
+  // prefixes are whole cache blocks; chunks count 16-token blocks
+  const int max_pb = max_prefix_len / block_size * (block_size / kBlk);
+  c.active = max_pb > 0 && num_members > 0 && num_prefixes > 0;
   if (!c.active) return c;
   const int G = num_heads / num_kv_heads;
   int cb = (max_pb + 15) / 16;            // about 16 chunks of 8..64 blocks
@@ -1131,17 +1167,29 @@ CascadePlan plan_cascade(int num_seqs, int max_context_len, int max_prefix_len, 
   return c;
 }
 
+template <int G, int BS>
+static void launch_cascade_bs(const DecodeKArgs& k, const CascadeArgs& ca, int grid, dim3 pgrid,
+                              const AttnArgs& a, hipStream_t stream) {
+  if (a.cache_fp8) {
+    hipLaunchKernelGGL((decode_prefix_kernel<G, true, BS>), pgrid, dim3(kThreads), 0, stream, k, ca);
+    hipLaunchKernelGGL((decode_stream_kernel<G, true, true, BS>), dim3(grid), dim3(kThreads), 0,
+                       stream, k);
+  } else {
+    hipLaunchKernelGGL((decode_prefix_kernel<G, false, BS>), pgrid, dim3(kThreads), 0, stream, k, ca);
+    hipLaunchKernelGGL((decode_stream_kernel<G, false, true, BS>), dim3(grid), dim3(kThreads), 0,
+                       stream, k);
+  }
+}
+
 template <int G>
 static void launch_cascade_g(const DecodeKArgs& k, const CascadeArgs& ca, int64_t tasks,
                              const AttnArgs& a, hipStream_t stream) {
   const int grid = k.num_ranges < kCUs ? k.num_ranges : kCUs;
   const dim3 pgrid(static_cast<unsigned>(1 + tasks));
-  if (a.cache_fp8) {
-    hipLaunchKernelGGL((decode_prefix_kernel<G, true>), pgrid, dim3(kThreads), 0, stream, k, ca);
-    hipLaunchKernelGGL((decode_stream_kernel<G, true, true>), dim3(grid), dim3(kThreads), 0, stream, k);
-  } else {
-    hipLaunchKernelGGL((decode_prefix_kernel<G, false>), pgrid, dim3(kThreads), 0, stream, k, ca);
-    hipLaunchKernelGGL((decode_stream_kernel<G, false, true>), dim3(grid), dim3(kThreads), 0, stream, k);
+  switch (block_shift(a.block_size)) {
+    case 0: launch_cascade_bs<G, 0>(k, ca, grid, pgrid, a, stream); break;
+    case 1: launch_cascade_bs<G, 1>(k, ca, grid, pgrid, a, stream); break;
+    default: launch_cascade_bs<G, 2>(k, ca, grid, pgrid, a, stream); break;
   }
   hipLaunchKernelGGL((decode_merge_kernel<G, true>), dim3(grid), dim3(G * kD), 0, stream, k);
 }

@@ -7,7 +7,8 @@
 // scaling head_dim^-0.5), keys gathered through the block table ("vLLM 部署
 // Qwen", §2.1).
 //
-// bf16, head_dim 128, block 16, group G <= 8:
+// bf16, head_dim 128, cache blocks of 16, 32 or 64 tokens (keys are taken
+// in 16-token blocks), group G <= 8:
 //   * one workgroup per (KV head, query tile, sequence), in one of two
 //     layouts chosen per launch by a cost estimate (key_groups below):
 //     - one key group: G waves, a wave owns 32 query columns = one head of
@@ -66,11 +67,11 @@ namespace qw {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kB = 16;               // tokens per cache block
+constexpr int kB = 16;               // tokens per key block (a cache block holds 16, 32 or 64)
 constexpr int kBK = 32;              // keys per key group and step
 constexpr int kTile = 16384;         // bytes of one 32-key tile in LDS: K 8 KiB + V^T 8 KiB
 constexpr int kTileLoads = 16;       // 1 KiB direct-to-LDS loads per 32-key tile
-constexpr int kBlockBytes = kB * kD * 2;   // one head's K (or V) of one cache block
+constexpr int kBlockBytes = kB * kD * 2;   // one head's K of one 16-token key block
 constexpr int kLdsBytes = 160 * 1024;   // LDS of one CU (a workgroup's static + dynamic share)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;        // raise the running max only past this margin (log2 units)
@@ -135,8 +136,9 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint8_t* l
 //           cache block b of the tile, dims row d, 8-key half h.
 // Load j (0..15) of a tile fills slots 64 j .. 64 j + 63: loads 0..7 the K
 // tile (block j / 4), loads 8..15 the V^T tile (block (j - 8) / 4).  Byte
-// offset inside the head's block tile of the chunk lane `lane` fetches:
-__device__ __forceinline__ int load_offset(int j, int lane) {
+// offset inside the head's 16-token (sub-)block of the chunk lane `lane`
+// fetches (vrow: bytes of one dims row of the V cache tile):
+__device__ __forceinline__ int load_offset(int j, int lane, int vrow) {
   if (j < 8) {
     const int kk = 4 * (j & 3) + (lane >> 4);          // key within the cache block
     const int c = (lane & 15) ^ perm23(kk);
@@ -145,7 +147,7 @@ __device__ __forceinline__ int load_offset(int j, int lane) {
   const int u = ((j - 8) & 3) * 64 + lane;
   const int d = u >> 1;
   const int h = (u & 1) ^ vswz(d);
-  return d * (kB * 2) + h * 16;
+  return d * vrow + h * 16;
 }
 
 // two E4M3FN codes (bytes 2 HI, 2 HI + 1 of w) -> a bf16 pair, exactly
@@ -161,7 +163,8 @@ __device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
 // into registers, widened exactly to bf16 and written to the same LDS
 // layout, one step ahead of the arithmetic; k_scale is folded into the
 // score scale and v_scale into the output.
-template <int KG, int WPG, bool F8>
+// BS: cache blocks of 16 << BS tokens, read as 16-token blocks.
+template <int KG, int WPG, bool F8, int BS>
 __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArgs a) {
   constexpr int NW = KG * WPG;                    // waves
   constexpr int HPW = KG == 1 ? 1 : 2;            // heads per wave
@@ -199,11 +202,12 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // this thread's block-table entry, fetched before (and in parallel with)
   // the sequence metadata: the table row needs only s
   const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
-  const int bt_early = tid < a.max_blocks ? bt[tid] : 0;
+  constexpr int bsh = BS;
+  const int bt_early = (tid >> bsh) < a.max_blocks ? bt[tid >> bsh] : 0;
   // the first 64 block ids again, lane i of every wave holding block i: the
   // first steps take their ids with v_readlane instead of an LDS round trip
   const int lane_id = tid & 63;
-  int idv = lane_id < a.max_blocks ? bt[lane_id] : 0;
+  int idv = (lane_id >> bsh) < a.max_blocks ? bt[lane_id >> bsh] : 0;
   // the sequence's context length is fetched with its row range, not after
   // it (one memory latency less before the first tile loads)
   int ctx = a.context_lens[s];
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     for (int i = tid; i < 2 * KG * nst; i += NW * 64) {
       int blk = 0;
       if (i < nblk) {
-        blk = i == tid ? bt_early : bt[i];
+        blk = i == tid ? bt_early : bt[i >> bsh];
         if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
           lbad = true;
           blk = 0;
@@ -278,15 +282,18 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // NW i, j / 16 the 32-key tile of the step, j % 16 the load within it)
   // (kept in registers when there are few; recomputed per load otherwise)
   const bool loader = !GROUPED || wave < 4 * KG;  // wave-uniform
+  const int vrow = (kB * 2) << bsh;               // bytes of a V cache tile's dims row
   constexpr int NV = NI <= 8 ? NI : 1;
   int voff[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int j = GROUPED ? 16 * (wave >> 2) + 4 * (wave & 3) + i : wave + NW * i;
-    voff[i] = loader && j < kLoads ? load_offset(j & 15, lane) : 0;
+    voff[i] = loader && j < kLoads ? load_offset(j & 15, lane, vrow) : 0;
   }
-  const int64_t head_off = static_cast<int64_t>(g) * (kB * kD);
-  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * (kB * kD);
+  const int64_t head_off = static_cast<int64_t>(g) * (kB * kD << bsh);
+  const int64_t blk_elems = static_cast<int64_t>(a.num_kv_heads) * (kB * kD << bsh);
+  const int submask = (1 << bsh) - 1;
+  const int vrange = (127 * (kB << bsh) + kB) * 2;   // V bytes from a sub-block's start
 
   // issue the loads of step t's keys into stage dst; a 32-key tile past the
   // causal limit gets empty ranges (no traffic).  Forced inline: with one or
@@ -314,9 +321,13 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
       const int bi = 2 * half + ((jj0 >> 2) & 1);
       const int blk = bi == 0 ? b0 : bi == 1 ? b1 : bi == 2 ? b2 : b3;
       const bool live = KG * t + half < nkt;
-      const uint16_t* base = (jj0 >= 8 ? a.v_cache : a.k_cache) + blk * blk_elems + head_off;
+      const int sub = (2 * KG * t + bi) & submask;   // 16-token sub-block of the entry
+      const bool isv = jj0 >= 8;
+      const uint16_t* base = (isv ? a.v_cache : a.k_cache) + blk * blk_elems + head_off +
+                             sub * (isv ? kB : kB * kD);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(base), static_cast<short>(0), live ? kBlockBytes : 0, 0x00020000);
+          const_cast<uint16_t*>(base), static_cast<short>(0),
+          live ? (isv ? vrange : kBlockBytes) : 0, 0x00020000);
       uint8_t* d = dst + half * kTile + jj0 * 1024;
 #pragma unroll
       for (int i = 0; i < 4; ++i) load_lds16(rs, d + i * 1024, voff[i]);
@@ -329,10 +340,14 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
       const bool live = j < kLoads && KG * t + half < nkt;
       const int bi = 2 * half + ((jj >> 2) & 1);
       const int blk = bi == 0 ? b0 : bi == 1 ? b1 : bi == 2 ? b2 : b3;
-      const uint16_t* base = (jj >= 8 ? a.v_cache : a.k_cache) + blk * blk_elems + head_off;
+      const int sub = (2 * KG * t + bi) & submask;
+      const bool isv = jj >= 8;
+      const uint16_t* base = (isv ? a.v_cache : a.k_cache) + blk * blk_elems + head_off +
+                             sub * (isv ? kB : kB * kD);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(base), static_cast<short>(0), live ? kBlockBytes : 0, 0x00020000);
-      const int vo = NI <= 8 ? voff[i < NV ? i : 0] : (j < kLoads ? load_offset(jj, lane) : 0);
+          const_cast<uint16_t*>(base), static_cast<short>(0),
+          live ? (isv ? vrange : kBlockBytes) : 0, 0x00020000);
+      const int vo = NI <= 8 ? voff[i < NV ? i : 0] : (j < kLoads ? load_offset(jj, lane, vrow) : 0);
       load_lds16(rs, j < kLoads ? dst + half * kTile + jj * 1024 : trash, vo);
     }
   };
@@ -468,30 +483,6 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     pv(alpha, stg);
   };
 
-  // One step: wait until step t's keys are in LDS for every wave (the wait
-  // leaves the loads of steps t + 1 and t + 2 outstanding), refill the stage
-  // of step t - 1 (every wave passed the barrier, so it finished with it)
-  // with step t + 3, then scores, softmax and PV of this key group's tile.
-  auto step = [&](int t, uint8_t* cur, uint8_t* refill) __attribute__((always_inline)) {
-    if (!loader) {
-      // no loads of this wave's own in flight
-    } else if (t + 2 < nst) {
-      wait_vm<2 * NI>();
-    } else if (t + 1 < nst) {
-      wait_vm<NI>();
-    } else {
-      wait_vm<0>();
-    }
-    barrier();
-    if (t == sani_st) {
-      sanitize(t, cur);
-      wait_lds();
-      barrier();
-    }
-    if (t + 3 < nst) issue(t + 3, refill);
-    if (KG * t + kg < nkt) finish(KG * t + kg, qk(cur), cur);
-  };
-
   if constexpr (F8) {
     // Chunk i of a step (8 codes -> one 16-byte LDS slot), tile hf = i / 1024
     // of the step, w = i % 1024:
@@ -508,8 +499,8 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     constexpr int kTile8 = kB * kD;                 // bytes of one head's FP8 K (or V) block tile
     const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(a.k_cache);
     const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(a.v_cache);
-    const int64_t head8 = static_cast<int64_t>(g) * kTile8;
-    const int64_t blk8 = static_cast<int64_t>(a.num_kv_heads) * kTile8;
+    const int64_t head8 = static_cast<int64_t>(g) * (kTile8 << bsh);
+    const int64_t blk8 = static_cast<int64_t>(a.num_kv_heads) * (kTile8 << bsh);
     auto gload = [&](int t, uint2 (&r)[NCH]) {
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
@@ -527,10 +518,12 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
           } else {
             const int v = w - 512;
             b = v >> 8;
-            off = ((v & 255) >> 1) * kB + (v & 1) * 8;
+            off = ((v & 255) >> 1) * (kB << bsh) + (v & 1) * 8;
             base = vc8;
           }
-          const int blk = sids[2 * (KG * t + hf) + b];
+          const int u = 2 * (KG * t + hf) + b;      // 16-token block of the sequence
+          off += (u & submask) * (w < 512 ? kB * kD : kB);
+          const int blk = sids[u];
           r[i] = *reinterpret_cast<const uint2*>(base + blk * blk8 + head8 + off);
         }
       }
@@ -701,17 +694,27 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   }
 }
 
-template <int KG, int WPG>
-void launch_kg(const PrefillKArgs& k, bool f8, size_t ids_bytes, hipStream_t stream) {
+template <int KG, int WPG, int BS>
+void launch_kg_bs(const PrefillKArgs& k, bool f8, size_t ids_bytes, hipStream_t stream) {
   const int64_t np = static_cast<int64_t>(k.num_kv_heads) * k.num_seqs;
   const int64_t slots = k.pairs_per_xcd > 0 ? int64_t{8} * k.pairs_per_xcd : np;
   const dim3 grid(static_cast<unsigned>(slots * k.num_qtiles));
   if (f8)
-    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, true>), grid, dim3(KG * WPG * 64), ids_bytes,
-                       stream, k);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, true, BS>), grid, dim3(KG * WPG * 64),
+                       ids_bytes, stream, k);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, false>), grid, dim3(KG * WPG * 64), ids_bytes,
-                       stream, k);
+    hipLaunchKernelGGL((prefill_mfma_kernel<KG, WPG, false, BS>), grid, dim3(KG * WPG * 64),
+                       ids_bytes, stream, k);
+}
+
+// bs: log2 of the cache block size in 16-token blocks
+template <int KG, int WPG>
+void launch_kg(const PrefillKArgs& k, bool f8, int bs, size_t ids_bytes, hipStream_t stream) {
+  switch (bs) {
+    case 0: launch_kg_bs<KG, WPG, 0>(k, f8, ids_bytes, stream); break;
+    case 1: launch_kg_bs<KG, WPG, 1>(k, f8, ids_bytes, stream); break;
+    default: launch_kg_bs<KG, WPG, 2>(k, f8, ids_bytes, stream); break;
+  }
 }
 
 }  // namespace
@@ -755,7 +758,8 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   // (half the stage bytes) takes the call
   if (KG == 2 && staged_ids(2, a.max_context_len) * 4 > kLdsBytes - lds_static_bytes(2)) KG = 1;
   const int ids = staged_ids(KG, a.max_context_len);
-  const bool mfma = a.dtype == kBF16 && a.head_dim == kD && a.block_size == kB &&
+  const bool mfma = a.dtype == kBF16 && a.head_dim == kD &&
+                    (a.block_size == kB || a.block_size == 2 * kB || a.block_size == 4 * kB) &&
                     G >= 1 && G <= 8 && ids * 4 <= kLdsBytes - lds_static_bytes(KG);
   if (!mfma) return launch_attn_generic(a, stream);
   PrefillKArgs k{};
@@ -787,25 +791,26 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   k.pairs_per_xcd = np >= 8 && (KG == 1 || np == 8) ? (np + 7) / 8 : 0;
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
+  const int bs = a.block_size == 4 * kB ? 2 : a.block_size == 2 * kB ? 1 : 0;
   const bool f8 = a.cache_fp8 != 0;
   const size_t ids_bytes = static_cast<size_t>(ids) * 4;
   if (KG == 1) {
     switch (G) {
-      case 1: launch_kg<1, 1>(k, f8, ids_bytes, stream); break;
-      case 2: launch_kg<1, 2>(k, f8, ids_bytes, stream); break;
-      case 3: launch_kg<1, 3>(k, f8, ids_bytes, stream); break;
-      case 4: launch_kg<1, 4>(k, f8, ids_bytes, stream); break;
-      case 5: launch_kg<1, 5>(k, f8, ids_bytes, stream); break;
-      case 6: launch_kg<1, 6>(k, f8, ids_bytes, stream); break;
-      case 7: launch_kg<1, 7>(k, f8, ids_bytes, stream); break;
-      default: launch_kg<1, 8>(k, f8, ids_bytes, stream); break;
+      case 1: launch_kg<1, 1>(k, f8, bs, ids_bytes, stream); break;
+      case 2: launch_kg<1, 2>(k, f8, bs, ids_bytes, stream); break;
+      case 3: launch_kg<1, 3>(k, f8, bs, ids_bytes, stream); break;
+      case 4: launch_kg<1, 4>(k, f8, bs, ids_bytes, stream); break;
+      case 5: launch_kg<1, 5>(k, f8, bs, ids_bytes, stream); break;
+      case 6: launch_kg<1, 6>(k, f8, bs, ids_bytes, stream); break;
+      case 7: launch_kg<1, 7>(k, f8, bs, ids_bytes, stream); break;
+      default: launch_kg<1, 8>(k, f8, bs, ids_bytes, stream); break;
     }
   } else {
     switch ((G + 1) / 2) {
-      case 1: launch_kg<2, 1>(k, f8, ids_bytes, stream); break;
-      case 2: launch_kg<2, 2>(k, f8, ids_bytes, stream); break;
-      case 3: launch_kg<2, 3>(k, f8, ids_bytes, stream); break;
-      default: launch_kg<2, 4>(k, f8, ids_bytes, stream); break;
+      case 1: launch_kg<2, 1>(k, f8, bs, ids_bytes, stream); break;
+      case 2: launch_kg<2, 2>(k, f8, bs, ids_bytes, stream); break;
+      case 3: launch_kg<2, 3>(k, f8, bs, ids_bytes, stream); break;
+      default: launch_kg<2, 4>(k, f8, bs, ids_bytes, stream); break;
     }
   }
   return hipGetLastError();

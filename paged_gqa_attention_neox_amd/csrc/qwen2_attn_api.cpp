@@ -47,7 +47,8 @@ int check_heads(int num_heads, int num_kv_heads, int head_dim, int block_size, i
     return fail(QW_ERR_UNSUPPORTED, "group %d > 16 not supported", num_heads / num_kv_heads);
   if (head_dim != 64 && head_dim != 128)
     return fail(QW_ERR_UNSUPPORTED, "head_dim=%d not supported (64 or 128)", head_dim);
-  if (block_size != 16) return fail(QW_ERR_UNSUPPORTED, "block_size=%d not supported (16)", block_size);
+  if (block_size != 16 && block_size != 32 && block_size != 64)
+    return fail(QW_ERR_UNSUPPORTED, "block_size=%d not supported (16, 32 or 64)", block_size);
   return QW_OK;
 }
 

@@ -217,7 +217,8 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
   constexpr int HALF = D / 2;
   constexpr int RCH = HALF / 8;   // chunks of 8 pairs per head
   constexpr int VCH = D / 8;      // v items per head (8 elements each)
-  constexpr int B = 16;           // tokens per cache block (validated on the host)
+  const int B = a.block_size;     // tokens per cache block: 16, 32 or 64 (validated on the host)
+  const int lb = 31 - __builtin_clz(B);
   const int H = a.num_heads, Hkv = a.num_kv_heads;
   const int NH = H + Hkv;                         // rotated heads per token
   const int rot_items = (NH + kRH - 1) / kRH * RCH;
@@ -271,8 +272,8 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       const int slot = a.slots[t];
       const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
       const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
-      const int64_t blk = slot_ok ? slot / B : 0;
-      const int off = slot_ok ? slot % B : 0;
+      const int64_t blk = slot_ok ? slot >> lb : 0;
+      const int off = slot_ok ? slot & (B - 1) : 0;
       double cv[8], sv[8];
       if (pos_ok) {
         const double* cs = a.cos_sin + static_cast<int64_t>(pos) * D;
@@ -378,8 +379,8 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
       const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
       if (!(pos_ok && slot_ok)) continue;
-      const int64_t blk = slot / B;
-      const int off = slot % B;
+      const int64_t blk = slot >> lb;
+      const int off = slot & (B - 1);
       if (CF8) {
         double xv[8];
         x.to_f64(xv);

@@ -201,3 +201,21 @@ def check_caches(batch, res, ora):
     assert wm[diff[0], diff[2]].all(), "K cache changed at slots the step does not write"
     blk, off = np.nonzero(wm)
     check_rotated(kc_g[blk, :, off, :], kc_o[blk, :, off, :], dt, "K cache (written slots)")
+
+
+def full_check(batch, seqs=None, label=""):
+    say(f"{label or batch.name}: GPU step")
+    res, _ = run_gpu(batch)
+    say(f"{label or batch.name}: oracle")
+    ora = run_oracle(batch, seqs=seqs)
+    dt = batch.shape.dtype
+    check_rotated(res["q_out"], ora["q_out"], dt, "q_out")
+    check_caches(batch, res, ora)
+    if seqs is None:
+        rows = None
+    else:
+        cu = batch.cu_seqlens_q
+        rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    mx, mean = check_out(res["out"], ora["out"], dt, rows=rows)
+    say(f"{label or batch.name}: out max abs {mx:.3e} mean abs {mean:.3e}")
+    return res, ora

@@ -89,7 +89,9 @@ def _decode(lib, **kw):
     (dict(bt=0), QW_ERR_NULL),
     (dict(H=30), QW_ERR_SHAPE),                    # not a multiple of Hkv
     (dict(d=96, qs=28 * 96, os=28 * 96), QW_ERR_UNSUPPORTED),
-    (dict(B=32), QW_ERR_UNSUPPORTED),
+    (dict(B=48), QW_ERR_UNSUPPORTED),              # block sizes: 16, 32 or 64 tokens
+    (dict(B=8), QW_ERR_UNSUPPORTED),
+    (dict(B=128), QW_ERR_UNSUPPORTED),
     (dict(dt=5), QW_ERR_UNSUPPORTED),
     (dict(H=68, Hkv=4, qs=68 * 128, os=68 * 128), QW_ERR_UNSUPPORTED),   # group 17
     (dict(q=MIS), QW_ERR_ALIGN),
@@ -127,6 +129,10 @@ def test_workspace_size(lib):
     assert 0 < small <= 1024 + 3 * 2 * 7 * 130 * 4
     assert B.qwen2_attn_decode_workspace_size(8, 512, 28, 4, 128, 16, bf16) > small
     assert lib.qwen2_attn_decode_workspace_size(8, 100, 28, 4, 96, 16, 1) == ctypes.c_size_t(-1).value
+    # 32- and 64-token cache blocks are streamed as 16-token blocks: the same plan
+    for bs in (32, 64):
+        assert B.qwen2_attn_decode_workspace_size(64, 32768, 28, 4, 128, bs, bf16) == n
+    assert lib.qwen2_attn_decode_workspace_size(8, 100, 28, 4, 128, 48, 1) == ctypes.c_size_t(-1).value
 
 
 def _rope(lib, **kw):
@@ -146,7 +152,7 @@ def _rope(lib, **kw):
     (dict(qs=128), QW_ERR_SHAPE), (dict(Hkv=3), QW_ERR_SHAPE),
     (dict(k=MIS), QW_ERR_ALIGN), (dict(cs=MIS), QW_ERR_ALIGN),
     (dict(qo=P + 64), QW_ERR_SHAPE),            # overlaps q without being q
-    (dict(d=80), QW_ERR_UNSUPPORTED),
+    (dict(d=80), QW_ERR_UNSUPPORTED), (dict(B=48), QW_ERR_UNSUPPORTED), (dict(B=8), QW_ERR_UNSUPPORTED),
 ])
 def test_rope_validation(lib, kw, status):
     assert _rope(lib, **kw) == status
@@ -397,7 +403,7 @@ def _decode_noalloc(lib, **kw):
     (dict(out=0), QW_ERR_NULL),
     (dict(bt=0), QW_ERR_NULL),
     (dict(H=30), QW_ERR_SHAPE),
-    (dict(B=32), QW_ERR_UNSUPPORTED),
+    (dict(B=48), QW_ERR_UNSUPPORTED),
     (dict(q=MIS), QW_ERR_ALIGN),
     (dict(mb=8), QW_ERR_SHAPE),
     (dict(S=-1), QW_ERR_SHAPE),

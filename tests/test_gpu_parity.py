@@ -13,8 +13,8 @@ import torch
 import oracle.reference as R
 from paged_gqa_attention_neox_amd import runner
 from paged_gqa_attention_neox_amd import workloads as W
-from gpu_common import (bits, check_caches, check_out, check_rotated, key_groups, require_gpu,
-                        run_gpu, run_oracle, say)
+from gpu_common import (bits, check_caches, check_out, check_rotated, full_check, key_groups,
+                        require_gpu, run_gpu, run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,24 +22,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     require_gpu()
-
-
-def full_check(batch, seqs=None, label=""):
-    say(f"{label or batch.name}: GPU step")
-    res, _ = run_gpu(batch)
-    say(f"{label or batch.name}: oracle")
-    ora = run_oracle(batch, seqs=seqs)
-    dt = batch.shape.dtype
-    check_rotated(res["q_out"], ora["q_out"], dt, "q_out")
-    check_caches(batch, res, ora)
-    if seqs is None:
-        rows = None
-    else:
-        cu = batch.cu_seqlens_q
-        rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
-    mx, mean = check_out(res["out"], ora["out"], dt, rows=rows)
-    say(f"{label or batch.name}: out max abs {mx:.3e} mean abs {mean:.3e}")
-    return res, ora
 
 
 # ---------------------------------------------------------------------------
