@@ -15,9 +15,11 @@
 // triples in that order, cut into contiguous ranges by a fixed schedule of
 // shrinking sizes: 75% of the units in kCUs ranges, 15% in kCUs, 10% in
 // 2 kCUs.  One persistent 4-wave workgroup per CU (its LDS reservation
-// admits no second one) claims ranges in order from a device-wide counter,
-// so CUs and XCDs that stream faster (measured: up to ~20% apart) take more
-// of the small ranges at the end and all finish together.  Which ranges a
+// admits no second one) takes range i = its index first and then claims
+// ranges in order from a device-wide counter, so CUs and XCDs that stream
+// faster (measured: up to ~20% apart) take more of the small ranges at the
+// end and all finish together.  (A first claim by every workgroup at once
+// queued ~2.5 us of atomics on the counter before any tile load.)  Which ranges a
 // workgroup gets varies; what is computed for each range does not.
 // A range covers whole (sequence, KV head) segments, which its workgroup
 // finishes itself, and at most two pieces of segments that other ranges
@@ -164,7 +166,7 @@ struct DecodeKArgs {
   int num_heads, num_kv_heads, max_context_len;
   int tier_wgs[kTiers];   // most ranges per tier (for the host's bound on U); R = their sum
   int num_ranges;
-  int* claim;             // range counter, zero at launch
+  int* claim;             // [0] range counter, [2] merge-job count: zero at launch
   int4* desc;             // per range: merge source range (-1: none), flags, segment (s, g)
   int* jobs;              // ranges whose first piece ends a shared segment (count in claim[2])
   float scale_log2;   // scale * log2 e (* k_scale with an FP8 cache)
@@ -371,16 +373,20 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   using VWord = typename std::conditional<F8, uint32_t, uint2>::type;
   const float c = a.scale_log2;
 
-  // Ranges are claimed in order.  The next claim is made a few blocks before
-  // the current range ends (by thread 0), so its latency is hidden but a
-  // workgroup never holds a range it has not nearly reached.
-  if (tid == 0) s_next = atomicAdd(a.claim, 1);
-  __syncthreads();
-  int rg = s_next;
-  __syncthreads();                       // every thread has read s_next
+  // Workgroup i takes range i first; later ranges are claimed in order
+  // (gridDim.x + the counter), each a few blocks before the current range
+  // ends (by thread 0), so its latency is hidden but a workgroup never holds
+  // a range it has not nearly reached.
+  int rg = blockIdx.x;
   while (rg < sched.R) {
   int next = 0;
   bool claimed = false;
+  // thread 0: whether this range's first piece ends a shared segment (a
+  // merge job), and the job's slot.  The slot's atomic goes out after the
+  // range's first tile loads and is stored when the range ends, so no wave
+  // waits for it (the first ranges all start at once).
+  bool job = false;
+  int jslot = -1;
   const int64_t u0 = range_begin(sched, rg, U), u1 = range_begin(sched, rg + 1, U);
   if (u0 >= u1) {
     if (tid == 0) a.desc[rg] = make_int4(-1, kRangeEmpty, 0, 0);
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
       d.y = range_begin(sched, ra, U) == cur.seg0 ? kRangeFirst : 0;
     }
     a.desc[rg] = d;
-    if (d.x >= 0) a.jobs[atomicAdd(a.claim + 2, 1)] = rg;
+    job = d.x >= 0;
   }
   int64_t u = u0;
   bool first_piece = true;
@@ -546,11 +552,15 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
       VWord vb[kNBuf][8];
 #pragma unroll
       for (int j = 0; j < kNBuf - 1; ++j) issue(j, kb[j], vb[j]);
+      if (job) {
+        jslot = atomicAdd(a.claim + 2, 1);
+        job = false;
+      }
       for (int i = 0; i < nbw; i += kNBuf) {
 #pragma unroll
         for (int j = 0; j < kNBuf; ++j) {
           if (i + j == claim_at) {
-            if (lane == 0) next = atomicAdd(a.claim, 1);
+            if (lane == 0) next = gridDim.x + atomicAdd(a.claim, 1);
             claimed = true;
           }
           if (i + j == cbase + 64 && i + j < nbw) {   // next 64 ids; the window covers the prefetch
@@ -621,7 +631,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
     }
   }
   }
-  if (tid == 0) s_next = claimed ? next : atomicAdd(a.claim, 1);
+  if (jslot >= 0) a.jobs[jslot] = rg;
+  if (tid == 0) s_next = claimed ? next : gridDim.x + atomicAdd(a.claim, 1);
   __syncthreads();                       // s_next is written; the merge buffers are free
   rg = s_next;
   __syncthreads();                       // every thread has read s_next
