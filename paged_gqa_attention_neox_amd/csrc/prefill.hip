@@ -77,6 +77,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;        // raise the running max only past this margin (log2 units)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct PrefillKArgs {
@@ -659,7 +660,11 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   // ---- epilogue: O = O^T / l, column col -> (row q0 + rq, head hq) ----
   // The wave's 32 x 128 bf16 tile goes through LDS (16-byte slots, slot of
   // (column, dims chunk c) = column * 16 + (c ^ (column & 15))) so that each
-  // store instruction writes four whole 256-byte output rows.
+  // store instruction writes four whole 256-byte output rows.  The stores
+  // carry the non-temporal hint: the output streams to memory while other
+  // workgroups compute, instead of staying dirty in L2 for the write-back
+  // at the kernel's end (measured: the Qwen2-7B batch 21.2 -> 20.0 us, the
+  // same batch over an FP8 cache 24.8 -> 23.1 us).
   const float lt = l + __shfl_xor(l, 32);
   const float inv = bad ? __builtin_nanf("") : a.out_scale / lt;
   uint8_t* ot;                                    // this wave's 8 KiB in the (free) ring
@@ -689,7 +694,8 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
     if (orow < n && oslot < G) {
       uint16_t* op = a.out + static_cast<int64_t>(r0 + orow) * a.out_stride +
                      static_cast<int64_t>(g * G + oslot) * kD + c * 8;
-      *reinterpret_cast<uint4*>(op) = v;
+      const u32x4_t vv = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(vv, reinterpret_cast<u32x4_t*>(op));
     }
   }
 }
