@@ -823,16 +823,21 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int r16 = lane & 15, j4 = lane >> 4;
+  // Tasks in the order (column tile xc, group p, KV head g, chunk), the
+  // column tile slowest.  The host sizes the column tiles for all members in
+  // one group, so with several groups most tiles past the first few find no
+  // column of their group: they leave after one round of loads (the group's
+  // member range), and coming last in the grid they do so while the live
+  // workgroups finish instead of holding CU slots among them (measured: the
+  // shared-prompt cascade 98.5 -> 85.2 us against the tile fastest).
   const int task = blockIdx.x - 1;
-  const int xc = task % ca.col_wgs;
-  int y = task / ca.col_wgs;
+  const int ny = ca.num_prefixes * a.num_kv_heads * ca.max_chunks;
+  const int xc = task / ny;
+  int y = task - xc * ny;
   const int chunk = y % ca.max_chunks;
   y /= ca.max_chunks;
   const int g = y % a.num_kv_heads;
   const int p = y / a.num_kv_heads;
-  // the host sizes the column workgroups for all members in one group, so
-  // most of them find no column of their group: they leave after one round
-  // of loads (the group's member range), before its length and table
   const int i0 = ca.indptr[p];
   const int cols = (ca.indptr[p + 1] - i0) * G;
   if (xc * kNW * 16 >= cols) return;                   // uniform per workgroup
