@@ -55,10 +55,14 @@
  *   named twice in one call; block ids of the first ceil(c/B) table entries
  *   in [0, num_blocks); 1 <= context_lens[s] <= max_context_len; query rows
  *   of a sequence sit at positions c - n .. c - 1.  Kernels bounds-check
- *   positions, slots and block ids: a token with an out-of-range position or
- *   slot is not written (its q_out row is set to NaN), and a sequence that
- *   names an out-of-range block produces NaN outputs -- never an
- *   out-of-bounds access.  qwen2_check_metadata_host() verifies the whole
+ *   this metadata and never access memory out of bounds for it: a token
+ *   with an out-of-range position writes no K/V and a NaN q_out row; one
+ *   with an out-of-range slot writes no K/V (q_out as usual); a sequence
+ *   with an out-of-range block id or context length (or more rows than
+ *   keys) produces NaN outputs; a prefill sequence whose rows lie outside
+ *   the packed batch or number more than max_context_len writes no rows.
+ *   Each case also sets a flag in the GPU's device error word
+ *   (qwen2_device_errors).  qwen2_check_metadata_host() verifies the whole
  *   contract on host copies.
  * Order per layer step: qwen2_rope_cache_write, then qwen2_attn_prefill_varlen
  *   and/or qwen2_attn_decode_paged, on the same stream.
@@ -468,6 +472,28 @@ int qwen2_check_metadata_host(const int32_t* positions, const int32_t* slot_mapp
                               int num_seqs, int max_blocks_per_seq, int num_blocks,
                               int block_size, int max_position, int max_context_len,
                               int max_query_len);
+
+/*
+ * Device error word (debugging aid).  Each GPU holds one 32-bit word inside
+ * the library, zero when the library loads.  When a kernel meets device
+ * metadata outside the contract above, besides producing NaN outputs or
+ * skipping the write it ORs a flag into the word of the GPU it runs on:
+ */
+#define QW_DEVICE_ERR_POSITION 1u  /* a position outside [0, max_position) */
+#define QW_DEVICE_ERR_SLOT 2u      /* a slot outside [-1, num_blocks * block_size) */
+#define QW_DEVICE_ERR_BLOCK 4u     /* a block id the attention reads outside [0, num_blocks) */
+#define QW_DEVICE_ERR_SEQUENCE 8u  /* a context length outside [1, max_context_len], more rows than
+                                      keys, or a row range outside the packed batch (a negative
+                                      row count included) */
+/*
+ * qwen2_device_errors reads the current device's word into *flags (HOST
+ * pointer) and, if clear != 0, resets it to zero.  It synchronises with the
+ * device (a blocking copy), so it is for tests and debugging, not for a hot
+ * path or graph capture.  The word gathers the flags of every call on that
+ * GPU since it was last cleared, from any thread or stream.  Returns QW_OK,
+ * QW_ERR_NULL for a NULL flags pointer, or QW_ERR_HIP.
+ */
+int qwen2_device_errors(unsigned int* flags, int clear);
 
 /* Static text for a qw_status value. */
 const char* qwen2_status_string(int status);

@@ -61,9 +61,13 @@ SIGNATURES = {
                                                  _i, _f, _i, _f, _f, _p]),
     "qwen2_check_prefix_groups_host": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _i, _i, _i]),
     "qwen2_check_metadata_host": (_i, [_p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i]),
+    "qwen2_device_errors": (_i, [_p, _i]),
     "qwen2_status_string": (ctypes.c_char_p, [_i]),
     "qwen2_last_error": (ctypes.c_char_p, []),
 }
+
+# flags of qwen2_device_errors (QW_DEVICE_ERR_* in the header)
+DEVICE_ERR_POSITION, DEVICE_ERR_SLOT, DEVICE_ERR_BLOCK, DEVICE_ERR_SEQUENCE = 1, 2, 4, 8
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -450,6 +454,14 @@ def qwen2_check_prefix_groups_host(prefix_indptr, prefix_seqs, prefix_lens, max_
                                                 len(lens), len(seqs), int(max_prefix_len),
                                                 ctx.ctypes.data, bt.ctypes.data, len(ctx),
                                                 bt.shape[1], block_size))
+
+
+def qwen2_device_errors(clear: bool = False) -> int:
+    """The current GPU's device error word (QW_DEVICE_ERR_* flags gathered
+    since it was last cleared); clear=True resets it.  Synchronises."""
+    flags = ctypes.c_uint(0)
+    _check("qwen2_device_errors", lib().qwen2_device_errors(ctypes.addressof(flags), int(clear)))
+    return int(flags.value)
 
 
 def status_string(status: int) -> str:

@@ -39,15 +39,21 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     r0 = s;
     n = 1;
   }
+  // a row range outside the packed batch (bad cu_seqlens), a negative row
+  // count or more rows than any valid context holds: flag, write no row
+  if (r0 < 0 || n < 0 || static_cast<int64_t>(r0) + n > a.num_tokens || n > a.max_context_len) {
+    if (row == 0) report_error(a.err, kErrSequence);
+    return;
+  }
   if (row >= n) return;
   int c = a.context_lens[s];
   bool bad = c < 1 || c > a.max_context_len;   // contract: 1 <= c <= max_context_len
+  if (bad) report_error(a.err, kErrSequence);
   if (bad) c = 0;
   const int pos = c - n + row;
   const int Hkv = a.num_kv_heads, B = a.block_size;
   const int g = h / (a.num_heads / Hkv);
   const int64_t t = static_cast<int64_t>(r0) + row;
-  if (r0 < 0 || t >= a.num_tokens) return;       // rows outside the packed batch (bad cu_seqlens)
   const T* qp = static_cast<const T*>(a.q) + t * a.q_stride + static_cast<int64_t>(h) * D;
   const C* kc = static_cast<const C*>(a.k_cache);
   const C* vc = static_cast<const C*>(a.v_cache);
@@ -62,11 +68,13 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
     acc[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
+  if (pos < 0) report_error(a.err, kErrSequence);   // more rows than keys
   bad = bad || pos < 0;
   for (int j = 0; j <= pos; ++j) {
     const int blk = bt[j / B];
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
       bad = true;
+      report_error(a.err, kErrBlock);
       break;
     }
     const int off = j % B;

@@ -77,4 +77,13 @@ __device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Device error word: kernels that meet metadata outside its contract (a
+// position, slot, block id or sequence length out of range) OR one of these
+// flags into the word (err may be null: no report).  Only the error path
+// touches it.  The values are those of QW_DEVICE_ERR_* in the public header.
+constexpr unsigned kErrPosition = 1u, kErrSlot = 2u, kErrBlock = 4u, kErrSequence = 8u;
+__device__ __forceinline__ void report_error(unsigned* err, unsigned flag) {
+  if (err) atomicOr(err, flag);
+}
+
 }  // namespace qw

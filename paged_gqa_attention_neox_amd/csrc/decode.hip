@@ -175,6 +175,7 @@ struct DecodeKArgs {
   int2* cas;              // per sequence: prefix blocks it skips, prefix chunks to fold in
   float* pre_ml;          // [chunk][S H][2]: prefix chunk states (reference max, sum)
   float* pre_acc;         // [chunk][S H][128]: prefix chunk partial outputs
+  unsigned* err;          // the device error word (may be null)
 };
 
 // Context lengths are clamped to [1, max_context_len] (what the workspace
@@ -413,7 +414,8 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
     const int cnt = static_cast<int>(min(static_cast<int64_t>(n - b0), u1 - u));
     const int nbw = cnt > wave ? (cnt - wave + kNW - 1) / kNW : 0;
     const int ctx_raw = a.context_lens[s];
-    bool bad = ctx_raw < 1 || ctx_raw > a.max_context_len;
+    // error flags of the piece (wave-uniform), reported once at its end
+    unsigned bad = ctx_raw < 1 || ctx_raw > a.max_context_len ? kErrSequence : 0u;
     const int ctx = clamp_ctx(ctx_raw, a.max_context_len);
     const int kb0 = b0 + (CAS ? a.cas[s].x : 0);   // the piece's first 16-token block
     const int vb0 = kb0 + wave;                      // this wave's first 16-token block
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
         const int k = i - cbase;
         id = k < 64 ? __builtin_amdgcn_readlane(ids_c, k) : __builtin_amdgcn_readlane(ids_n, k - 64);
         if (static_cast<unsigned>(id) >= static_cast<unsigned>(a.num_blocks)) {
-          bad = true;
+          bad |= kErrBlock;
           id = 0;
         }
       }
@@ -587,11 +589,13 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
         sl[wave][r16] = l;
       }
     }
-    if (lane == 0) sbad[wave] = bad;
+    if (lane == 0) sbad[wave] = static_cast<int>(bad);
     __syncthreads();
-    bool pbad = false;
+    unsigned pflags = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) pbad = pbad || sbad[w] != 0;
+    for (int w = 0; w < kNW; ++w) pflags |= static_cast<unsigned>(sbad[w]);
+    const bool pbad = pflags != 0;
+    if (pbad && tid == 0) report_error(a.err, pflags);
     const bool whole = b0 == 0 && cnt == n;
     const int64_t slot = 2 * static_cast<int64_t>(rg) + (first_piece ? 0 : 1);
     for (int idx = tid; idx < G * kD; idx += kThreads) {
@@ -1023,6 +1027,7 @@ __global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, 
 
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  if (bad && lane == 0) report_error(a.err, kErrBlock);
   if (s >= 0) {
     const int64_t row = static_cast<int64_t>(chunk) * a.num_seqs * a.num_heads +
                         static_cast<int64_t>(s) * a.num_heads + qh;
@@ -1126,6 +1131,7 @@ static DecodeKArgs make_kargs(const AttnArgs& a) {
   for (int t = 0; t < kTiers; ++t) k.num_ranges += k.tier_wgs[t];
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
+  k.err = a.err;
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   k.claim = reinterpret_cast<int*>(ws);
   k.desc = reinterpret_cast<int4*>(ws + kWsHeader);

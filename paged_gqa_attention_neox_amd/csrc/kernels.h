@@ -26,6 +26,7 @@ struct RopeWriteArgs {
   const void* q_norm_w;          // Qwen3 q/k RMSNorm weights [head_dim] (dtype), or null
   const void* k_norm_w;
   double rms_eps;
+  unsigned* err;                 // the GPU's device error word (may be null)
 };
 
 struct AttnArgs {
@@ -42,6 +43,7 @@ struct AttnArgs {
   void* workspace; size_t workspace_bytes;
   int cache_fp8;                 // caches hold E4M3FN codes; value = code * scale
   float k_scale, v_scale;
+  unsigned* err;                 // the GPU's device error word (may be null)
 };
 
 // decode plan: which kernel runs and how much workspace it needs

@@ -90,6 +90,7 @@ struct PrefillKArgs {
   int num_seqs, num_qtiles, pairs_per_xcd;        // pairs_per_xcd 0: plain order
   float scale_log2;                               // scale * log2 e (* k_scale for an FP8 cache)
   float out_scale;                                // 1, or v_scale for an FP8 cache
+  unsigned* err;                                  // the device error word (may be null)
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -217,10 +218,18 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   asm volatile("" ::"s"(ctx), "s"(r0), "s"(r1));  // all three loaded here (none sunk past the exit)
   const int n = r1 - r0;
   const int q0 = qt * kBQ;
-  if (q0 >= n) return;
-  bool bad = ctx < n || ctx > a.max_context_len || r0 < 0 || r0 + n > a.num_tokens;
+  if (q0 >= n) {
+    if (n < 0 && qt == 0 && tid == 0) report_error(a.err, kErrSequence);
+    return;
+  }
+  // rows outside the packed batch, or more rows than any valid context
+  // holds (the block-id staging is sized for max_context_len keys): flag,
+  // write nothing
+  const bool rows_bad = r0 < 0 || r0 + n > a.num_tokens || n > a.max_context_len;
+  bool bad = rows_bad || ctx < n || ctx > a.max_context_len;
+  if (bad && tid == 0) report_error(a.err, kErrSequence);
+  if (rows_bad) return;
   if (bad) ctx = n;                               // keep every index in range; output is NaN
-  if (r0 < 0 || r0 + n > a.num_tokens) return;    // rows not ours to write
   const int pos0 = ctx - n;                       // position of row 0
   const int qlast = min(q0 + kBQ, n) - 1;         // last valid row of the tile
   const int nkt = (pos0 + qlast) / kBK + 1;       // 32-key tiles up to the causal limit
@@ -620,7 +629,10 @@ __global__ __launch_bounds__(KG * WPG * 64) void prefill_mfma_kernel(PrefillKArg
   }
 
   __syncthreads();
-  if (sbad) bad = true;
+  if (sbad) {
+    bad = true;
+    if (tid == 0) report_error(a.err, kErrBlock);
+  }
   uint8_t* mg = hw == 0 ? st0 : hw == 1 ? st1 : hw == 2 ? st2 : st3;
   if constexpr (KG == 2) {
   // ---- merge the key groups through LDS (the ring is free now) ----
@@ -797,6 +809,7 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   k.pairs_per_xcd = np >= 8 && (KG == 1 || np == 8) ? (np + 7) / 8 : 0;
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
+  k.err = a.err;
   const int bs = a.block_size == 4 * kB ? 2 : a.block_size == 2 * kB ? 1 : 0;
   const bool f8 = a.cache_fp8 != 0;
   const size_t ids_bytes = static_cast<size_t>(ids) * 4;

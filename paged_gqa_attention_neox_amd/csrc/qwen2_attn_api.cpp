@@ -1,6 +1,7 @@
 // C ABI of libqwen2attn.so: argument validation, status codes, dispatch to
 // the kernel launchers.  Declared (and documented) in include/qwen2_attn.h.
-// No allocation, no retained state except the thread-local error message.
+// No allocation; retained state: the thread-local error message, and per GPU
+// the device error word and the no-alloc decode's static scratch.
 #include "../../include/qwen2_attn.h"
 
 #include <hip/hip_runtime.h>
@@ -29,6 +30,35 @@ int fail(int status, const char* fmt, ...) {
 
 int ok() {
   g_err[0] = '\0';
+  return QW_OK;
+}
+
+// Device error word, one per GPU (zero when the library loads): the kernels
+// OR QW_DEVICE_ERR_* flags into it when they meet metadata outside its
+// contract.  In host code the name is only a stand-in for the symbol; the
+// kernels get the address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ unsigned int device_errors;
+
+constexpr int kMaxDevs = 64;
+std::mutex g_errword_mu;
+unsigned* g_errword_ptr[kMaxDevs] = {};
+
+int current_error_word(unsigned** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QW_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevs) return fail(QW_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevs);
+  std::lock_guard<std::mutex> lock(g_errword_mu);
+  if (!g_errword_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(device_errors));
+    if (e != hipSuccess || !p)
+      return fail(QW_ERR_HIP, "hipGetSymbolAddress(device_errors) on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+    g_errword_ptr[dev] = static_cast<unsigned*>(p);
+  }
+  *ptr = g_errword_ptr[dev];
   return QW_OK;
 }
 
@@ -88,6 +118,22 @@ const char* qwen2_status_string(int status) {
 }
 
 const char* qwen2_last_error(void) { return g_err; }
+
+int qwen2_device_errors(unsigned int* flags, int clear) {
+  if (!flags) return fail(QW_ERR_NULL, "flags is NULL");
+  unsigned* word = nullptr;
+  const int st = current_error_word(&word);
+  if (st) return st;
+  hipError_t e = hipMemcpy(flags, word, sizeof(unsigned), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(QW_ERR_HIP, "reading the device error word failed: %s", hipGetErrorString(e));
+  if (clear) {
+    e = hipMemset(word, 0, sizeof(unsigned));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+      return fail(QW_ERR_HIP, "clearing the device error word failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
 
 int qwen2_rope_table_init(double* cos_sin, int max_position, int rotary_dim, double rope_theta,
                           hipStream_t stream) {
@@ -185,6 +231,7 @@ static int rope_write_impl(const void* q, int64_t q_row_stride, void* q_out, int
   a.head_dim = head_dim; a.block_size = block_size; a.dtype = dtype;
   a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
   a.q_norm_w = q_norm_w; a.k_norm_w = k_norm_w; a.rms_eps = rms_eps;
+  if ((st = current_error_word(&a.err))) return st;
   return launched(qw::launch_rope_cache_write(a, stream));
 }
 
@@ -307,6 +354,7 @@ static int prefill_impl(const void* q, int64_t q_row_stride, const void* k_cache
   a.num_heads = num_heads; a.num_kv_heads = num_kv_heads; a.head_dim = head_dim;
   a.block_size = block_size; a.scale = scale; a.dtype = dtype;
   a.cache_fp8 = cache_fp8; a.k_scale = k_scale; a.v_scale = v_scale;
+  if ((st = current_error_word(&a.err))) return st;
   return launched(qw::launch_prefill(a, stream));
 }
 
@@ -419,11 +467,13 @@ static int decode_impl(const void* q, int64_t q_row_stride, const void* k_cache,
       return fail(QW_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
     if (!aligned16(workspace)) return fail(QW_ERR_ALIGN, "workspace is not 16-byte aligned");
   }
-  const qw::AttnArgs a = decode_args(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
-                                     max_blocks_per_seq, context_lens, out, out_row_stride,
-                                     workspace, workspace_bytes, num_seqs, max_context_len,
-                                     num_heads, num_kv_heads, head_dim, block_size, scale, dtype,
-                                     cache_fp8, k_scale, v_scale);
+  qw::AttnArgs a = decode_args(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, context_lens, out, out_row_stride, workspace,
+                               workspace_bytes, num_seqs, max_context_len, num_heads,
+                               num_kv_heads, head_dim, block_size, scale, dtype, cache_fp8,
+                               k_scale, v_scale);
+  const int est = current_error_word(&a.err);
+  if (est) return est;
   return launched(qw::launch_decode(a, plan, stream));
 }
 
@@ -587,11 +637,13 @@ static int cascade_impl(const void* q, int64_t q_row_stride, const void* k_cache
       return fail(QW_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, plan.ws_bytes);
     if (!aligned16(workspace)) return fail(QW_ERR_ALIGN, "workspace is not 16-byte aligned");
   }
-  const qw::AttnArgs a = decode_args(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
-                                     max_blocks_per_seq, context_lens, out, out_row_stride,
-                                     workspace, workspace_bytes, num_seqs, max_context_len,
-                                     num_heads, num_kv_heads, head_dim, block_size, scale, dtype,
-                                     cache_fp8, k_scale, v_scale);
+  qw::AttnArgs a = decode_args(q, q_row_stride, k_cache, v_cache, num_blocks, block_tables,
+                               max_blocks_per_seq, context_lens, out, out_row_stride, workspace,
+                               workspace_bytes, num_seqs, max_context_len, num_heads,
+                               num_kv_heads, head_dim, block_size, scale, dtype, cache_fp8,
+                               k_scale, v_scale);
+  const int est = current_error_word(&a.err);
+  if (est) return est;
   qw::CascadeMeta m{};
   m.indptr = prefix_indptr;
   m.seqs = prefix_seqs;

@@ -272,6 +272,8 @@ __global__ __launch_bounds__(256) void rope_cache_write_kernel(RopeWriteArgs a) 
       const int slot = a.slots[t];
       const bool pos_ok = static_cast<unsigned>(pos) < static_cast<unsigned>(a.max_position);
       const bool slot_ok = slot >= 0 && static_cast<int64_t>(slot) < cache_slots;
+      if (!pos_ok) report_error(a.err, kErrPosition);
+      if (!slot_ok && slot != -1) report_error(a.err, kErrSlot);
       const int64_t blk = slot_ok ? slot >> lb : 0;
       const int off = slot_ok ? slot & (B - 1) : 0;
       double cv[8], sv[8];
