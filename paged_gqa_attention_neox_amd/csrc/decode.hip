@@ -12,15 +12,20 @@
 // exactly once and used for all G heads.
 //
 // Work decomposition.  The work units are the (sequence, KV head, block)
-// triples in that order, cut into contiguous ranges by a fixed schedule of
-// shrinking sizes: 75% of the units in kCUs ranges, 15% in kCUs, 10% in
-// 2 kCUs.  One persistent 4-wave workgroup per CU (its LDS reservation
-// admits no second one) takes range i = its index first and then claims
-// ranges in order from a device-wide counter, so CUs and XCDs that stream
-// faster (measured: up to ~20% apart) take more of the small ranges at the
-// end and all finish together.  (A first claim by every workgroup at once
-// queued ~2.5 us of atomics on the counter before any tile load.)  Which ranges a
-// workgroup gets varies; what is computed for each range does not.
+// triples in that order, cut into contiguous ranges.  Persistent 4-wave
+// workgroups, two per CU (a wave per SIMD each: while one starts a piece,
+// waiting for its first tiles, the other streams), take range i = their
+// index first and then claim ranges in order from a device-wide counter.
+// The plain decode cuts the units into equal ranges of at least
+// kOneTierMin units, two per CU (one per CU for bf16 batches of
+// kBf16WideUnits units or more, where the pieces and merges that more
+// ranges cut cost more than the overlap wins).  The cascade's private level
+// keeps a schedule of shrinking sizes (75% of the units in kCUs ranges, 15%
+// in kCUs, 10% in 2 kCUs; one tier from kOneTierUnits), so that CUs and
+// XCDs that stream faster (measured: up to ~20% apart) take more of the
+// small ranges at the end.  (A first claim by every workgroup at once
+// queued ~2.5 us of atomics on the counter before any tile load.)  Which
+// ranges a workgroup gets varies; what is computed for each range does not.
 // A range covers whole (sequence, KV head) segments, which its workgroup
 // finishes itself, and at most two pieces of segments that other ranges
 // share: those partial softmax states go to the workspace and decode_merge
@@ -47,6 +52,7 @@
 //     every load instruction reads 512 contiguous bytes.
 // Results depend only on the logical sizes (never on the physical block
 // placement) and are bitwise reproducible.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -65,15 +71,16 @@ constexpr int kNW = 4;                  // waves per workgroup, one per SIMD
 constexpr int kThreads = kNW * 64;
 constexpr int kCUs = 256;               // workgroups per round of the schedule
 constexpr int kTiers = 3;
-// the schedule: tier t takes units [U pct[t] / 100, U pct[t + 1] / 100) in
-// equal ranges of at least kTierMin[t] units, at most kTierWgs[t] of them
-// (the host sizes the workspace for the bound it knows; the kernels count
-// the ranges for the actual U).  Batches of at least kOneTierUnits units
-// (128 blocks per CU) take one tier: equal ranges, one per workgroup, the
-// two later tiers empty.  There the shrinking tiers cost more in pieces and
-// merges than their balancing wins (measured: the long decode 295 -> 284 us,
-// the mixed step's 96 decodes 91 -> 86 us); smaller batches keep them (a
-// cascade's 64 short suffixes: 99 against 122 us with one tier).
+// The cascade's schedule: tier t takes units [U pct[t] / 100, U pct[t + 1] /
+// 100) in equal ranges of at least kTierMin[t] units, at most kTierWgs[t] of
+// them (the host sizes the workspace for the bound it knows; the kernels
+// count the ranges for the actual U).  Batches of at least kOneTierUnits
+// units (128 blocks per CU) take one tier: equal ranges, one per CU, the two
+// later tiers empty.  There the shrinking tiers cost more in pieces and
+// merges than their balancing wins (measured on the plain decode: the long
+// decode 295 -> 284 us, the mixed step's 96 decodes 91 -> 86 us); smaller
+// batches keep them (a cascade's 64 short suffixes: 99 against 122 us with
+// one tier).
 __constant__ int kTierPct[kTiers + 1] = {0, 75, 90, 100};
 __constant__ int kOneTierPct[kTiers + 1] = {0, 100, 100, 100};
 constexpr int kTierPctHost[kTiers + 1] = {0, 75, 90, 100};
@@ -81,10 +88,18 @@ constexpr int64_t kOneTierUnits = 128 * 256;
 constexpr int kTierWgs[kTiers] = {kCUs, kCUs, 2 * kCUs};
 __constant__ int kTierMin[kTiers] = {64, 32, 24};
 constexpr int kTierMinHost[kTiers] = {64, 32, 24};
+// The plain decode's schedule (above): equal ranges of at least
+// kOneTierMin units, at most kPlainRanges of them (kCUs for a bf16 batch of
+// kBf16WideUnits units or more).  Measured per call against one range per
+// CU: the Qwen3-0.6B-shaped decode (17K units) 42.2 -> 40.9 us, the mixed
+// step's decodes (47K) 81.2 -> 79.2, the FP8 long decode (215K) 170.2 ->
+// 167.9; the bf16 long decode (215K) 278.2 against 282.0 with two per CU.
+constexpr int kOneTierMin = 32;
+constexpr int kPlainRanges = 2 * kCUs;
+constexpr int64_t kBf16WideUnits = 256 * kCUs;
 constexpr int kClaimAhead = 6;          // blocks of wave 0 left when the next range is claimed
-// LDS per workgroup: the merge buffer, sized so that a CU holds one
-// workgroup (four waves, one per SIMD)
-constexpr int kLdsFloats = 21504;       // 84 KiB
+// LDS per workgroup: the merge buffer (16 KiB; two workgroups share a CU)
+constexpr int kLdsFloats = kNW * kMaxG * kD;
 static_assert(kLdsFloats >= kNW * kMaxG * kD, "merge buffer");
 constexpr size_t kWsHeader = 256;       // counters; then the range descriptors, the merge jobs, the partial states
 constexpr int kRangeEmpty = 2, kRangeFirst = 1;   // descriptor flags
@@ -164,8 +179,8 @@ struct DecodeKArgs {
   float* ws_acc;   // [2 R][G][128]: partial outputs (range r: slots 2r, 2r + 1)
   float* ws_ml;    // [2 R][G][2]:   reference max (log2 domain) and sum
   int num_heads, num_kv_heads, max_context_len;
-  int tier_wgs[kTiers];   // most ranges per tier (for the host's bound on U); R = their sum
-  int num_ranges;
+  int tier_wgs[kTiers];   // most ranges per tier of the cascade's schedule (host bound on U)
+  int num_ranges;         // ranges the workspace holds (every schedule's R is at most this)
   int* claim;             // [0] range counter, [2] merge-job count: zero at launch
   int4* desc;             // per range: merge source range (-1: none), flags, segment (s, g)
   int* jobs;              // ranges whose first piece ends a shared segment (count in claim[2])
@@ -258,9 +273,21 @@ struct Schedule {
   int pct[kTiers + 1];
   int R;
 };
+template <bool CAS, bool F8>
 __device__ Schedule schedule_for(const DecodeKArgs& a, int64_t U) {
   Schedule sc;
   sc.R = 0;
+  if constexpr (!CAS) {
+    // one tier of equal ranges; tiers 1 and 2 hold one empty range each,
+    // and the host's bound a.num_ranges covers every R this gives
+    for (int t = 0; t <= kTiers; ++t) sc.pct[t] = kOneTierPct[t];
+    const int cap = min(!F8 && U >= kBf16WideUnits ? kCUs : kPlainRanges, a.num_ranges - (kTiers - 1));
+    const int64_t n = (U + kOneTierMin - 1) / kOneTierMin;
+    sc.n[0] = static_cast<int>(n < 1 ? 1 : (n > cap ? cap : n));
+    for (int t = 1; t < kTiers; ++t) sc.n[t] = 1;
+    for (int t = 0; t < kTiers; ++t) sc.R += sc.n[t];
+    return sc;
+  }
   const int* pct = U >= kOneTierUnits ? kOneTierPct : kTierPct;
   for (int t = 0; t <= kTiers; ++t) sc.pct[t] = pct[t];
   for (int t = 0; t < kTiers; ++t) {
@@ -343,7 +370,7 @@ __device__ __forceinline__ void fold_prefix(const DecodeKArgs& a, int s, int qh,
 // whose K rows are contiguous and whose V rows are 16-key runs of the
 // longer dims rows of the [d][16 << BS] tile.
 template <int G, bool F8, bool CAS, int BS>
-__global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeKArgs a) {
   constexpr int kEl = F8 ? 1 : 2;                 // bytes per cache element
   constexpr int kTileBytes = kBlk * kD * kEl;     // one 16-token (sub-)tile of K or V
   constexpr int kBS = kBlk << BS;                 // tokens per cache block
@@ -353,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void decode_stream_kernel(DecodeKArgs a) 
   const int wave = uniform(tid >> 6);
   const int Hkv = a.num_kv_heads;
   const int64_t U = total_units<CAS>(a, lane);
-  const Schedule sched = schedule_for(a, U);
+  const Schedule sched = schedule_for<CAS, F8>(a, U);
 
   // per-wave softmax states of a piece, merged at its end
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
@@ -1066,6 +1093,19 @@ static void decode_schedule(int num_seqs, int max_context_len, int num_kv_heads,
   }
 }
 
+// The ranges the workspace holds: the cascade's three-tier bound (wgs) or
+// the plain decode's one-tier bound, whichever is larger.
+static int decode_num_ranges(int num_seqs, int max_context_len, int num_kv_heads, int (&wgs)[kTiers]) {
+  decode_schedule(num_seqs, max_context_len, num_kv_heads, wgs);
+  int tiers = 0;
+  for (int t = 0; t < kTiers; ++t) tiers += wgs[t];
+  const int64_t umax = static_cast<int64_t>(num_kv_heads) * num_seqs *
+                       ((static_cast<int64_t>(max_context_len) + kBlk - 1) / kBlk);
+  const int64_t n = std::min<int64_t>(kPlainRanges, (umax + kOneTierMin - 1) / kOneTierMin);
+  const int one = static_cast<int>(n < 1 ? 1 : n) + (kTiers - 1);
+  return std::max(tiers, one);
+}
+
 DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num_kv_heads,
                        int head_dim, int block_size, int dtype, int cache_fp8) {
   (void)cache_fp8;                    // both cache formats have the stream kernel
@@ -1076,9 +1116,7 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
            G <= kMaxG;
   if (!p.fast) return p;
   int wgs[kTiers];
-  decode_schedule(num_seqs, max_context_len, num_kv_heads, wgs);
-  p.num_ranges = 0;
-  for (int t = 0; t < kTiers; ++t) p.num_ranges += wgs[t];
+  p.num_ranges = decode_num_ranges(num_seqs, max_context_len, num_kv_heads, wgs);
   p.ws_bytes = kWsHeader + desc_bytes(p.num_ranges) + jobs_bytes(p.num_ranges) +
                static_cast<size_t>(2) * p.num_ranges * G * (kD + 2) * sizeof(float);
   return p;
@@ -1099,7 +1137,8 @@ static void launch_stream_bs(const DecodeKArgs& k, const AttnArgs& a, int grid, 
 
 template <int G>
 static void launch_stream(const DecodeKArgs& k, const AttnArgs& a, hipStream_t stream) {
-  const int grid = k.num_ranges < kCUs ? k.num_ranges : kCUs;
+  // up to two workgroups per CU; those past the batch's R leave at once
+  const int grid = k.num_ranges < kPlainRanges ? k.num_ranges : kPlainRanges;
   hipLaunchKernelGGL(decode_claim_reset_kernel, dim3(1), dim3(64), 0, stream, k.claim);
   switch (block_shift(a.block_size)) {
     case 0: launch_stream_bs<G, 0>(k, a, grid, stream); break;
@@ -1126,9 +1165,7 @@ static DecodeKArgs make_kargs(const AttnArgs& a) {
   k.num_heads = a.num_heads;
   k.num_kv_heads = a.num_kv_heads;
   k.max_context_len = a.max_context_len;
-  decode_schedule(a.num_seqs, a.max_context_len, a.num_kv_heads, k.tier_wgs);
-  k.num_ranges = 0;
-  for (int t = 0; t < kTiers; ++t) k.num_ranges += k.tier_wgs[t];
+  k.num_ranges = decode_num_ranges(a.num_seqs, a.max_context_len, a.num_kv_heads, k.tier_wgs);
   k.scale_log2 = a.scale * kLog2e * (a.cache_fp8 ? a.k_scale : 1.0f);
   k.out_scale = a.cache_fp8 ? a.v_scale : 1.0f;
   k.err = a.err;

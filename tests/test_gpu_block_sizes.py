@@ -35,8 +35,8 @@ CASES = [
     ("decode_g2_b32", 32, "bf16", 16, 8, 128, [129, 2048, 1, 700], [1] * 4, 0, {}),
     ("decode_g8_b64", 64, "bf16", 32, 4, 128, [777, 1500], [1] * 2, 0, {}),
     ("decode_g1_b32", 32, "bf16", 4, 4, 128, [300, 700, 3], [1] * 3, 0, {}),
-    # 32768 (sequence, KV head, 16-token block) units: the one-tier schedule
-    ("decode_one_tier_b32", 32, "bf16", 28, 4, 128, [16384] * 8, [1] * 8, 0, {}),
+    # 65536 (sequence, KV head, 16-token block) units: one range per CU
+    ("decode_256_ranges_b32", 32, "bf16", 28, 4, 128, [16384] * 16, [1] * 16, 0, {}),
     ("decode_fp8_b32", 32, "bf16", 28, 4, 128, _EDGES, [1] * len(_EDGES), 0, _FP8),
     ("decode_fp8_b64", 64, "bf16", 28, 4, 128, [5000, 65, 64, 1], [1] * 4, 0, _FP8),
     ("prefill_ragged_b32", 32, "bf16", 28, 4, 128, [1, 17, 64, 65, 130, 200],

@@ -81,6 +81,12 @@ CASES = [
     ("g7_long_prefix_chunks", 28, 4, [9000, 8500, 12000], [([0, 1, 2], 8192)], False),
     ("fp8_g7", 28, 4, [300, 1100, 513, 2000, 47], [([1, 3], 256), ([2, 4], 32)], True),
     ("fp8_g8_suffix_in_one_block", 32, 4, [1025, 1030, 1040], [([0, 1, 2], 1024)], True),
+    # the private level's schedule switches at 32768 units of suffix blocks:
+    # exactly 32768 takes one tier of equal ranges, one unit less the three
+    # shrinking tiers
+    ("g7_one_tier_at_threshold", 28, 4, [17408] * 8, [(list(range(8)), 1024)], False),
+    ("g7_three_tiers_below_threshold", 28, 4, [17408] * 7 + [17392], [(list(range(8)), 1024)],
+     False),
 ]
 
 

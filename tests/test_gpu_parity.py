@@ -108,11 +108,14 @@ SMALL = [
      [1] * 1000, 0),
     # 160 tiny prefill sequences (1..40 tokens): 640 (sequence, KV head) pairs
     ("prefill_160_tiny", "bf16", 28, 4, 128, list(range(1, 41)) * 4, list(range(1, 41)) * 4, 160),
-    # the decode schedule's switch at 32768 units ((sequence, KV head, block)
-    # triples): exactly 32768 takes one tier of equal ranges, one unit less
-    # the three shrinking tiers
-    ("decode_one_tier_at_threshold", "bf16", 28, 4, 128, [16384] * 8, [1] * 8, 0),
-    ("decode_three_tiers_below_threshold", "bf16", 28, 4, 128, [16384] * 7 + [16368], [1] * 8, 0),
+    # the plain decode's range count for bf16 switches at 65536 units
+    # ((sequence, KV head, block) triples): exactly 65536 takes one range per
+    # CU, one unit less two per CU (512 ranges, the cap)
+    ("decode_256_ranges_at_threshold", "bf16", 28, 4, 128, [16384] * 16, [1] * 16, 0),
+    ("decode_512_ranges_below_threshold", "bf16", 28, 4, 128, [16384] * 15 + [16368], [1] * 16,
+     0),
+    # 32768 units: 512 ranges of 64 units
+    ("decode_32k_units", "bf16", 28, 4, 128, [16384] * 8, [1] * 8, 0),
 ]
 
 
