@@ -498,9 +498,14 @@ def qwen2_long_decode(seed: int = 4, num_seqs: int = 64, keep_logical: bool = Fa
 
 # FP8 cache scales of the FP8 workloads: with N(0,1) values the codes use
 # the upper part of the E4M3FN range (|x| / scale up to ~180 < 448) and stay
-# clear of its subnormals; deliberately not powers of two.
-FP8_K_SCALE = 0.0312
-FP8_V_SCALE = 0.0287
+# clear of its subnormals; deliberately not powers of two.  A cache scale is
+# a float32 (the library's argument type), so these are the float32 values
+# nearest 0.0312 and 0.0287: the oracle then divides by exactly the number
+# the kernels receive (with the float64 0.0312 the two quotients differ by
+# ~3e-8 relative, enough to move an occasional code across a rounding
+# boundary).
+FP8_K_SCALE = float(np.float32(0.0312))
+FP8_V_SCALE = float(np.float32(0.0287))
 
 
 def qwen2_long_decode_fp8(seed: int = 4, num_seqs: int = 64, keep_logical: bool = False) -> Batch:
