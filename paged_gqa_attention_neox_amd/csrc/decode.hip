@@ -840,7 +840,7 @@ __device__ void cascade_prep(const DecodeKArgs& a, const CascadeArgs& ca) {
 }
 
 template <int G, bool F8, int BS>
-__global__ __launch_bounds__(kThreads) void decode_prefix_kernel(DecodeKArgs a, CascadeArgs ca) {
+__global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(DecodeKArgs a, CascadeArgs ca) {
   if (blockIdx.x == 0) {
     cascade_prep<BS>(a, ca);
     return;
