@@ -90,10 +90,11 @@ __constant__ int kTierMin[kTiers] = {64, 32, 24};
 constexpr int kTierMinHost[kTiers] = {64, 32, 24};
 // The plain decode's schedule (above): equal ranges of at least
 // kOneTierMin units, at most kPlainRanges of them (kCUs for a bf16 batch of
-// kBf16WideUnits units or more).  Measured per call against one range per
-// CU: the Qwen3-0.6B-shaped decode (17K units) 42.2 -> 40.9 us, the mixed
-// step's decodes (47K) 81.2 -> 79.2, the FP8 long decode (215K) 170.2 ->
-// 167.9; the bf16 long decode (215K) 278.2 against 282.0 with two per CU.
+// kBf16WideUnits units or more).  Measured per call, two workgroups per CU
+// in both, against the cascade's schedule: the Qwen3-0.6B-shaped decode
+// (17K units) 42.2 -> 38.1 us, the mixed step's decodes (47K) 81.2 -> 78.2,
+// the FP8 long decode (215K) 170.2 -> 166.6; the bf16 long decode (215K)
+// 277.0 us with 256 ranges against 282.0 with 512.
 constexpr int kOneTierMin = 32;
 constexpr int kPlainRanges = 2 * kCUs;
 constexpr int64_t kBf16WideUnits = 256 * kCUs;
