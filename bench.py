@@ -6,7 +6,7 @@ Headline workload: Qwen2-7B-shaped long-context paged decode, bf16 (28 query
 heads, 4 KV heads, head_dim 128, block 16, batch 64, contexts log-uniform in
 [2048, 32768]).  One step = qwen2_rope_cache_write of the 64 new tokens (rotate
 q/k, write k/v into the paged cache) + qwen2_attn_decode_paged (counter
-reset + stream kernel + merge kernel).  ``value`` is KV bytes read per step divided
+reset + stream kernel, which also merges shared segments).  ``value`` is KV bytes read per step divided
 by the step time (GB/s), inputs resident in HBM.  The K timed steps are
 captured in one HIP graph and replayed once between HIP events on the
 launching stream, so the figures are GPU time without the Python call cost;
@@ -582,7 +582,7 @@ def main():
         "tokens_per_s": round(b.num_seqs / (dec["step_ms"] * 1e-3), 1),
         "wall_ms_per_step": round(dec["wall_ms"], 4),
         "roofline": {
-            "kernel": "qwen2_attn_decode_paged (counter reset + stream + merge)",
+            "kernel": "qwen2_attn_decode_paged (counter reset + stream kernel with its merges)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

@@ -210,10 +210,13 @@ size_t qwen2_attn_decode_workspace_size(int num_seqs, int max_context_len, int n
  * (out_row_stride) is written.  The batch's (sequence, KV head, block)
  * units are spread evenly over the GPU: a sequence may be cut into pieces
  * whose partial softmax states are merged exactly (log-sum-exp, in a fixed
- * order, so results are bitwise reproducible) by a second kernel; workspace
+ * order, so results are bitwise reproducible) by the workgroup that
+ * finishes a sequence's last piece, inside the same kernel; workspace
  * (device, 16-byte aligned, workspace_bytes >=
- * qwen2_attn_decode_workspace_size(...)) holds a work counter and those
- * partial states and is scratch: its contents on entry do not matter.
+ * qwen2_attn_decode_workspace_size(...)) holds a work counter, per-range
+ * arrival counters and those partial states and is scratch: its contents
+ * on entry do not matter (a small launch before the kernel zeroes the
+ * counters).
  * Calls that share one workspace must not overlap.
  * "vLLM 部署 Qwen", §2.1 and §4.1 (paged KV access dominates decode).
  */

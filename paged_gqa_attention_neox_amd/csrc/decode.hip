@@ -28,9 +28,11 @@
 // ranges a workgroup gets varies; what is computed for each range does not.
 // A range covers whole (sequence, KV head) segments, which its workgroup
 // finishes itself, and at most two pieces of segments that other ranges
-// share: those partial softmax states go to the workspace and decode_merge
-// combines them exactly:
+// share: those partial softmax states go to the workspace, and the range
+// that completes a shared segment (the last to add its units to the
+// segment's arrival counter) combines them exactly, in range order:
 //   M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
+// (no separate merge launch: measured, it cost 7-10 us per call).
 // Partial states are the only HBM writes besides the output, and while the
 // reads saturate HBM every written byte costs several read bytes, so the
 // schedule keeps them to about one per range.
@@ -102,8 +104,7 @@ constexpr int kClaimAhead = 6;          // blocks of wave 0 left when the next r
 // LDS per workgroup: the merge buffer (16 KiB; two workgroups share a CU)
 constexpr int kLdsFloats = kNW * kMaxG * kD;
 static_assert(kLdsFloats >= kNW * kMaxG * kD, "merge buffer");
-constexpr size_t kWsHeader = 256;       // counters; then the range descriptors, the merge jobs, the partial states
-constexpr int kRangeEmpty = 2, kRangeFirst = 1;   // descriptor flags
+constexpr size_t kWsHeader = 256;       // the range counter; then the arrival counters, the partial states
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;           // log2-domain slack before the softmax reference moves
 
@@ -182,9 +183,9 @@ struct DecodeKArgs {
   int num_heads, num_kv_heads, max_context_len;
   int tier_wgs[kTiers];   // most ranges per tier of the cascade's schedule (host bound on U)
   int num_ranges;         // ranges the workspace holds (every schedule's R is at most this)
-  int* claim;             // [0] range counter, [2] merge-job count: zero at launch
-  int4* desc;             // per range: merge source range (-1: none), flags, segment (s, g)
-  int* jobs;              // ranges whose first piece ends a shared segment (count in claim[2])
+  int* claim;             // [0] range counter: zero at launch
+  int* arrive;            // [num_ranges] per range r: units arrived of the shared segment
+                          // whose last unit is in r: zero at launch
   float scale_log2;   // scale * log2 e (* k_scale with an FP8 cache)
   float out_scale;    // 1, or v_scale with an FP8 cache
   // shared-prefix cascade (unused by the plain decode)
@@ -302,6 +303,7 @@ __device__ Schedule schedule_for(const DecodeKArgs& a, int64_t U) {
 // First unit of range r (r = R gives U).
 __device__ int64_t range_begin(const Schedule& sc, int64_t r, int64_t U) {
   int64_t first = 0;
+#pragma unroll
   for (int t = 0; t < kTiers; ++t) {
     const int n = sc.n[t];
     const int64_t b0 = U * sc.pct[t] / 100, b1 = U * sc.pct[t + 1] / 100;
@@ -314,6 +316,7 @@ __device__ int64_t range_begin(const Schedule& sc, int64_t r, int64_t U) {
 // whose [begin, end) contains u).
 __device__ int64_t range_of(const Schedule& sc, int64_t u, int64_t U) {
   int64_t first = 0;
+#pragma unroll
   for (int t = 0; t < kTiers; ++t) {
     const int n = sc.n[t];
     const int64_t b0 = U * sc.pct[t] / 100, b1 = U * sc.pct[t + 1] / 100;
@@ -361,6 +364,145 @@ __device__ __forceinline__ void fold_prefix(const DecodeKArgs& a, int s, int qh,
   }
 }
 
+// fold_prefix for four consecutive dims e0 .. e0 + 3 of one state: the
+// chunks' (max, sum) are loaded once for the four, and each dim's arithmetic
+// is fold_prefix's
+__device__ __forceinline__ void fold_prefix4(const DecodeKArgs& a, int s, int qh, int e0, float& M,
+                                             float& L, float4& o) {
+  const int nc = a.cas[s].y;
+  const int64_t row = static_cast<int64_t>(s) * a.num_heads + qh;
+  const int64_t cstride = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+  for (int c0 = 0; c0 < nc; c0 += kFoldBatch) {
+    float pm[kFoldBatch], pl[kFoldBatch];
+    float4 pv[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const int64_t r = (c0 + i < nc ? c0 + i : c0) * cstride + row;
+      pm[i] = a.pre_ml[r * 2];
+      pl[i] = a.pre_ml[r * 2 + 1];
+      pv[i] = *reinterpret_cast<const float4*>(a.pre_acc + r * kD + e0);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i)
+      if (c0 + i < nc) Mn = fmaxf(Mn, pm[i]);
+    const float f = __builtin_amdgcn_exp2f(M - Mn);
+    L *= f;
+    o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+    M = Mn;
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      if (c0 + i < nc) {
+        const float wt = __builtin_amdgcn_exp2f(pm[i] - M);
+        L = fmaf(pl[i], wt, L);
+        o.x = fmaf(pv[i].x, wt, o.x);
+        o.y = fmaf(pv[i].y, wt, o.y);
+        o.z = fmaf(pv[i].z, wt, o.z);
+        o.w = fmaf(pv[i].w, wt, o.w);
+      }
+    }
+  }
+}
+
+// Device-coherent (agent scope) accesses to the partial states: they reach
+// or read the point where every XCD's accesses meet (gfx950's SC1 bit), so
+// a state one workgroup stores and waits for is what a workgroup on any XCD
+// loads after the arrival counter says it is there.
+constexpr int kCoherent = 16;           // buffer-load cache policy: SC1
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Range r holds units [range_begin(r), range_begin(r + 1)); a tier with at
+// least one unit has at least as many units as ranges, so only a tier
+// without units has an empty range (its only one).  Bit t: tier t has units.
+__device__ __forceinline__ unsigned live_tiers(const Schedule& sc, int64_t U) {
+  unsigned m = 0;
+#pragma unroll
+  for (int t = 0; t < kTiers; ++t)
+    if (U * sc.pct[t + 1] / 100 > U * sc.pct[t] / 100) m |= 1u << t;
+  return m;
+}
+
+// Merge of shared segment (s, g), units [seg0, seg0 + n), by the workgroup
+// whose range completed it.  Its pieces are the partial states of the
+// non-empty ranges ra..rb that hold its units: ra's piece is ra's first
+// (slot 2 ra) if ra begins with the segment, else ra's last (slot 2 ra + 1);
+// every later range's piece is its first (slot 2 r).  Thread (head h, dims
+// 4 e4 .. 4 e4 + 3) merges them in range order, kMergeBatch at a time with
+// every load of a batch in flight:
+//   M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
+// The result depends only on the logical sizes: bitwise reproducible.
+constexpr int kMergeBatch = 16;
+template <int G, bool CAS>
+__device__ __forceinline__ void merge_segment(const DecodeKArgs& a, const Schedule& sc, int64_t U,
+                                              int s, int g, int64_t seg0, int n, int tid) {
+  if (tid >= G * (kD / 4)) return;
+  const int h = tid / (kD / 4), e4 = tid % (kD / 4);
+  const int64_t ra = range_of(sc, seg0, U), rb = range_of(sc, seg0 + n - 1, U);
+  const bool ra_first = range_begin(sc, ra, U) == seg0;
+  const unsigned tiers = live_tiers(sc, U);
+  const int64_t n0 = sc.n[0], n01 = n0 + sc.n[1];
+  float M = -INFINITY, L = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const auto racc = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws_acc, static_cast<short>(0), 2 * a.num_ranges * G * kD * 4, kBufferFlags);
+  for (int64_t x0 = ra; x0 <= rb; x0 += kMergeBatch) {
+    float pm[kMergeBatch], pl[kMergeBatch];
+    float4 v[kMergeBatch];
+    bool live[kMergeBatch];
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      // loads only for pieces of the segment (x0 + q <= rb is uniform)
+      const int64_t x = x0 + q;
+      live[q] = x <= rb && (x == ra || ((tiers >> (x < n0 ? 0 : x < n01 ? 1 : 2)) & 1u));
+      if (live[q]) {
+        const int64_t sb = (2 * x + (x == ra && !ra_first ? 1 : 0)) * G + h;
+        pm[q] = load_coherent(&a.ws_ml[sb * 2]);
+        pl[q] = load_coherent(&a.ws_ml[sb * 2 + 1]);
+        v[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              racc, static_cast<int>((sb * (kD / 4) + e4) * 16), 0,
+                                              kCoherent));
+      } else {
+        pm[q] = pl[q] = 0.0f;
+        v[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q)
+      if (live[q]) Mc = fmaxf(Mc, pm[q]);
+    if (Mc > M) {                        // rescale the running sums (M = -inf: they are 0)
+      const float f = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+      L *= f;
+      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+      M = Mc;
+    }
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      if (live[q]) {
+        const float wt = __builtin_amdgcn_exp2f(pm[q] - M);
+        L = fmaf(pl[q], wt, L);
+        o.x = fmaf(v[q].x, wt, o.x);
+        o.y = fmaf(v[q].y, wt, o.y);
+        o.z = fmaf(v[q].z, wt, o.z);
+        o.w = fmaf(v[q].w, wt, o.w);
+      }
+    }
+  }
+  const int qh = g * G + h;
+  if constexpr (CAS) fold_prefix4(a, s, qh, 4 * e4, M, L, o);
+  const float os = a.out_scale;
+  uint2 w;
+  w.x = pack_bf16x2(o.x * os / L, o.y * os / L);
+  w.y = pack_bf16x2(o.z * os / L, o.w * os / L);
+  *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(s) * a.out_stride +
+                            static_cast<int64_t>(qh) * kD + 4 * e4) = w;
+}
+
 // F8: the caches hold E4M3FN codes (K tile 2 KiB, V tile 2 KiB); they are
 // widened to bf16 in registers and the same arithmetic follows.
 // CAS: a cascade's private level (each sequence's keys after its shared
@@ -388,7 +530,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeKArgs 
   float (*sacc)[kMaxG * kD] = reinterpret_cast<float (*)[kMaxG * kD]>(lds);
   __shared__ float sm[kNW][kMaxG], sl[kNW][kMaxG];
   __shared__ int sbad[kNW];
-  __shared__ int s_next;
+  __shared__ int s_next, s_merge;
 
   // MFMA lane roles: lane group j4, column (query head, or row of the A
   // operand) r16
@@ -410,29 +552,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeKArgs 
   while (rg < sched.R) {
   int next = 0;
   bool claimed = false;
-  // thread 0: whether this range's first piece ends a shared segment (a
-  // merge job), and the job's slot.  The slot's atomic goes out after the
-  // range's first tile loads and is stored when the range ends, so no wave
-  // waits for it (the first ranges all start at once).
-  bool job = false;
-  int jslot = -1;
   const int64_t u0 = range_begin(sched, rg, U), u1 = range_begin(sched, rg + 1, U);
-  if (u0 >= u1) {
-    if (tid == 0) a.desc[rg] = make_int4(-1, kRangeEmpty, 0, 0);
-  } else {
+  if (u0 < u1) {
   Cursor cur = locate<CAS>(a, u0, lane);
-  if (tid == 0) {
-    // the segment of this range's first piece: does this range end it after
-    // it began in an earlier range?  Then the merge combines ranges ra..rg.
-    int4 d = make_int4(-1, 0, cur.s, cur.g);
-    if (u0 > cur.seg0 && cur.seg0 + cur.n <= u1) {
-      const int64_t ra = range_of(sched, cur.seg0, U);
-      d.x = static_cast<int>(ra);
-      d.y = range_begin(sched, ra, U) == cur.seg0 ? kRangeFirst : 0;
-    }
-    a.desc[rg] = d;
-    job = d.x >= 0;
-  }
   int64_t u = u0;
   bool first_piece = true;
   while (true) {
@@ -582,10 +704,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeKArgs 
       VWord vb[kNBuf][8];
 #pragma unroll
       for (int j = 0; j < kNBuf - 1; ++j) issue(j, kb[j], vb[j]);
-      if (job) {
-        jslot = atomicAdd(a.claim + 2, 1);
-        job = false;
-      }
       for (int i = 0; i < nbw; i += kNBuf) {
 #pragma unroll
         for (int j = 0; j < kNBuf; ++j) {
@@ -644,12 +762,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeKArgs 
         a.out[static_cast<int64_t>(s) * a.out_stride + static_cast<int64_t>(qh) * kD + e] =
             f32_to_bf16(pbad ? __builtin_nanf("") : v * a.out_scale / L);
       } else {                           // a share of the segment: partial state
-        a.ws_acc[(slot * G + h) * kD + e] = v;
+        store_coherent(&a.ws_acc[(slot * G + h) * kD + e], v);
         if (e == 0) {
-          a.ws_ml[(slot * G + h) * 2] = M;
-          a.ws_ml[(slot * G + h) * 2 + 1] = pbad ? __builtin_nanf("") : L;
+          store_coherent(&a.ws_ml[(slot * G + h) * 2], M);
+          store_coherent(&a.ws_ml[(slot * G + h) * 2 + 1], pbad ? __builtin_nanf("") : L);
         }
       }
+    }
+    if (!whole) {
+      // a share of segment (s, g): once every thread's partial-state stores
+      // are complete, add its units to the arrival counter of the range
+      // that holds the segment's last unit; the range whose units complete
+      // the segment merges it.  The states are stored and read with
+      // device-coherent accesses (each XCD has its own L2); fences would
+      // write back and invalidate whole L2s (measured: the Qwen3-0.6B-shaped
+      // decode 38 -> 205 us).
+      const int64_t seg0 = u - b0;
+      const int64_t rb = range_of(sched, seg0 + n - 1, U);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tid == 0) s_merge = atomicAdd(a.arrive + rb, cnt) + cnt == n;
+      __syncthreads();
+      if (s_merge) merge_segment<G, CAS>(a, sched, U, s, g, seg0, n, tid);
     }
     u += cnt;
     if (u >= u1) break;
@@ -663,108 +797,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeKArgs 
     }
   }
   }
-  if (jslot >= 0) a.jobs[jslot] = rg;
   if (tid == 0) s_next = claimed ? next : gridDim.x + atomicAdd(a.claim, 1);
   __syncthreads();                       // s_next is written; the merge buffers are free
   rg = s_next;
   __syncthreads();                       // every thread has read s_next
-  }
-}
-
-// Merge of the shared segments.  Range r's descriptor names, when r's first
-// piece ends a segment that began in an earlier range r_a, that segment and
-// r_a.  Its pieces are the partial states of ranges r_a..r: r_a's piece is
-// in slot 2 r_a if the segment is r_a's first, else 2 r_a + 1; every later
-// non-empty range's piece is its first (slot 2 r'); empty ranges have none.
-//   M = max_r m_r,  L = sum_r l_r 2^(m_r - M),  o = sum_r a_r 2^(m_r - M) / L
-// One workgroup per job (a range whose first piece ends a shared segment),
-// G x 128 threads.  The merge is bound by memory latency: in the first phase
-// thread (quarter qr, head h, dims 4 e4 .. 4 e4 + 3) merges every fourth
-// piece (x = qr, qr + 4, ...), taking them kMergeBatch at a time with every
-// load of a batch (the ranges' empty flags, (m, l), 16 bytes of partial
-// output) in flight together, so a segment of up to 4 kMergeBatch pieces
-// costs one round of loads.  The four quarters' states meet in LDS and
-// thread (h, e) merges them in quarter order: the result depends only on the
-// logical sizes and is bitwise reproducible.
-constexpr int kMergeBatch = 16;
-template <int G, bool CAS>
-__global__ __launch_bounds__(G * kD) void decode_merge_kernel(DecodeKArgs a) {
-  __shared__ float4 q_o[4][G][kD / 4];
-  __shared__ float q_ml[4][G][2];
-  const int tid = threadIdx.x;
-  const int qr = tid / (G * (kD / 4)), qh = (tid / (kD / 4)) % G, e4 = tid % (kD / 4);
-  const int h = tid / kD, e = tid % kD;
-  const int njobs = a.claim[2];          // written by the stream kernel
-  for (int job = blockIdx.x; job < njobs; job += gridDim.x) {
-  const int r = a.jobs[job];
-  const int4 d = a.desc[r];
-  const int ra = d.x;
-  const bool ra_first = (d.y & kRangeFirst) != 0;
-  const int np = r - ra + 1;
-  float M = -INFINITY, L = 0.0f;
-  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int x0 = qr; x0 < np; x0 += 4 * kMergeBatch) {
-    float pm[kMergeBatch], pl[kMergeBatch];
-    float4 v[kMergeBatch];
-    bool live[kMergeBatch];
-#pragma unroll
-    for (int q = 0; q < kMergeBatch; ++q) {
-      const int x = x0 + 4 * q;
-      const int rx = ra + (x < np ? x : 0);
-      const int64_t sb = static_cast<int64_t>(2 * rx + (x == 0 && !ra_first ? 1 : 0)) * G + qh;
-      live[q] = x < np && (x == 0 || (a.desc[rx].y & kRangeEmpty) == 0);
-      pm[q] = a.ws_ml[sb * 2];
-      pl[q] = a.ws_ml[sb * 2 + 1];
-      v[q] = reinterpret_cast<const float4*>(a.ws_acc)[sb * (kD / 4) + e4];
-    }
-    float Mc = M;
-#pragma unroll
-    for (int q = 0; q < kMergeBatch; ++q)
-      if (live[q]) Mc = fmaxf(Mc, pm[q]);
-    if (Mc > M) {                        // rescale the running sums (M = -inf: they are 0)
-      const float f = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
-      L *= f;
-      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
-      M = Mc;
-    }
-#pragma unroll
-    for (int q = 0; q < kMergeBatch; ++q) {
-      if (live[q]) {
-        const float wt = __builtin_amdgcn_exp2f(pm[q] - M);
-        L = fmaf(pl[q], wt, L);
-        o.x = fmaf(v[q].x, wt, o.x);
-        o.y = fmaf(v[q].y, wt, o.y);
-        o.z = fmaf(v[q].z, wt, o.z);
-        o.w = fmaf(v[q].w, wt, o.w);
-      }
-    }
-  }
-  q_o[qr][qh][e4] = o;
-  if (e4 == 0) {
-    q_ml[qr][qh][0] = M;
-    q_ml[qr][qh][1] = L;
-  }
-  __syncthreads();
-  {
-    // quarters in order; quarter 0 holds piece 0, so Mf is finite
-    float Mf = q_ml[0][h][0];
-#pragma unroll
-    for (int k = 1; k < 4; ++k) Mf = fmaxf(Mf, q_ml[k][h][0]);
-    float Lf = 0.0f, of = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float mk = q_ml[k][h][0];
-      if (mk != -INFINITY) {
-        const float wt = __builtin_amdgcn_exp2f(mk - Mf);
-        Lf = fmaf(q_ml[k][h][1], wt, Lf);
-        of = fmaf(reinterpret_cast<const float*>(&q_o[k][h][0])[e], wt, of);
-      }
-    }
-    if constexpr (CAS) fold_prefix(a, d.z, d.w * G + h, e, Mf, Lf, of);
-    a.out[static_cast<int64_t>(d.z) * a.out_stride + static_cast<int64_t>(d.w * G + h) * kD + e] =
-        f32_to_bf16(of * a.out_scale / Lf);
-  }
-  __syncthreads();                       // the LDS states are read before the next job
   }
 }
 
@@ -818,10 +854,8 @@ __device__ __forceinline__ int group_prefix_blocks(const DecodeKArgs& a, const C
 template <int BS>
 __device__ void cascade_prep(const DecodeKArgs& a, const CascadeArgs& ca) {
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    a.claim[0] = 0;
-    a.claim[2] = 0;
-  }
+  if (tid == 0) a.claim[0] = 0;
+  for (int r = tid; r < a.num_ranges; r += kThreads) a.arrive[r] = 0;
   for (int s = tid; s < a.num_seqs; s += kThreads) a.cas[s] = make_int2(0, 0);
   __syncthreads();
   for (int i = tid; i < ca.num_members; i += kThreads) {
@@ -1072,16 +1106,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_prefix_kernel(DecodeKArgs 
   }
 }
 
-// zero the range counter
-__global__ void decode_claim_reset_kernel(int* claim) {
-  if (threadIdx.x == 0) {
-    claim[0] = 0;                        // range counter
-    claim[2] = 0;                        // merge jobs
-  }
+// zero the range counter and the arrival counters
+__global__ void decode_claim_reset_kernel(int* claim, int* arrive, int num_ranges) {
+  if (threadIdx.x == 0) claim[0] = 0;
+  for (int r = threadIdx.x; r < num_ranges; r += blockDim.x) arrive[r] = 0;
 }
 
-static size_t desc_bytes(int num_ranges) { return (static_cast<size_t>(num_ranges) * 16 + 255) / 256 * 256; }
-static size_t jobs_bytes(int num_ranges) { return (static_cast<size_t>(num_ranges) * 4 + 255) / 256 * 256; }
+static size_t arrive_bytes(int num_ranges) { return (static_cast<size_t>(num_ranges) * 4 + 255) / 256 * 256; }
 
 // ranges per tier for a batch of at most umax units
 static void decode_schedule(int num_seqs, int max_context_len, int num_kv_heads, int (&wgs)[kTiers]) {
@@ -1118,7 +1149,7 @@ DecodePlan plan_decode(int num_seqs, int max_context_len, int num_heads, int num
   if (!p.fast) return p;
   int wgs[kTiers];
   p.num_ranges = decode_num_ranges(num_seqs, max_context_len, num_kv_heads, wgs);
-  p.ws_bytes = kWsHeader + desc_bytes(p.num_ranges) + jobs_bytes(p.num_ranges) +
+  p.ws_bytes = kWsHeader + arrive_bytes(p.num_ranges) +
                static_cast<size_t>(2) * p.num_ranges * G * (kD + 2) * sizeof(float);
   return p;
 }
@@ -1140,13 +1171,13 @@ template <int G>
 static void launch_stream(const DecodeKArgs& k, const AttnArgs& a, hipStream_t stream) {
   // up to two workgroups per CU; those past the batch's R leave at once
   const int grid = k.num_ranges < kPlainRanges ? k.num_ranges : kPlainRanges;
-  hipLaunchKernelGGL(decode_claim_reset_kernel, dim3(1), dim3(64), 0, stream, k.claim);
+  hipLaunchKernelGGL(decode_claim_reset_kernel, dim3(1), dim3(256), 0, stream, k.claim, k.arrive,
+                     k.num_ranges);
   switch (block_shift(a.block_size)) {
     case 0: launch_stream_bs<G, 0>(k, a, grid, stream); break;
     case 1: launch_stream_bs<G, 1>(k, a, grid, stream); break;
     default: launch_stream_bs<G, 2>(k, a, grid, stream); break;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<G, false>), dim3(grid), dim3(G * kD), 0, stream, k);
 }
 
 static DecodeKArgs make_kargs(const AttnArgs& a) {
@@ -1172,10 +1203,8 @@ static DecodeKArgs make_kargs(const AttnArgs& a) {
   k.err = a.err;
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   k.claim = reinterpret_cast<int*>(ws);
-  k.desc = reinterpret_cast<int4*>(ws + kWsHeader);
-  k.jobs = reinterpret_cast<int*>(ws + kWsHeader + desc_bytes(k.num_ranges));
-  k.ws_acc = reinterpret_cast<float*>(ws + kWsHeader + desc_bytes(k.num_ranges) +
-                                      jobs_bytes(k.num_ranges));
+  k.arrive = reinterpret_cast<int*>(ws + kWsHeader);
+  k.ws_acc = reinterpret_cast<float*>(ws + kWsHeader + arrive_bytes(k.num_ranges));
   k.ws_ml = k.ws_acc + static_cast<size_t>(2) * k.num_ranges * G * kD;
   return k;
 }
@@ -1251,7 +1280,6 @@ static void launch_cascade_g(const DecodeKArgs& k, const CascadeArgs& ca, int64_
     case 1: launch_cascade_bs<G, 1>(k, ca, grid, pgrid, a, stream); break;
     default: launch_cascade_bs<G, 2>(k, ca, grid, pgrid, a, stream); break;
   }
-  hipLaunchKernelGGL((decode_merge_kernel<G, true>), dim3(grid), dim3(G * kD), 0, stream, k);
 }
 
 hipError_t launch_decode_cascade(const AttnArgs& a, const CascadeMeta& m, const CascadePlan& p,
