@@ -12,6 +12,9 @@ the oracle.
 import numpy as np
 import pytest
 
+import oracle.reference as R
+
+from paged_gqa_attention_neox_amd import runner
 from paged_gqa_attention_neox_amd import workloads as W
 from gpu_common import full_check, require_gpu, say
 from test_gpu_cascade import cascade_check
@@ -60,3 +63,30 @@ def test_cascade_long_suffixes(fp8):
                      **(FP8 if fp8 else {}))
     W.with_prefix_groups(b, [([0, 1, 2], 2048)])
     cascade_check(b, f"cascade_long_suffixes{'_fp8' if fp8 else ''}")
+
+
+@pytest.mark.parametrize("label", ["one_32k_sequence", "two_20k_sequences_g1", "cascade"])
+def test_long_segments_run_to_run_bitwise(label):
+    """Which workgroup completes (and so merges) a segment depends on timing;
+    the merge order does not: repeated calls give identical bits."""
+    if label == "cascade":
+        ctx = [2048 + 30000, 2048 + 25000, 2048 + 20000, 5000, 100]
+        b = W.small_case(1330, "bf16", 28, 4, 128, context_lens=ctx, query_lens=[1] * len(ctx),
+                         num_prefill=0, keep_logical=False)
+        W.with_prefix_groups(b, [([0, 1, 2], 2048)])
+        dev = runner.DeviceStep(b, cascade=True)
+    else:
+        H, Hkv, ctx, kw = CASES[label]
+        b = W.small_case(1331, "bf16", H, Hkv, 128, context_lens=ctx, query_lens=[1] * len(ctx),
+                         num_prefill=0, keep_logical=False, **kw)
+        dev = runner.DeviceStep(b)
+    dev.rope_write()
+    outs = []
+    for i in range(4):
+        say(f"{label}: decode call {i}")
+        dev.out.fill_(float("nan"))          # a segment left unmerged would stay NaN
+        dev.decode()
+        outs.append(runner.to_host(dev.out).copy())
+    assert not np.isnan(R.to_f64(outs[0], "bf16")).any()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
