@@ -98,17 +98,24 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
 }
 
 // The decode rows (one query row per sequence, no cu_seqlens): one
-// workgroup per (sequence, query head).  Its four waves take the keys round
-// robin; a wave's lanes hold D / 64 consecutive dims each, so a key's K row
-// is one coalesced load per lane and its score the wave's sum of q_e k_e.
-// Each wave keeps an online softmax state (m, l, acc); the four states are
-// merged through LDS at the end (o = sum_w acc_w e^(m_w - M) / sum_w l_w
-// e^(m_w - M)).  The per-thread kernel above walked a whole context in one
-// thread per head.
+// workgroup per (sequence, query head).  Its four waves take 16-key chunks
+// of the context round robin (a chunk lies in one cache block: block sizes
+// are multiples of 16); a lane holds D / 64 consecutive dims.  Per chunk a
+// wave issues every K and V load of its 16 keys at once, then:
+//   * partial dots q_e k_e per lane and key, summed over the wave by a
+//     butterfly that halves the keys a lane carries at each of the exchanges
+//     over lane bits 5..2 (8 + 4 + 2 + 1 shuffles) and then adds over bits 1
+//     and 0: lanes 4k .. 4k + 3 end with key k's score;
+//   * an online softmax update per chunk (keys past the context masked by
+//     selection), key k's p broadcast from lane 4k for the O += p V products
+//     over the lane's dims (a V row holds the chunk's 16 keys contiguously).
+// The four waves' states (m, l, acc) are merged through LDS at the end
+// (o = sum_w acc_w e^(m_w - M) / sum_w l_w e^(m_w - M)).
 template <typename T, typename C, int D>
 __global__ __launch_bounds__(256) void attn_generic_decode_kernel(AttnArgs a) {
   constexpr int E = D / 64;                       // dims per lane
   constexpr int NW = 4;
+  constexpr int KC = 16;                          // keys per chunk
   const int s = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __shared__ float sm[NW], sl[NW], sacc[NW][D];
@@ -133,28 +140,89 @@ __global__ __launch_bounds__(256) void attn_generic_decode_kernel(AttnArgs a) {
     qv[i] = ld<T>(qp + i) * qs;
     acc[i] = 0.0f;
   }
+  // the chunk key whose score this lane ends with (lane bits 5..2)
+  const int my = lane >> 2;
   float m = -INFINITY, l = 0.0f;
   bool wbad = false;
   __syncthreads();                                // sbad is set
-  for (int j = w; j < c; j += NW) {               // wave-uniform
-    const int blk = bt[j / B];
+  const int nch = (c + KC - 1) / KC;
+  for (int ch = w; ch < nch; ch += NW) {          // wave-uniform
+    const int j0 = ch * KC;
+    const int blk = bt[j0 / B];
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
       wbad = true;
       break;
     }
-    const int off = j % B;
-    const C* kr = kc + ((static_cast<int64_t>(blk) * Hkv + g) * B + off) * D + lane * E;
-    float z = 0.0f;
+    const int off0 = j0 % B;
+    const int64_t tile = static_cast<int64_t>(blk) * Hkv + g;
+    const C* kr = kc + (tile * B + off0) * D + lane * E;          // K tile [B][D]
+    float z[KC];
 #pragma unroll
-    for (int i = 0; i < E; ++i) z = fmaf(qv[i], ldc<C>(kr + i), z);
-    z = wave_sum(z);
-    const float mn = fmaxf(m, z);
-    const float alpha = expf(m - mn);             // 0 for the first key (m = -inf)
-    const float pz = expf(z - mn);
-    l = fmaf(l, alpha, pz);
-    const C* vr = vc + ((static_cast<int64_t>(blk) * Hkv + g) * D + lane * E) * B + off;
+    for (int i = 0; i < KC; ++i) {
+      float p = 0.0f;
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] = fmaf(acc[i], alpha, pz * ldc<C>(vr + static_cast<int64_t>(i) * B));
+      for (int e = 0; e < E; ++e) p = fmaf(qv[e], ldc<C>(kr + i * D + e), p);
+      z[i] = p;
+    }
+    float vv[E][KC];                                              // V tile [D][B]
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const C* vr = vc + (tile * D + lane * E + e) * B + off0;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) vv[e][i] = ldc<C>(vr + i);
+    }
+    // butterfly: after the exchange over lane bit b (5, 4, 3, 2) a lane keeps
+    // the half of its keys that bit selects, summed with its partner's
+    float z8[8], z4[4], z2[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool hi = lane & 32;
+      z8[i] = (hi ? z[i + 8] : z[i]) + __shfl_xor(hi ? z[i] : z[i + 8], 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool hi = lane & 16;
+      z4[i] = (hi ? z8[i + 4] : z8[i]) + __shfl_xor(hi ? z8[i] : z8[i + 4], 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool hi = lane & 8;
+      z2[i] = (hi ? z4[i + 2] : z4[i]) + __shfl_xor(hi ? z4[i] : z4[i + 2], 8);
+    }
+    float zk;
+    {
+      const bool hi = lane & 4;
+      zk = (hi ? z2[1] : z2[0]) + __shfl_xor(hi ? z2[0] : z2[1], 4);
+    }
+    zk += __shfl_xor(zk, 2);
+    zk += __shfl_xor(zk, 1);
+    // keys past the context (their slots may hold anything) are masked
+    zk = j0 + my < c ? zk : -INFINITY;
+    float bm = zk;
+    bm = fmaxf(bm, __shfl_xor(bm, 4));
+    bm = fmaxf(bm, __shfl_xor(bm, 8));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);                // finite: key j0 is inside the context
+    const float alpha = expf(m - mn);             // 0 for the first chunk (m = -inf)
+    const float pk = expf(zk - mn);               // 0 past the context
+    // the chunk's sum of p: the lanes that differ in bits 5..2 hold each key once
+    float ps = pk;
+    ps += __shfl_xor(ps, 4);
+    ps += __shfl_xor(ps, 8);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = fmaf(l, alpha, ps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const float pi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, pk), 4 * i));
+      const bool in = j0 + i < c;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(pi, in ? vv[e][i] : 0.0f, acc[e]);
+    }
     m = mn;
   }
   if (wbad && lane == 0) {
