@@ -1,13 +1,13 @@
-// Generic causal GQA attention over the paged cache, one query row and head
-// per thread, fp32 arithmetic with an online (running-max) softmax.
+// Generic causal GQA attention over the paged cache, fp32 arithmetic with an
+// online (running-max) softmax, one wave per query row and head.
 //
 // It serves the fp32 storage path, head_dim 64, group sizes the tuned bf16
-// kernels do not instantiate, and FP8 (E4M3FN) caches in prefill; it is the plain, per-row statement of the
-// method: row i of a sequence with n new rows and context c sits at position
-// c - n + i and attends to keys 0..c-n+i ("Qwen2大模型架构解析与vLLM优化实践",
-// §7.3 causal mask; "Qwen 开源工程笔记", §3 varlen rows), head h reads KV
-// head h / G ("Qwen2 模型结构代码详解", §2), keys are gathered through the
-// block table ("vLLM 部署 Qwen", §2.1).
+// kernels do not instantiate, and FP8 (E4M3FN) caches in prefill beyond the
+// MFMA kernel's shapes.  Row i of a sequence with n new rows and context c
+// sits at position c - n + i and attends to keys 0..c-n+i
+// ("Qwen2大模型架构解析与vLLM优化实践", §7.3 causal mask; "Qwen 开源工程笔记", §3
+// varlen rows), head h reads KV head h / G ("Qwen2 模型结构代码详解", §2), keys
+// are gathered through the block table ("vLLM 部署 Qwen", §2.1).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,97 +25,161 @@ template <typename T> __device__ __forceinline__ T st(float v);
 template <> __device__ __forceinline__ float st<float>(float v) { return v; }
 template <> __device__ __forceinline__ uint16_t st<uint16_t>(float v) { return f32_to_bf16(v); }
 
+constexpr int kChunk = 16;                        // keys per chunk (block sizes are multiples)
+
+// One wave attends keys j0 .. j0 + 15 of (cache tile `tile`, 16-key run at
+// offset off0 of its block); keys at or past kend are masked by selection
+// (their slots may hold anything).  A lane holds dims lane E .. lane E + E - 1
+// (E = D / 64) of q and of the output state (m, l, acc).  Every K and V load
+// of the chunk is issued at once.  The 16 partial dots are summed over the
+// wave by a butterfly: at each exchange over lane bits 5..2 a lane keeps the
+// half of its keys that bit selects, summed with its partner's (8 + 4 + 2 +
+// 1 shuffles); two more exchanges over bits 1 and 0 leave key k's score in
+// lanes 4k .. 4k + 3.  Then one online softmax update, with key k's p read
+// from lane 4k for the O += p V products (a V row of the [D][B] tile holds
+// the chunk's 16 keys contiguously).
+template <typename C, int D>
+__device__ __forceinline__ void attend_chunk(const C* kc, const C* vc, int64_t tile, int B,
+                                             int off0, int j0, int kend, int lane,
+                                             const float (&qv)[D / 64], float& m, float& l,
+                                             float (&acc)[D / 64]) {
+  constexpr int E = D / 64;
+  const C* kr = kc + (tile * B + off0) * D + lane * E;             // K tile [B][D]
+  float z[kChunk];
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    float p = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) p = fmaf(qv[e], ldc<C>(kr + i * D + e), p);
+    z[i] = p;
+  }
+  float vv[E][kChunk];                                             // V tile [D][B]
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const C* vr = vc + (tile * D + lane * E + e) * B + off0;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) vv[e][i] = ldc<C>(vr + i);
+  }
+  float z8[8], z4[4], z2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool hi = lane & 32;
+    z8[i] = (hi ? z[i + 8] : z[i]) + __shfl_xor(hi ? z[i] : z[i + 8], 32);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool hi = lane & 16;
+    z4[i] = (hi ? z8[i + 4] : z8[i]) + __shfl_xor(hi ? z8[i] : z8[i + 4], 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool hi = lane & 8;
+    z2[i] = (hi ? z4[i + 2] : z4[i]) + __shfl_xor(hi ? z4[i] : z4[i + 2], 8);
+  }
+  float zk;
+  {
+    const bool hi = lane & 4;
+    zk = (hi ? z2[1] : z2[0]) + __shfl_xor(hi ? z2[0] : z2[1], 4);
+  }
+  zk += __shfl_xor(zk, 2);
+  zk += __shfl_xor(zk, 1);
+  zk = j0 + (lane >> 2) < kend ? zk : -INFINITY;
+  float bm = zk;
+  bm = fmaxf(bm, __shfl_xor(bm, 4));
+  bm = fmaxf(bm, __shfl_xor(bm, 8));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float mn = fmaxf(m, bm);                  // finite: key j0 is below kend
+  const float alpha = expf(m - mn);               // 0 for a first chunk (m = -inf)
+  const float pk = expf(zk - mn);                 // 0 for masked keys
+  // the chunk's sum of p: the lanes that differ in bits 5..2 hold each key once
+  float ps = pk;
+  ps += __shfl_xor(ps, 4);
+  ps += __shfl_xor(ps, 8);
+  ps += __shfl_xor(ps, 16);
+  ps += __shfl_xor(ps, 32);
+  l = fmaf(l, alpha, ps);
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    const float pi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pk), 4 * i));
+    const bool in = j0 + i < kend;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = fmaf(pi, in ? vv[e][i] : 0.0f, acc[e]);
+  }
+  m = mn;
+}
+
 // C: cache element type (T, or uint8_t E4M3FN codes whose values are scaled
 // by k_scale / v_scale: folded into the query scaling and the final divide)
+
+// Prefill rows (cu_seqlens given): one wave per (row, head), four rows of one
+// sequence and head per workgroup; the wave attends its row's keys 0..pos in
+// 16-key chunks and writes the row.
 template <typename T, typename C, int D>
-__global__ __launch_bounds__(64) void attn_generic_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_generic_rows_kernel(AttnArgs a) {
+  constexpr int E = D / 64;
   const int s = blockIdx.z, h = blockIdx.y;
-  const int row = blockIdx.x * 64 + threadIdx.x;
-  int r0, n;
-  if (a.cu_seqlens) {
-    r0 = a.cu_seqlens[s];
-    n = a.cu_seqlens[s + 1] - r0;
-  } else {
-    r0 = s;
-    n = 1;
-  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + w;
+  const int r0 = a.cu_seqlens[s];
+  const int n = a.cu_seqlens[s + 1] - r0;
   // a row range outside the packed batch (bad cu_seqlens), a negative row
   // count or more rows than any valid context holds: flag, write no row
   if (r0 < 0 || n < 0 || static_cast<int64_t>(r0) + n > a.num_tokens || n > a.max_context_len) {
-    if (row == 0) report_error(a.err, kErrSequence);
+    if (row == 0 && lane == 0) report_error(a.err, kErrSequence);
     return;
   }
-  if (row >= n) return;
+  if (row >= n) return;                           // wave-uniform
   int c = a.context_lens[s];
-  bool bad = c < 1 || c > a.max_context_len;   // contract: 1 <= c <= max_context_len
-  if (bad) report_error(a.err, kErrSequence);
+  bool bad = c < 1 || c > a.max_context_len;     // contract: 1 <= c <= max_context_len
+  if (bad && lane == 0) report_error(a.err, kErrSequence);
   if (bad) c = 0;
   const int pos = c - n + row;
+  if (pos < 0 && lane == 0) report_error(a.err, kErrSequence);   // more rows than keys
+  bad = bad || pos < 0;
   const int Hkv = a.num_kv_heads, B = a.block_size;
   const int g = h / (a.num_heads / Hkv);
-  const int64_t t = static_cast<int64_t>(r0) + row;
-  const T* qp = static_cast<const T*>(a.q) + t * a.q_stride + static_cast<int64_t>(h) * D;
-  const C* kc = static_cast<const C*>(a.k_cache);
-  const C* vc = static_cast<const C*>(a.v_cache);
   const bool f8 = sizeof(C) == 1;
   const float qs = a.scale * (f8 ? a.k_scale : 1.0f);
+  const int64_t t = static_cast<int64_t>(r0) + row;
+  const T* qp = static_cast<const T*>(a.q) + t * a.q_stride + static_cast<int64_t>(h) * D + lane * E;
+  const C* kc = static_cast<const C*>(a.k_cache);
+  const C* vc = static_cast<const C*>(a.v_cache);
   const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
-
-  float qv[D], acc[D];
+  float qv[E], acc[E];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = ld<T>(qp + e) * qs;
-    acc[e] = 0.0f;
+  for (int i = 0; i < E; ++i) {
+    qv[i] = ld<T>(qp + i) * qs;
+    acc[i] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
-  if (pos < 0) report_error(a.err, kErrSequence);   // more rows than keys
-  bad = bad || pos < 0;
-  for (int j = 0; j <= pos; ++j) {
-    const int blk = bt[j / B];
+  for (int j0 = 0; j0 <= pos; j0 += kChunk) {     // wave-uniform
+    const int blk = bt[j0 / B];
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
       bad = true;
-      report_error(a.err, kErrBlock);
+      if (lane == 0) report_error(a.err, kErrBlock);
       break;
     }
-    const int off = j % B;
-    const C* kr = kc + ((static_cast<int64_t>(blk) * Hkv + g) * B + off) * D;
-    float z = 0.0f;
-#pragma unroll
-    for (int e = 0; e < D; ++e) z = fmaf(qv[e], ldc<C>(kr + e), z);
-    const float mn = fmaxf(m, z);
-    const float alpha = expf(m - mn);
-    const float pz = expf(z - mn);
-    l = fmaf(l, alpha, pz);
-    const C* vr = vc + (static_cast<int64_t>(blk) * Hkv + g) * D * B + off;
-#pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] = fmaf(acc[e], alpha, pz * ldc<C>(vr + static_cast<int64_t>(e) * B));
-    m = mn;
+    attend_chunk<C, D>(kc, vc, static_cast<int64_t>(blk) * Hkv + g, B, j0 % B, j0, pos + 1, lane,
+                       qv, m, l, acc);
   }
-  T* op = static_cast<T*>(a.out) + t * a.out_stride + static_cast<int64_t>(h) * D;
+  T* op = static_cast<T*>(a.out) + t * a.out_stride + static_cast<int64_t>(h) * D + lane * E;
   const float inv = bad ? __builtin_nanf("") : (f8 ? a.v_scale : 1.0f) / l;
 #pragma unroll
-  for (int e = 0; e < D; ++e) op[e] = st<T>(acc[e] * inv);
+  for (int i = 0; i < E; ++i) op[i] = st<T>(acc[i] * inv);
 }
 
-// The decode rows (one query row per sequence, no cu_seqlens): one
-// workgroup per (sequence, query head).  Its four waves take 16-key chunks
-// of the context round robin (a chunk lies in one cache block: block sizes
-// are multiples of 16); a lane holds D / 64 consecutive dims.  Per chunk a
-// wave issues every K and V load of its 16 keys at once, then:
-//   * partial dots q_e k_e per lane and key, summed over the wave by a
-//     butterfly that halves the keys a lane carries at each of the exchanges
-//     over lane bits 5..2 (8 + 4 + 2 + 1 shuffles) and then adds over bits 1
-//     and 0: lanes 4k .. 4k + 3 end with key k's score;
-//   * an online softmax update per chunk (keys past the context masked by
-//     selection), key k's p broadcast from lane 4k for the O += p V products
-//     over the lane's dims (a V row holds the chunk's 16 keys contiguously).
-// The four waves' states (m, l, acc) are merged through LDS at the end
-// (o = sum_w acc_w e^(m_w - M) / sum_w l_w e^(m_w - M)).
+// Decode rows (one query row per sequence, no cu_seqlens): one workgroup per
+// (sequence, query head).  Its four waves take the 16-key chunks of the
+// context round robin, each keeping its own state; the four states (m, l,
+// acc) are merged through LDS at the end (o = sum_w acc_w e^(m_w - M) /
+// sum_w l_w e^(m_w - M)).
 template <typename T, typename C, int D>
 __global__ __launch_bounds__(256) void attn_generic_decode_kernel(AttnArgs a) {
-  constexpr int E = D / 64;                       // dims per lane
+  constexpr int E = D / 64;
   constexpr int NW = 4;
-  constexpr int KC = 16;                          // keys per chunk
   const int s = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __shared__ float sm[NW], sl[NW], sacc[NW][D];
@@ -140,90 +204,17 @@ __global__ __launch_bounds__(256) void attn_generic_decode_kernel(AttnArgs a) {
     qv[i] = ld<T>(qp + i) * qs;
     acc[i] = 0.0f;
   }
-  // the chunk key whose score this lane ends with (lane bits 5..2)
-  const int my = lane >> 2;
   float m = -INFINITY, l = 0.0f;
   bool wbad = false;
   __syncthreads();                                // sbad is set
-  const int nch = (c + KC - 1) / KC;
-  for (int ch = w; ch < nch; ch += NW) {          // wave-uniform
-    const int j0 = ch * KC;
+  for (int j0 = w * kChunk; j0 < c; j0 += NW * kChunk) {   // wave-uniform
     const int blk = bt[j0 / B];
     if (static_cast<unsigned>(blk) >= static_cast<unsigned>(a.num_blocks)) {
       wbad = true;
       break;
     }
-    const int off0 = j0 % B;
-    const int64_t tile = static_cast<int64_t>(blk) * Hkv + g;
-    const C* kr = kc + (tile * B + off0) * D + lane * E;          // K tile [B][D]
-    float z[KC];
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      float p = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) p = fmaf(qv[e], ldc<C>(kr + i * D + e), p);
-      z[i] = p;
-    }
-    float vv[E][KC];                                              // V tile [D][B]
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const C* vr = vc + (tile * D + lane * E + e) * B + off0;
-#pragma unroll
-      for (int i = 0; i < KC; ++i) vv[e][i] = ldc<C>(vr + i);
-    }
-    // butterfly: after the exchange over lane bit b (5, 4, 3, 2) a lane keeps
-    // the half of its keys that bit selects, summed with its partner's
-    float z8[8], z4[4], z2[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool hi = lane & 32;
-      z8[i] = (hi ? z[i + 8] : z[i]) + __shfl_xor(hi ? z[i] : z[i + 8], 32);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool hi = lane & 16;
-      z4[i] = (hi ? z8[i + 4] : z8[i]) + __shfl_xor(hi ? z8[i] : z8[i + 4], 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool hi = lane & 8;
-      z2[i] = (hi ? z4[i + 2] : z4[i]) + __shfl_xor(hi ? z4[i] : z4[i + 2], 8);
-    }
-    float zk;
-    {
-      const bool hi = lane & 4;
-      zk = (hi ? z2[1] : z2[0]) + __shfl_xor(hi ? z2[0] : z2[1], 4);
-    }
-    zk += __shfl_xor(zk, 2);
-    zk += __shfl_xor(zk, 1);
-    // keys past the context (their slots may hold anything) are masked
-    zk = j0 + my < c ? zk : -INFINITY;
-    float bm = zk;
-    bm = fmaxf(bm, __shfl_xor(bm, 4));
-    bm = fmaxf(bm, __shfl_xor(bm, 8));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);                // finite: key j0 is inside the context
-    const float alpha = expf(m - mn);             // 0 for the first chunk (m = -inf)
-    const float pk = expf(zk - mn);               // 0 past the context
-    // the chunk's sum of p: the lanes that differ in bits 5..2 hold each key once
-    float ps = pk;
-    ps += __shfl_xor(ps, 4);
-    ps += __shfl_xor(ps, 8);
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l = fmaf(l, alpha, ps);
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const float pi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                      __builtin_bit_cast(int, pk), 4 * i));
-      const bool in = j0 + i < c;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(pi, in ? vv[e][i] : 0.0f, acc[e]);
-    }
-    m = mn;
+    attend_chunk<C, D>(kc, vc, static_cast<int64_t>(blk) * Hkv + g, B, j0 % B, j0, c, lane, qv, m,
+                       l, acc);
   }
   if (wbad && lane == 0) {
     report_error(a.err, kErrBlock);
@@ -259,13 +250,12 @@ __global__ __launch_bounds__(256) void attn_generic_decode_kernel(AttnArgs a) {
 }
 
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream) {
-  const int rows = a.cu_seqlens ? a.max_query_len : 1;
-  const dim3 grid((rows + 63) / 64, a.num_heads, a.num_seqs);
-  const dim3 dgrid(a.num_seqs, a.num_heads);
+  const dim3 grid((a.max_query_len + 3) / 4, a.num_heads, a.num_seqs);   // prefill rows
+  const dim3 dgrid(a.num_seqs, a.num_heads);                             // decode rows
 #define QW_GEN(T, C, D)                                                                      \
   do {                                                                                       \
     if (a.cu_seqlens)                                                                        \
-      hipLaunchKernelGGL((attn_generic_kernel<T, C, D>), grid, dim3(64), 0, stream, a);      \
+      hipLaunchKernelGGL((attn_generic_rows_kernel<T, C, D>), grid, dim3(256), 0, stream, a); \
     else                                                                                     \
       hipLaunchKernelGGL((attn_generic_decode_kernel<T, C, D>), dgrid, dim3(256), 0, stream, \
                          a);                                                                 \
