@@ -172,14 +172,15 @@ __global__ __launch_bounds__(256) void attn_generic_rows_kernel(AttnArgs a) {
 }
 
 // Decode rows (one query row per sequence, no cu_seqlens): one workgroup per
-// (sequence, query head).  Its four waves take the 16-key chunks of the
-// context round robin, each keeping its own state; the four states (m, l,
-// acc) are merged through LDS at the end (o = sum_w acc_w e^(m_w - M) /
-// sum_w l_w e^(m_w - M)).
+// (sequence, query head).  Its sixteen waves take the 16-key chunks of the
+// context round robin, each keeping its own state; the states (m, l, acc)
+// are merged through LDS at the end (o = sum_w acc_w e^(m_w - M) /
+// sum_w l_w e^(m_w - M)).  Sixteen waves, not four, so that a small batch
+// (a few sequences x heads workgroups) still has many chunks in flight.
 template <typename T, typename C, int D>
-__global__ __launch_bounds__(256) void attn_generic_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(1024) void attn_generic_decode_kernel(AttnArgs a) {
   constexpr int E = D / 64;
-  constexpr int NW = 4;
+  constexpr int NW = 16;
   const int s = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __shared__ float sm[NW], sl[NW], sacc[NW][D];
@@ -257,7 +258,7 @@ hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream) {
     if (a.cu_seqlens)                                                                        \
       hipLaunchKernelGGL((attn_generic_rows_kernel<T, C, D>), grid, dim3(256), 0, stream, a); \
     else                                                                                     \
-      hipLaunchKernelGGL((attn_generic_decode_kernel<T, C, D>), dgrid, dim3(256), 0, stream, \
+      hipLaunchKernelGGL((attn_generic_decode_kernel<T, C, D>), dgrid, dim3(1024), 0, stream, \
                          a);                                                                 \
   } while (0)
   const bool d128 = a.head_dim == 128;
