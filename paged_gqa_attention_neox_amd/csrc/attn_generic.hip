@@ -171,31 +171,59 @@ __global__ __launch_bounds__(256) void attn_generic_rows_kernel(AttnArgs a) {
   for (int i = 0; i < E; ++i) op[i] = st<T>(acc[i] * inv);
 }
 
-// Decode rows (one query row per sequence, no cu_seqlens): one workgroup per
-// (sequence, query head).  Its sixteen waves take the 16-key chunks of the
-// context round robin, each keeping its own state; the states (m, l, acc)
-// are merged through LDS at the end (o = sum_w acc_w e^(m_w - M) /
-// sum_w l_w e^(m_w - M)).  Sixteen waves, not four, so that a small batch
-// (a few sequences x heads workgroups) still has many chunks in flight.
-template <typename T, typename C, int D>
-__global__ __launch_bounds__(1024) void attn_generic_decode_kernel(AttnArgs a) {
+// One row per workgroup: the decode rows (one query row per sequence, no
+// cu_seqlens; ROWS false), and prefill rows with long contexts (ROWS: row
+// blockIdx.x of sequence blockIdx.z).  The workgroup's sixteen waves take
+// the 16-key chunks of the row's keys round robin, each keeping its own
+// state; the states (m, l, acc) are merged through LDS at the end
+// (o = sum_w acc_w e^(m_w - M) / sum_w l_w e^(m_w - M)).  Sixteen waves, not
+// four, so that a small batch (a few sequences x heads workgroups) or a long
+// row still has many chunks in flight.
+template <typename T, typename C, int D, bool ROWS>
+__global__ __launch_bounds__(1024) void attn_generic_wide_kernel(AttnArgs a) {
   constexpr int E = D / 64;
   constexpr int NW = 16;
-  const int s = blockIdx.x, h = blockIdx.y;
+  const int h = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __shared__ float sm[NW], sl[NW], sacc[NW][D];
   __shared__ int sbad;
+  int s, c;
+  int64_t t;                                      // the row's token
+  bool bad;
+  if constexpr (ROWS) {
+    s = blockIdx.z;
+    const int row = blockIdx.x;
+    const int r0 = a.cu_seqlens[s];
+    const int n = a.cu_seqlens[s + 1] - r0;
+    // as in attn_generic_rows_kernel: a row range outside the batch is
+    // flagged once and no row is written
+    if (r0 < 0 || n < 0 || static_cast<int64_t>(r0) + n > a.num_tokens || n > a.max_context_len) {
+      if (row == 0 && threadIdx.x == 0) report_error(a.err, kErrSequence);
+      return;
+    }
+    if (row >= n) return;                         // the whole workgroup
+    c = a.context_lens[s];
+    bad = c < 1 || c > a.max_context_len;
+    if (bad && threadIdx.x == 0) report_error(a.err, kErrSequence);
+    const int pos = (bad ? 0 : c) - n + row;
+    if (pos < 0 && threadIdx.x == 0) report_error(a.err, kErrSequence);   // more rows than keys
+    bad = bad || pos < 0;
+    c = bad ? 0 : pos + 1;                        // the row's keys
+    t = static_cast<int64_t>(r0) + row;
+  } else {
+    s = blockIdx.x;
+    c = a.context_lens[s];
+    bad = c < 1 || c > a.max_context_len;         // contract: 1 <= c <= max_context_len
+    if (bad && threadIdx.x == 0) report_error(a.err, kErrSequence);
+    if (bad) c = 0;
+    t = s;
+  }
   if (threadIdx.x == 0) sbad = 0;
-  int c = a.context_lens[s];
-  bool bad = c < 1 || c > a.max_context_len;     // contract: 1 <= c <= max_context_len
-  if (bad && threadIdx.x == 0) report_error(a.err, kErrSequence);
-  if (bad) c = 0;
   const int Hkv = a.num_kv_heads, B = a.block_size;
   const int g = h / (a.num_heads / Hkv);
   const bool f8 = sizeof(C) == 1;
   const float qs = a.scale * (f8 ? a.k_scale : 1.0f);
-  const T* qp = static_cast<const T*>(a.q) + static_cast<int64_t>(s) * a.q_stride +
-                static_cast<int64_t>(h) * D + lane * E;
+  const T* qp = static_cast<const T*>(a.q) + t * a.q_stride + static_cast<int64_t>(h) * D + lane * E;
   const C* kc = static_cast<const C*>(a.k_cache);
   const C* vc = static_cast<const C*>(a.v_cache);
   const int32_t* bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
@@ -244,22 +272,31 @@ __global__ __launch_bounds__(1024) void attn_generic_decode_kernel(AttnArgs a) {
     for (int i = 0; i < E; ++i) o[i] = fmaf(sacc[k][lane * E + i], wt, o[i]);
   }
   const float inv = bad || sbad ? __builtin_nanf("") : (f8 ? a.v_scale : 1.0f) / L;
-  T* op = static_cast<T*>(a.out) + static_cast<int64_t>(s) * a.out_stride +
-          static_cast<int64_t>(h) * D + lane * E;
+  T* op = static_cast<T*>(a.out) + t * a.out_stride + static_cast<int64_t>(h) * D + lane * E;
 #pragma unroll
   for (int i = 0; i < E; ++i) op[i] = st<T>(o[i] * inv);
 }
 
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((a.max_query_len + 3) / 4, a.num_heads, a.num_seqs);   // prefill rows
+  // Prefill rows: a wave per row, or a workgroup per row where every row has
+  // a long context (at least kWideKeys keys and four times the longest
+  // chunk: a chunk after a long prefix), so that a row's chunks are spread
+  // over sixteen waves instead of walked by one.
+  constexpr int kWideKeys = 2048;
+  const bool wide = a.max_context_len >= kWideKeys && a.max_context_len >= 4 * a.max_query_len;
+  const dim3 grid((a.max_query_len + 3) / 4, a.num_heads, a.num_seqs);   // prefill, wave per row
+  const dim3 wgrid(a.max_query_len, a.num_heads, a.num_seqs);            // prefill, workgroup per row
   const dim3 dgrid(a.num_seqs, a.num_heads);                             // decode rows
 #define QW_GEN(T, C, D)                                                                      \
   do {                                                                                       \
-    if (a.cu_seqlens)                                                                        \
-      hipLaunchKernelGGL((attn_generic_rows_kernel<T, C, D>), grid, dim3(256), 0, stream, a); \
+    if (!a.cu_seqlens)                                                                       \
+      hipLaunchKernelGGL((attn_generic_wide_kernel<T, C, D, false>), dgrid, dim3(1024), 0,   \
+                         stream, a);                                                         \
+    else if (wide)                                                                           \
+      hipLaunchKernelGGL((attn_generic_wide_kernel<T, C, D, true>), wgrid, dim3(1024), 0,    \
+                         stream, a);                                                         \
     else                                                                                     \
-      hipLaunchKernelGGL((attn_generic_decode_kernel<T, C, D>), dgrid, dim3(1024), 0, stream, \
-                         a);                                                                 \
+      hipLaunchKernelGGL((attn_generic_rows_kernel<T, C, D>), grid, dim3(256), 0, stream, a); \
   } while (0)
   const bool d128 = a.head_dim == 128;
   if (a.dtype == kBF16) {
